@@ -1,0 +1,82 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that
+the pins catch every one of them.  The real oracle is never modified: each
+mutant is a patched copy of oracle.c compiled into a temporary directory."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+import oracle_pins
+
+ORACLE_DIR = os.path.dirname(oracle_build.SRC)
+
+MUTANTS = {
+    "emb_drops_last_index": (
+        "for (int64_t l = start; l < end; ++l)",
+        "for (int64_t l = start; l + 1 < end; ++l)"),
+    "emb_wrong_column": (
+        "acc += (double)W[r * (int64_t)D + d];",
+        "acc += (double)W[r * (int64_t)D];"),
+    "emb_transposed_output": (
+        "out[((int64_t)b * K + k) * D + d] = (float)acc;",
+        "out[((int64_t)k * B + b) * D + d] = (float)acc;"),
+    "emb_last_bag_empty": (
+        "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : n_idx[k];",
+        "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : start;"),
+    "pair_order_column_major": (
+        "for (int64_t i = 1; i < F; ++i)\n"
+        "      for (int64_t j = 0; j < i; ++j) row[D + p++] = (float)Z[i * F + j];",
+        "for (int64_t j = 0; j < F; ++j)\n"
+        "      for (int64_t i = j + 1; i < F; ++i) row[D + p++] = (float)Z[i * F + j];"),
+    "dot_drops_first_term": (
+        "for (int32_t d = 0; d < D; ++d) acc += X[i * D + d] * X[j * D + d];",
+        "for (int32_t d = 1; d < D; ++d) acc += X[i * D + d] * X[j * D + d];"),
+    "dense_feature_sign": (
+        "X[d] = (double)dense[(int64_t)b * D + d];",
+        "X[d] = -(double)dense[(int64_t)b * D + d];"),
+    "dense_copy_dropped": (
+        "memcpy(row, dense + (int64_t)b * D, sizeof(float) * (size_t)D);",
+        "memset(row, 0, sizeof(float) * (size_t)D);"),
+    "linear_transposed_weight": (
+        "(double)W[(int64_t)n * Kd + k];",
+        "(double)W[(int64_t)k * N + n];"),
+    "linear_drops_bias": (
+        "double acc = bias ? (double)bias[n] : 0.0;",
+        "double acc = 0.0;"),
+    "relu_wrong_branch": (
+        "acc = acc > 0.0 ? acc : 0.0;",
+        "acc = acc > 0.0 ? acc : -acc;"),
+    "sigmoid_wrong_sign": (
+        "acc = 1.0 / (1.0 + exp(-acc));",
+        "acc = 1.0 / (1.0 + exp(acc));"),
+    "pair_column_formula": (
+        "*j_out = p - i * (i - 1) / 2;",
+        "*j_out = p - i * (i + 1) / 2;"),
+    "pair_float_sqrt_no_fixups": (
+        "  int64_t i = (int64_t)floor((1.0 + sqrt(1.0 + 8.0 * (double)p)) / 2.0);\n"
+        "  while (i * (i - 1) / 2 > p) --i;\n"
+        "  while ((i + 1) * i / 2 <= p) ++i;\n",
+        "  int64_t i = (int64_t)floorf((1.0f + sqrtf(1.0f + 8.0f * (float)p)) / 2.0f);\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle_build.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    shutil.copy(os.path.join(ORACLE_DIR, "oracle.h"), tmp_path / "oracle.h")
+    mutant_c = tmp_path / "oracle.c"
+    mutant_c.write_text(src.replace(old, new))
+    so = str(tmp_path / "liboracle_mutant.so")
+    oracle_build.build(str(mutant_c), so, extra_flags=["-Wno-error"])
+    lib = oracle.load(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, oracle.OracleError) as e:
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught the planted mistake {name}"
