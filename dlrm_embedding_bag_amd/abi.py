@@ -1,0 +1,315 @@
+"""ctypes binding of libdlrm_mi355x.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks that tensors are float32/int32 device
+tensors, passes their device pointers and the current HIP stream, and turns a
+non-zero dlrm_status into a DlrmError.  There is no CPU fallback: without the
+built library, or with tensors off the GPU, calls raise.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdlrm_mi355x.so")
+
+DLRM_OK = 0
+STATUS_NAMES = {0: "DLRM_OK", 1: "DLRM_ERR_NULL", 2: "DLRM_ERR_SHAPE",
+                3: "DLRM_ERR_UNSUPPORTED", 4: "DLRM_ERR_WORKSPACE", 5: "DLRM_ERR_HIP"}
+ACTS = {"none": 0, "relu": 1, "sigmoid": 2}
+MAX_TABLES = 64
+MAX_DIM = 1024
+EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
+           "dlrm_interact_lower_tri", "dlrm_emb_interact", "linear_bias_act",
+           "dlrm_forward_workspace_bytes", "dlrm_forward")
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class DlrmError(RuntimeError):
+    def __init__(self, status: int, call: str, message: str):
+        super().__init__(f"{call}: {message}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("in_features", _i32), ("out_features", _i32),
+                ("weight", _vp), ("bias", _vp), ("act", _i32)]
+
+
+class Model(ctypes.Structure):
+    _fields_ = [("num_bottom", _i32), ("bottom", ctypes.POINTER(Layer)),
+                ("num_top", _i32), ("top", ctypes.POINTER(Layer)),
+                ("num_tables", _i32), ("dim", _i32),
+                ("tables", ctypes.POINTER(_vp)), ("rows", ctypes.POINTER(_i64))]
+
+
+_LIB = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None and path == LIB_PATH:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    lib.dlrm_status_string.restype = ctypes.c_char_p
+    lib.dlrm_status_string.argtypes = [ctypes.c_int]
+    lib.dlrm_abi_version.restype = ctypes.c_int
+    lib.dlrm_abi_version.argtypes = []
+    ptrs = ctypes.POINTER(_vp)
+    lib.emb_bag_sum_multi.restype = ctypes.c_int
+    lib.emb_bag_sum_multi.argtypes = [_i32, _i32, _i32, ptrs, ctypes.POINTER(_i64), ptrs,
+                                      ptrs, ctypes.POINTER(_i64), _vp, _vp]
+    lib.dlrm_interact_lower_tri.restype = ctypes.c_int
+    lib.dlrm_interact_lower_tri.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
+    lib.dlrm_emb_interact.restype = ctypes.c_int
+    lib.dlrm_emb_interact.argtypes = [_i32, _i32, _i32, ptrs, ctypes.POINTER(_i64), ptrs,
+                                      ptrs, ctypes.POINTER(_i64), _vp, _vp, _vp, _vp]
+    lib.linear_bias_act.restype = ctypes.c_int
+    lib.linear_bias_act.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _i64,
+                                    _vp]
+    lib.dlrm_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.dlrm_forward_workspace_bytes.argtypes = [ctypes.POINTER(Model), _i32]
+    lib.dlrm_forward.restype = ctypes.c_int
+    lib.dlrm_forward.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
+                                 ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t, _vp]
+    if path == LIB_PATH:
+        _LIB = lib
+    return lib
+
+
+def _check(status: int, call: str):
+    if status != DLRM_OK:
+        msg = load().dlrm_status_string(status).decode()
+        raise DlrmError(status, call, msg)
+
+
+# ------------------------------------------------------------ marshalling --
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev(t, dtype, what):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _ptr_array(tensors):
+    arr = (_vp * len(tensors))()
+    for k, t in enumerate(tensors):
+        arr[k] = t.data_ptr() if t is not None else None
+    return arr
+
+
+def _i64_array(values):
+    arr = (_i64 * len(values))()
+    for k, v in enumerate(values):
+        arr[k] = int(v)
+    return arr
+
+
+def _tables_args(tables, indices, offsets):
+    torch = _torch()
+    tables = [_dev(t, torch.float32, f"tables[{k}]") for k, t in enumerate(tables)]
+    indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
+    if len(tables) != len(indices):
+        raise ValueError("tables and indices must have the same length")
+    if offsets is not None:
+        offsets = [_dev(o, torch.int32, f"offsets[{k}]") for k, o in enumerate(offsets)]
+        if len(offsets) != len(tables):
+            raise ValueError("offsets must have one entry per table")
+    rows = [t.shape[0] for t in tables]
+    n_idx = [i.numel() for i in indices]
+    return (tables, indices, offsets, _ptr_array(tables), _i64_array(rows),
+            _ptr_array(indices), _ptr_array(offsets) if offsets is not None else None,
+            _i64_array(n_idx))
+
+
+# ---------------------------------------------------------------- entries --
+def emb_bag_sum_multi(tables, indices, offsets=None, batch=None, out=None, stream=None):
+    """(B, K, D) float32 pooled sums; see include/dlrm_embedding_bag.h."""
+    torch = _torch()
+    lib = load()
+    (tables, indices, offsets, tp, rows, ip, op, nidx) = _tables_args(tables, indices, offsets)
+    K = len(tables)
+    D = tables[0].shape[1]
+    B = offsets[0].shape[0] if offsets is not None else batch
+    if B is None:
+        raise ValueError("batch is required with uniform-stride (offsets=None) bags")
+    if out is None:
+        out = torch.empty((B, K, D), dtype=torch.float32, device=tables[0].device)
+    _dev(out, torch.float32, "out")
+    _check(lib.emb_bag_sum_multi(K, B, D, tp, rows, ip, op, nidx, out.data_ptr(),
+                                 _stream(stream)), "emb_bag_sum_multi")
+    return out
+
+
+def dlrm_interact_lower_tri(dense, emb, out=None, stream=None):
+    """(B, D + F(F-1)/2) float32 = [dense | strict-lower-triangle dots]."""
+    torch = _torch()
+    lib = load()
+    _dev(dense, torch.float32, "dense")
+    _dev(emb, torch.float32, "emb")
+    B, N, D = emb.shape
+    P = (N + 1) * N // 2
+    if out is None:
+        out = torch.empty((B, D + P), dtype=torch.float32, device=emb.device)
+    _dev(out, torch.float32, "out")
+    if dense.shape != (B, D) or out.shape != (B, D + P):
+        raise ValueError("dense must be (B, D) and out (B, D + F(F-1)/2)")
+    _check(lib.dlrm_interact_lower_tri(B, N, D, dense.data_ptr(), emb.data_ptr(),
+                                       out.data_ptr(), _stream(stream)),
+           "dlrm_interact_lower_tri")
+    return out
+
+
+def dlrm_emb_interact(tables, indices, dense, offsets=None, out=None, emb_out=None,
+                      stream=None):
+    """Fused gather + interaction: (B, D + F(F-1)/2) float32."""
+    torch = _torch()
+    lib = load()
+    (tables, indices, offsets, tp, rows, ip, op, nidx) = _tables_args(tables, indices, offsets)
+    _dev(dense, torch.float32, "dense")
+    K = len(tables)
+    B, D = dense.shape
+    P = (K + 1) * K // 2
+    if out is None:
+        out = torch.empty((B, D + P), dtype=torch.float32, device=dense.device)
+    _dev(out, torch.float32, "out")
+    if out.shape != (B, D + P):
+        raise ValueError("out must be (B, D + F(F-1)/2)")
+    eo = None
+    if emb_out is not None:
+        _dev(emb_out, torch.float32, "emb_out")
+        if emb_out.shape != (B, K, D):
+            raise ValueError("emb_out must be (B, K, D)")
+        eo = emb_out.data_ptr()
+    _check(lib.dlrm_emb_interact(K, B, D, tp, rows, ip, op, nidx, dense.data_ptr(),
+                                 out.data_ptr(), eo, _stream(stream)), "dlrm_emb_interact")
+    return out
+
+
+def linear_bias_act(a, w, bias=None, act="none", out=None, stream=None):
+    """act(a @ w.T + bias) as (M, N) float32."""
+    torch = _torch()
+    lib = load()
+    if not isinstance(a, torch.Tensor) or a.device.type != "cuda" or a.dtype != torch.float32:
+        raise ValueError("a must be a float32 GPU tensor")
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with unit column stride")
+    _dev(w, torch.float32, "w")
+    M, Kd = a.shape
+    N = w.shape[0]
+    if w.shape[1] != Kd:
+        raise ValueError("w must be (N, K)")
+    bp = None
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+        bp = bias.data_ptr()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape != (M, N):
+        raise ValueError("out must be (M, N) with unit column stride")
+    _check(lib.linear_bias_act(M, N, Kd, a.data_ptr(), a.stride(0), w.data_ptr(), bp,
+                               ACTS[act] if isinstance(act, str) else int(act),
+                               out.data_ptr(), out.stride(0), _stream(stream)),
+           "linear_bias_act")
+    return out
+
+
+class DlrmModel:
+    """Host description of a DLRMv1 model over caller-owned device tensors.
+
+    bottom / top: lists of (weight (out, in), bias (out,) or None, act) with
+    GPU float32 tensors; tables: list of (rows_k, D) GPU float32 tensors.
+    """
+
+    def __init__(self, bottom, top, tables):
+        torch = _torch()
+        self._keep = []
+        self.tables = [_dev(t, torch.float32, f"tables[{k}]") for k, t in enumerate(tables)]
+        self.dim = self.tables[0].shape[1]
+
+        def layers(spec, what):
+            arr = (Layer * len(spec))()
+            for n, (wt, b, act) in enumerate(spec):
+                _dev(wt, torch.float32, f"{what}[{n}].weight")
+                if b is not None:
+                    _dev(b, torch.float32, f"{what}[{n}].bias")
+                self._keep.extend([wt, b])
+                arr[n].in_features = wt.shape[1]
+                arr[n].out_features = wt.shape[0]
+                arr[n].weight = wt.data_ptr()
+                arr[n].bias = b.data_ptr() if b is not None else None
+                arr[n].act = ACTS[act] if isinstance(act, str) else int(act)
+            return arr
+
+        self._bottom = layers(bottom, "bottom")
+        self._top = layers(top, "top")
+        self._tables = _ptr_array(self.tables)
+        self._rows = _i64_array([t.shape[0] for t in self.tables])
+        self.out_features = top[-1][0].shape[0]
+        self.struct = Model(len(bottom), self._bottom, len(top), self._top,
+                            len(self.tables), self.dim, self._tables, self._rows)
+
+    def workspace_bytes(self, batch: int) -> int:
+        return dlrm_forward_workspace_bytes(self, batch)
+
+
+def dlrm_forward_workspace_bytes(model: DlrmModel, batch: int) -> int:
+    return int(load().dlrm_forward_workspace_bytes(ctypes.byref(model.struct), batch))
+
+
+def dlrm_forward(model: DlrmModel, dense_in, indices, offsets=None, out=None, workspace=None,
+                 stream=None):
+    """DLRMv1 forward: (B, top[last].out_features) float32."""
+    torch = _torch()
+    lib = load()
+    _dev(dense_in, torch.float32, "dense_in")
+    B = dense_in.shape[0]
+    indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
+    if offsets is not None:
+        offsets = [_dev(o, torch.int32, f"offsets[{k}]") for k, o in enumerate(offsets)]
+    if out is None:
+        out = torch.empty((B, model.out_features), dtype=torch.float32, device=dense_in.device)
+    _dev(out, torch.float32, "out")
+    need = model.workspace_bytes(B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dense_in.device)
+    ws = workspace.data_ptr()
+    _check(lib.dlrm_forward(ctypes.byref(model.struct), B, dense_in.data_ptr(),
+                            _ptr_array(indices),
+                            _ptr_array(offsets) if offsets is not None else None,
+                            _i64_array([i.numel() for i in indices]), out.data_ptr(), ws,
+                            workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dlrm_forward")
+    return out

@@ -1,0 +1,39 @@
+"""Build libdlrm_mi355x.so (the HIP kernels and the C ABI) for gfx950.
+
+hipcc compiles ahead of time for gfx950 only.  Packed-FP32 instructions are
+disabled: ordinary float code is compiled to scalar VALU operations.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libdlrm_mi355x.so")
+SOURCES = ["abi.hip", "emb_interact.hip", "linear.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fvisibility=hidden",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
+    """Compile every HIP source into `out` and return its path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra_flags, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=CSRC)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

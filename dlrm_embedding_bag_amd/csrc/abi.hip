@@ -1,0 +1,265 @@
+// abi.hip -- the extern "C" entry points of libdlrm_mi355x: argument
+// validation, kernel selection and the DLRMv1 forward composition.  Every
+// argument error is reported before any work is enqueued; nothing here
+// allocates device memory or synchronizes the stream.
+#include <limits.h>
+#include <string.h>
+
+#include "../../include/dlrm_embedding_bag.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace dlrm;
+
+static_assert(DLRM_MAX_TABLES == kMaxTables, "table limit mismatch");
+
+namespace {
+
+bool valid_act(int act) {
+  return act == DLRM_ACT_NONE || act == DLRM_ACT_RELU || act == DLRM_ACT_SIGMOID;
+}
+
+int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Validates the table arguments shared by the gather entry points and packs
+// them into the by-value kernel argument.
+int pack_tables(int32_t K, int32_t B, int32_t D, const float *const *tables,
+                const int64_t *rows, const int32_t *const *indices,
+                const int32_t *const *offsets, const int64_t *n_idx, TableSet &ts, bool &csr,
+                bool &vec_ok) {
+  if (K < 1 || K > DLRM_MAX_TABLES || B < 0 || D < 1 || D > DLRM_MAX_DIM) return DLRM_ERR_SHAPE;
+  if (!tables || !rows || !indices || !n_idx) return DLRM_ERR_NULL;
+  memset(&ts, 0, sizeof(ts));
+  csr = offsets != nullptr;
+  vec_ok = (D % 4) == 0;
+  for (int k = 0; k < K; ++k) {
+    if (!tables[k]) return DLRM_ERR_NULL;
+    if (rows[k] < 1 || n_idx[k] < 0 || n_idx[k] > INT32_MAX) return DLRM_ERR_SHAPE;
+    if (n_idx[k] > 0 && !indices[k]) return DLRM_ERR_NULL;
+    if (csr) {
+      if (!offsets[k] && B > 0) return DLRM_ERR_NULL;
+    } else if (B > 0 && n_idx[k] % B != 0) {
+      return DLRM_ERR_SHAPE;
+    }
+    ts.table[k] = tables[k];
+    ts.idx[k] = indices[k];
+    ts.off[k] = csr ? offsets[k] : nullptr;
+    ts.bag[k] = (!csr && B > 0) ? (int32_t)(n_idx[k] / B) : 0;
+    ts.nidx[k] = (int32_t)n_idx[k];
+    vec_ok = vec_ok && aligned16(tables[k]);
+  }
+  return DLRM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DLRM_OK : DLRM_ERR_HIP; }
+
+struct ForwardLayout {
+  int64_t P = 0, ldR = 0, ld_buf = 0;
+  size_t off_R = 0, off_buf0 = 0, off_buf1 = 0, total = 0;
+};
+
+// Checks the model's shapes and computes the workspace layout for batch B.
+int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
+  if (!m) return DLRM_ERR_NULL;
+  if (m->num_bottom < 1 || m->num_top < 1 || m->num_tables < 1 ||
+      m->num_tables > DLRM_MAX_TABLES || m->dim < 1 || m->dim > DLRM_MAX_DIM || B < 0)
+    return DLRM_ERR_SHAPE;
+  if (!m->bottom || !m->top || !m->tables || !m->rows) return DLRM_ERR_NULL;
+  const int64_t F = (int64_t)m->num_tables + 1;
+  lay.P = F * (F - 1) / 2;
+  lay.ldR = round4(m->dim + lay.P);
+  int64_t widest = 4;
+  for (int l = 0; l < m->num_bottom; ++l) {
+    const dlrm_layer &L = m->bottom[l];
+    if (!L.weight) return DLRM_ERR_NULL;
+    if (L.in_features < 1 || L.out_features < 1 || !valid_act(L.act)) return DLRM_ERR_SHAPE;
+    if (l > 0 && L.in_features != m->bottom[l - 1].out_features) return DLRM_ERR_SHAPE;
+    if (l + 1 < m->num_bottom) widest = widest > L.out_features ? widest : L.out_features;
+  }
+  if (m->bottom[m->num_bottom - 1].out_features != m->dim) return DLRM_ERR_SHAPE;
+  for (int l = 0; l < m->num_top; ++l) {
+    const dlrm_layer &L = m->top[l];
+    if (!L.weight) return DLRM_ERR_NULL;
+    if (L.in_features < 1 || L.out_features < 1 || !valid_act(L.act)) return DLRM_ERR_SHAPE;
+    if (l > 0 && L.in_features != m->top[l - 1].out_features) return DLRM_ERR_SHAPE;
+    if (l + 1 < m->num_top) widest = widest > L.out_features ? widest : L.out_features;
+  }
+  if (m->top[0].in_features != m->dim + lay.P) return DLRM_ERR_SHAPE;
+  lay.ld_buf = round4(widest);
+  lay.off_R = 0;
+  lay.off_buf0 = round256((size_t)B * (size_t)lay.ldR * sizeof(float));
+  lay.off_buf1 = lay.off_buf0 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
+  lay.total = lay.off_buf1 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
+  return DLRM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dlrm_status_string(int status) {
+  switch (status) {
+    case DLRM_OK: return "DLRM_OK";
+    case DLRM_ERR_NULL: return "DLRM_ERR_NULL: a required pointer is NULL";
+    case DLRM_ERR_SHAPE: return "DLRM_ERR_SHAPE: a size is out of range or sizes disagree";
+    case DLRM_ERR_UNSUPPORTED: return "DLRM_ERR_UNSUPPORTED: request beyond a documented limit";
+    case DLRM_ERR_WORKSPACE: return "DLRM_ERR_WORKSPACE: workspace too small or misaligned";
+    case DLRM_ERR_HIP: return "DLRM_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown dlrm_status";
+  }
+}
+
+int dlrm_abi_version(void) { return DLRM_ABI_VERSION; }
+
+int emb_bag_sum_multi(int32_t num_tables, int32_t batch, int32_t dim,
+                      const float *const *tables, const int64_t *rows,
+                      const int32_t *const *indices, const int32_t *const *offsets,
+                      const int64_t *n_idx, float *out, void *stream) {
+  TableSet ts;
+  bool csr, vec_ok;
+  int rc = pack_tables(num_tables, batch, dim, tables, rows, indices, offsets, n_idx, ts, csr,
+                       vec_ok);
+  if (rc) return rc;
+  if (!out) return DLRM_ERR_NULL;
+  if (batch == 0) return DLRM_OK;
+  const bool vec4 = vec_ok && aligned16(out);
+  return hip_status(launch_emb_bag(ts, csr, batch, num_tables, dim, vec4, out,
+                                   (hipStream_t)stream));
+}
+
+int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim, const float *dense,
+                            const float *emb, float *out, void *stream) {
+  if (batch < 0 || num_emb < 1 || num_emb > DLRM_MAX_TABLES || dim < 1 || dim > DLRM_MAX_DIM)
+    return DLRM_ERR_SHAPE;
+  if (!dense || !emb || !out) return DLRM_ERR_NULL;
+  if (batch == 0) return DLRM_OK;
+  const bool vec4 = dim % 4 == 0 && aligned16(dense) && aligned16(emb);
+  InteractParams ip{};
+  int threads = 0;
+  if (!plan_interact(batch, num_emb, dim, vec4, ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  ip.copy_dense = 1;
+  ip.dense = dense;
+  ip.ld_dense = dim;
+  ip.out = out;
+  ip.ld_out = dim + ip.P;
+  ip.out_vec = aligned16(out) && ip.ld_out % 4 == 0;
+  ip.emb_out = nullptr;
+  ip.emb_in = emb;
+  return hip_status(launch_interact(nullptr, false, ip, threads, vec4, (hipStream_t)stream));
+}
+
+int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
+                      const float *const *tables, const int64_t *rows,
+                      const int32_t *const *indices, const int32_t *const *offsets,
+                      const int64_t *n_idx, const float *dense, float *out, float *emb_out,
+                      void *stream) {
+  TableSet ts;
+  bool csr, vec_ok;
+  int rc = pack_tables(num_tables, batch, dim, tables, rows, indices, offsets, n_idx, ts, csr,
+                       vec_ok);
+  if (rc) return rc;
+  if (!dense || !out) return DLRM_ERR_NULL;
+  if (batch == 0) return DLRM_OK;
+  const bool vec4 = vec_ok && aligned16(dense) && (!emb_out || aligned16(emb_out));
+  InteractParams ip{};
+  int threads = 0;
+  if (!plan_interact(batch, num_tables, dim, vec4, ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  ip.copy_dense = 1;
+  ip.dense = dense;
+  ip.ld_dense = dim;
+  ip.out = out;
+  ip.ld_out = dim + ip.P;
+  ip.out_vec = aligned16(out) && ip.ld_out % 4 == 0;
+  ip.emb_out = emb_out;
+  ip.emb_in = nullptr;
+  return hip_status(launch_interact(&ts, csr, ip, threads, vec4, (hipStream_t)stream));
+}
+
+int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda,
+                    const float *w, const float *bias, int32_t act, float *c, int64_t ldc,
+                    void *stream) {
+  if (m < 0 || n < 1 || k < 1 || lda < k || ldc < n || !valid_act(act)) return DLRM_ERR_SHAPE;
+  if (!a || !w || !c) return DLRM_ERR_NULL;
+  if (m == 0) return DLRM_OK;
+  return hip_status(launch_linear(m, n, k, a, lda, w, bias, act, c, ldc, (hipStream_t)stream));
+}
+
+size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t batch) {
+  ForwardLayout lay;
+  if (plan_forward(model, batch, lay) != DLRM_OK) return 0;
+  return lay.total;
+}
+
+int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
+                 const int32_t *const *indices, const int32_t *const *offsets,
+                 const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+  ForwardLayout lay;
+  int rc = plan_forward(model, batch, lay);
+  if (rc) return rc;
+  TableSet ts;
+  bool csr, vec_ok;
+  rc = pack_tables(model->num_tables, batch, model->dim, model->tables, model->rows, indices,
+                   offsets, n_idx, ts, csr, vec_ok);
+  if (rc) return rc;
+  if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
+  if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return DLRM_ERR_WORKSPACE;
+  if (batch == 0) return DLRM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const int B = batch, D = model->dim, K = model->num_tables;
+  char *ws = static_cast<char *>(workspace);
+  float *R = reinterpret_cast<float *>(ws + lay.off_R);
+  float *buf[2] = {reinterpret_cast<float *>(ws + lay.off_buf0),
+                   reinterpret_cast<float *>(ws + lay.off_buf1)};
+
+  // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
+  const float *x = dense_in;
+  int64_t ldx = model->bottom[0].in_features;
+  for (int l = 0; l < model->num_bottom; ++l) {
+    const dlrm_layer &L = model->bottom[l];
+    const bool last = l + 1 == model->num_bottom;
+    float *y = last ? R : buf[l & 1];
+    const int64_t ldy = last ? lay.ldR : lay.ld_buf;
+    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
+                                  L.act, y, ldy, st));
+    if (rc) return rc;
+    x = y;
+    ldx = ldy;
+  }
+
+  // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
+  const bool vec4 = vec_ok && lay.ldR % 4 == 0;
+  InteractParams ip{};
+  int threads = 0;
+  if (!plan_interact(B, K, D, vec4, ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  ip.copy_dense = 0;
+  ip.dense = R;
+  ip.ld_dense = lay.ldR;
+  ip.out = R;
+  ip.ld_out = lay.ldR;
+  ip.out_vec = 1;
+  ip.emb_out = nullptr;
+  ip.emb_in = nullptr;
+  rc = hip_status(launch_interact(&ts, csr, ip, threads, vec4, st));
+  if (rc) return rc;
+
+  // Top MLP on cat(dense, dots) = R.
+  x = R;
+  ldx = lay.ldR;
+  for (int l = 0; l < model->num_top; ++l) {
+    const dlrm_layer &L = model->top[l];
+    const bool last = l + 1 == model->num_top;
+    float *y = last ? out : buf[l & 1];
+    const int64_t ldy = last ? L.out_features : lay.ld_buf;
+    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
+                                  L.act, y, ldy, st));
+    if (rc) return rc;
+    x = y;
+    ldx = ldy;
+  }
+  return DLRM_OK;
+}
+
+}  // extern "C"

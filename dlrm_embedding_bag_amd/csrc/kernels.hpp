@@ -1,0 +1,42 @@
+// kernels.hpp -- host-side launchers of the HIP kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dlrm {
+
+// Geometry and buffers of one interaction launch.
+struct InteractParams {
+  int B, K, D, P;   // batch, pooled vectors per sample, dim, pairs F(F-1)/2
+  int S;            // samples per workgroup
+  int DP;           // LDS row stride in floats
+  int G;            // lanes per gathered row
+  int lds_bytes;    // dynamic LDS per workgroup
+  int copy_dense;   // write dense into out[:, 0:D]
+  int out_vec;      // out rows are 16-byte aligned (vector dense copy)
+  const float *dense;
+  int64_t ld_dense;
+  float *out;
+  int64_t ld_out;
+  float *emb_out;        // optional (B, K, D) copy of the pooled vectors
+  const float *emb_in;   // (B, K, D) input of the interaction-only kernel
+};
+
+hipError_t launch_emb_bag(const TableSet &ts, bool csr, int B, int K, int D, bool vec4,
+                          float *out, hipStream_t stream);
+
+// Fills the geometry fields of `ip`; false if one sample's tile exceeds LDS.
+bool plan_interact(int B, int K, int D, bool vec4, InteractParams &ip, int &threads);
+
+// ts == nullptr: interaction over ip.emb_in; otherwise fused gather + interaction.
+hipError_t launch_interact(const TableSet *ts, bool csr, const InteractParams &ip, int threads,
+                           bool vec4, hipStream_t stream);
+
+// C = act(A W^T + bias); A (M, K) stride lda, W (N, K) dense, C stride ldc.
+hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const float *W,
+                         const float *bias, int act, float *C, int64_t ldc, hipStream_t stream);
+
+}  // namespace dlrm

@@ -1,0 +1,275 @@
+// linear.hip -- fused linear + bias + activation for gfx950:
+//   C[m, n] = act(bias[n] + sum_k A[m, k] W[n, k])
+// ([FASTPATHS] matmul2d.rs, Activation epilogue; the linear_bias_relu /
+// linear_bias_sigmoid frontends), where [FASTPATHS] = page "luminal_python:
+// vanilla-PyTorch DLRMv1 fast paths + batched FFI + input cache".
+//
+// The MLP layers are the one dense contraction of the path, so they run on
+// the f32 matrix cores: v_mfma_f32_16x16x4f32 (16x16 output block, k = 4 per
+// instruction, full f32 precision).  Both A and W are k-contiguous; each lane
+// reads a float4 of 4 consecutive k and feeds its components to 4 successive
+// MFMAs, which permutes the order of the k sum but not its terms.  W is fed
+// as the matrix core's first operand, so a lane's 4 accumulators are 4
+// consecutive output columns of one row: the epilogue adds a float4 of bias,
+// applies the activation and stores a float4.
+//
+// Tiles: BM x BN per 256-thread workgroup (4 waves in 2 x 2), BK = 32 staged
+// through LDS (row stride 36 floats: the 16 rows a ds_read_b128 touches start
+// on different banks), with the next k-slab prefetched into registers while
+// the current one is multiplied.  Tiles are assigned to XCDs in contiguous
+// m-major runs so the workgroups that share rows of A share an L2.
+//
+// Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
+// bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dlrm {
+
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBK = 32;
+constexpr int kLdsStride = kBK + 4;
+
+__device__ __forceinline__ float apply_act(float x, int act) {
+  if (act == 1) return x > 0.0f ? x : 0.0f;
+  if (act == 2) return 1.0f / (1.0f + expf(-x));
+  return x;
+}
+
+// float4 of row `row`, columns k..k+3 of a (nrows, K) matrix with stride ld;
+// zero outside the matrix.
+template <bool VEC>
+__device__ __forceinline__ float4 load_k4(const float *__restrict__ base, int64_t ld, int row,
+                                          int nrows, int k, int K) {
+  if (row >= nrows) return make_float4(0.f, 0.f, 0.f, 0.f);
+  const float *p = base + (int64_t)row * ld + k;
+  if (VEC && k + 3 < K) return *reinterpret_cast<const float4 *>(p);
+  float4 v;
+  v.x = (k + 0 < K) ? p[0] : 0.f;
+  v.y = (k + 1 < K) ? p[1] : 0.f;
+  v.z = (k + 2 < K) ? p[2] : 0.f;
+  v.w = (k + 3 < K) ? p[3] : 0.f;
+  return v;
+}
+
+template <int BM, int BN, bool VA, bool VW, bool VC>
+__global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K,
+                                                   const float *__restrict__ A, int64_t lda,
+                                                   const float *__restrict__ W,
+                                                   const float *__restrict__ bias, int act,
+                                                   float *__restrict__ C, int64_t ldc,
+                                                   int tiles_n, int xcd_chunk) {
+  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int A_V4 = BM * kBK / 4 / 256;  // float4 loads per thread per slab
+  constexpr int W_V4 = BN * kBK / 4 / 256;
+  static_assert(A_V4 >= 1 && W_V4 >= 1, "tile too small for 256 threads");
+
+  __shared__ float As[BM * kLdsStride];
+  __shared__ float Ws[BN * kLdsStride];
+
+  // XCD-aware tile order: workgroup ids are dealt to the 8 XCDs round robin;
+  // give XCD x the contiguous m-major tile range [x*chunk, (x+1)*chunk).
+  int bid = blockIdx.x;
+  if (xcd_chunk > 0) bid = (bid & 7) * xcd_chunk + (bid >> 3);
+  const int tm_blk = bid / tiles_n;
+  const int tn_blk = bid - tm_blk * tiles_n;
+  const int m0 = tm_blk * BM, n0 = tn_blk * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, lq = lane >> 4;
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  float4 ra[A_V4], rw[W_V4];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < A_V4; ++i) {
+      const int v = tid + 256 * i;
+      const int row = v >> 3, c4 = v & 7;
+      ra[i] = load_k4<VA>(A, lda, m0 + row, M, kb + 4 * c4, K);
+    }
+#pragma unroll
+    for (int i = 0; i < W_V4; ++i) {
+      const int v = tid + 256 * i;
+      const int row = v >> 3, c4 = v & 7;
+      rw[i] = load_k4<VW>(W, K, n0 + row, N, kb + 4 * c4, K);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < A_V4; ++i) {
+      const int v = tid + 256 * i;
+      const int row = v >> 3, c4 = v & 7;
+      *reinterpret_cast<float4 *>(&As[row * kLdsStride + 4 * c4]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < W_V4; ++i) {
+      const int v = tid + 256 * i;
+      const int row = v >> 3, c4 = v & 7;
+      *reinterpret_cast<float4 *>(&Ws[row * kLdsStride + 4 * c4]) = rw[i];
+    }
+  };
+
+  const int nslab = (K + kBK - 1) / kBK;
+  fetch(0);
+  stash();
+  __syncthreads();
+  for (int sl = 0; sl < nslab; ++sl) {
+    if (sl + 1 < nslab) fetch((sl + 1) * kBK);
+#pragma unroll
+    for (int kq = 0; kq < kBK; kq += 16) {
+      float4 af[TM], wf[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+        af[a] = *reinterpret_cast<const float4 *>(
+            &As[(wm * WM + a * 16 + l16) * kLdsStride + kq + 4 * lq]);
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        wf[b] = *reinterpret_cast<const float4 *>(
+            &Ws[(wn * WN + b * 16 + l16) * kLdsStride + kq + 4 * lq]);
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].x, af[a].x, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].y, af[a].y, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].z, af[a].z, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].w, af[a].w, acc[a][b], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    if (sl + 1 < nslab) {
+      stash();
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: lane holds C[m][n .. n+3] for m = .. + l16, n = .. + 4*lq.
+#pragma unroll
+  for (int b = 0; b < TN; ++b) {
+    const int n = n0 + wn * WN + b * 16 + 4 * lq;
+    float bv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) bv[v] = (bias && n + v < N) ? bias[n + v] : 0.0f;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int m = m0 + wm * WM + a * 16 + l16;
+      if (m >= M) continue;
+      float o[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v] = apply_act(acc[a][b][v] + bv[v], act);
+      float *cp = C + (int64_t)m * ldc + n;
+      if (VC && n + 3 < N) {
+        *reinterpret_cast<float4 *>(cp) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (n + v < N) cp[v] = o[v];
+      }
+    }
+  }
+}
+
+// N <= 8: each wave computes 4 rows at a time, 16 lanes per row.
+template <bool VEC>
+__global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K,
+                                                   const float *__restrict__ A, int64_t lda,
+                                                   const float *__restrict__ W,
+                                                   const float *__restrict__ bias, int act,
+                                                   float *__restrict__ C, int64_t ldc) {
+  const int lane = threadIdx.x & 63;
+  const int row_in_wave = lane >> 4;
+  const int c = lane & 15;
+  const int m = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 4 + row_in_wave;
+  // All 16 lanes of a row stay active through the DPP sums, so rows past M
+  // compute on row M-1 and skip the store.
+  const int mr = m < M ? m : M - 1;
+  const float *a = A + (int64_t)mr * lda;
+  for (int n = 0; n < N; ++n) {
+    const float *w = W + (int64_t)n * K;
+    float acc = 0.0f;
+    if (VEC) {
+      for (int k = 4 * c; k < K; k += 64) {
+        const float4 x = *reinterpret_cast<const float4 *>(a + k);
+        const float4 y = *reinterpret_cast<const float4 *>(w + k);
+        acc = vdot_acc(x, y, acc);
+      }
+    } else {
+      for (int k = c; k < K; k += 16) acc = __builtin_fmaf(a[k], w[k], acc);
+    }
+    acc = row16_sum(acc);
+    if (c == 0 && m < M) {
+      const float bv = bias ? bias[n] : 0.0f;
+      C[(int64_t)m * ldc + n] = apply_act(acc + bv, act);
+    }
+  }
+}
+
+template <int BM, int BN>
+hipError_t launch_gemm_cfg(int M, int N, int K, const float *A, int64_t lda, const float *W,
+                           const float *bias, int act, float *C, int64_t ldc, bool va, bool vw,
+                           bool vc, hipStream_t stream) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  const int xcd_chunk = (tiles % 8 == 0) ? (int)(tiles / 8) : 0;
+  dim3 grid((unsigned)tiles), block(256);
+#define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                     \
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_, W_, C_>), grid, block, 0, stream, M, N, K, A, \
+                     lda, W, bias, act, C, ldc, tiles_n, xcd_chunk)
+  if (va && vw && vc)
+    DLRM_GEMM_LAUNCH(true, true, true);
+  else if (va && !vw && vc)
+    DLRM_GEMM_LAUNCH(true, false, true);
+  else if (!va && vw && vc)
+    DLRM_GEMM_LAUNCH(false, true, true);
+  else if (!va && !vw && vc)
+    DLRM_GEMM_LAUNCH(false, false, true);
+  else if (va && vw)
+    DLRM_GEMM_LAUNCH(true, true, false);
+  else
+    DLRM_GEMM_LAUNCH(false, false, false);
+#undef DLRM_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const float *W,
+                         const float *bias, int act, float *C, int64_t ldc, hipStream_t stream) {
+  const bool va = aligned16(A) && lda % 4 == 0;
+  const bool vw = aligned16(W) && K % 4 == 0;
+  const bool vc = aligned16(C) && ldc % 4 == 0;
+  if (N <= 8) {
+    const int rows_per_block = 16;
+    dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(256);
+    if (va && vw && K % 4 == 0)
+      hipLaunchKernelGGL((gemv_kernel<true>), grid, block, 0, stream, M, N, K, A, lda, W, bias,
+                         act, C, ldc);
+    else
+      hipLaunchKernelGGL((gemv_kernel<false>), grid, block, 0, stream, M, N, K, A, lda, W, bias,
+                         act, C, ldc);
+    return hipGetLastError();
+  }
+  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t12864 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
+  if (t128 >= 512)
+    return launch_gemm_cfg<128, 128>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc, stream);
+  if (t12864 >= 512)
+    return launch_gemm_cfg<128, 64>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc, stream);
+  return launch_gemm_cfg<64, 64>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc, stream);
+}
+
+}  // namespace dlrm

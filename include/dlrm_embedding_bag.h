@@ -1,0 +1,215 @@
+/*
+ * dlrm_embedding_bag.h -- C ABI of the MI355X (gfx950) DLRMv1 forward hot path.
+ *
+ * Library: libdlrm_mi355x.so (hand-written HIP kernels for CDNA4).
+ *
+ * Citations name the web page an operation follows and the section on it:
+ *   [FASTPATHS] = page "luminal_python: vanilla-PyTorch DLRMv1 fast paths +
+ *                 batched FFI + input cache" (compare main...vanilla-pytorch)
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers unless marked [host].  [host] arrays are
+ *    read during the call only and may be freed as soon as it returns.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    pointer after a call returns and has no global mutable state, so calls
+ *    are re-entrant ([FASTPATHS] runtime.rs: non-owning views over caller
+ *    memory).
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Every call only enqueues work on `stream` and never synchronizes
+ *    ([FASTPATHS] runtime.rs: execute() stays capturable, no trailing sync).
+ *  - Floating point data is float32, row-major and dense unless a leading
+ *    dimension says otherwise.  Indices and offsets are int32 (the caller
+ *    narrows int64 indices, as the pages' Python bridge does).
+ *  - Outputs must not overlap inputs.
+ *  - Return value: a dlrm_status.  Argument errors are reported before any
+ *    work is enqueued; DLRM_ERR_HIP reports a failed launch.
+ *  - Index values are trusted, as on the pages ([FASTPATHS] embedding_bag.rs:
+ *    the kernel trusts user indices): every index of table k must lie in
+ *    [0, rows[k]); an index outside it is undefined behaviour.  Explicit
+ *    offsets are clamped into [0, n_idx[k]] on the device, so a bad offset
+ *    gives a wrong bag, never an out-of-bounds index read.
+ *  - Vectorised paths are used when dim % 4 == 0 and the relevant pointers
+ *    and leading dimensions are 16-byte aligned; anything else takes a scalar
+ *    path.  Alignment is never an error.
+ */
+#ifndef DLRM_EMBEDDING_BAG_H
+#define DLRM_EMBEDDING_BAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DLRM_API __attribute__((visibility("default")))
+#else
+#define DLRM_API
+#endif
+
+typedef enum dlrm_status {
+  DLRM_OK = 0,
+  DLRM_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  DLRM_ERR_SHAPE = 2,       /* a size is out of range or sizes disagree      */
+  DLRM_ERR_UNSUPPORTED = 3, /* valid request beyond a documented limit       */
+  DLRM_ERR_WORKSPACE = 4,   /* workspace smaller than required               */
+  DLRM_ERR_HIP = 5          /* the HIP runtime reported an error             */
+} dlrm_status;
+
+typedef enum dlrm_act {
+  DLRM_ACT_NONE = 0,
+  DLRM_ACT_RELU = 1,   /* x > 0 ? x : 0                                     */
+  DLRM_ACT_SIGMOID = 2 /* 1 / (1 + exp(-x))                                 */
+} dlrm_act;
+
+/* Documented limits. */
+#define DLRM_MAX_TABLES 64        /* K per call (pointer table travels by value) */
+#define DLRM_MAX_DIM 1024         /* embedding dim D                             */
+
+/* Human-readable name of a status code (static string, never NULL). */
+DLRM_API const char *dlrm_status_string(int status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+DLRM_API int dlrm_abi_version(void);
+#define DLRM_ABI_VERSION 1
+
+/*
+ * emb_bag_sum_multi -- K EmbeddingBag(sum) lookups in one launch
+ * ([FASTPATHS] embedding_bag.rs, module doc "Semantics" and
+ * MultiTableEmbeddingBagSumKernel doc; translator dispatch,
+ * aten._embedding_bag_forward_only lowering):
+ *
+ *   out[b, k, :] = sum over l in bag(b, k) of tables[k][indices[k][l], :]
+ *
+ *   num_tables  K, 1 <= K <= DLRM_MAX_TABLES
+ *   batch       B >= 0 (0: nothing to do, DLRM_OK)
+ *   dim         D, 1 <= D <= DLRM_MAX_DIM (shared by all tables)
+ *   tables      [host] K device pointers; table k is (rows[k], D) float32
+ *   rows        [host] K row counts (>= 1; row counts may differ per table)
+ *   indices     [host] K device pointers; indices[k] is (n_idx[k],) int32
+ *   offsets     [host] NULL for uniform stride: bag(b, k) = [b*L_k, (b+1)*L_k)
+ *               with L_k = n_idx[k] / B (n_idx[k] must be a multiple of B);
+ *               or K device pointers to (B,) int32 bag starts (CSR, as
+ *               torch.nn.EmbeddingBag with include_last_offset = False: the
+ *               last bag ends at n_idx[k]; an empty bag pools to 0).
+ *   n_idx       [host] K index counts, 0 <= n_idx[k] <= INT32_MAX
+ *   out         (B, K, D) float32
+ * Sum mode only; per-sample weights, padding_idx and include_last_offset are
+ * not part of the pages' path and have no parameter here.
+ */
+DLRM_API int emb_bag_sum_multi(int32_t num_tables, int32_t batch, int32_t dim,
+                      const float *const *tables, const int64_t *rows,
+                      const int32_t *const *indices,
+                      const int32_t *const *offsets, const int64_t *n_idx,
+                      float *out, void *stream);
+
+/*
+ * dlrm_interact_lower_tri -- strict-lower-triangle pairwise-dot interaction
+ * ([FASTPATHS] dlrm_interact.rs, PairwiseDotLowerTriStackedKernel: feature 0
+ * is the dense vector, features 1..N the stacked embeddings; pair p = (i, j),
+ * i > j, in torch.tril_indices(F, F, -1) order; translator dispatch: the top
+ * MLP reads cat(dense, dots)):
+ *
+ *   X_b = [dense[b]; emb[b, 0]; ...; emb[b, N-1]]           F = N + 1 rows
+ *   out[b, 0:D]       = dense[b]                             (exact copy)
+ *   out[b, D + p]     = dot(X_b[i], X_b[j]),  (i, j) = pair p
+ *
+ *   batch    B >= 0 (0: nothing to do, DLRM_OK)
+ *   num_emb  N, 1 <= N <= DLRM_MAX_TABLES
+ *   dim      D, 1 <= D <= DLRM_MAX_DIM, with F * D * 4 bytes of features per
+ *            sample fitting the 64 KiB shared-memory budget (else
+ *            DLRM_ERR_UNSUPPORTED)
+ *   dense    (B, D) float32
+ *   emb      (B, N, D) float32
+ *   out      (B, D + F(F-1)/2) float32
+ */
+DLRM_API int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim,
+                            const float *dense, const float *emb, float *out,
+                            void *stream);
+
+/*
+ * dlrm_emb_interact -- emb_bag_sum_multi fused with dlrm_interact_lower_tri
+ * in one launch: the pooled vectors stay on chip and go straight into the
+ * interaction ([FASTPATHS] commit message: the multi-table emb-bag kernel
+ * feeding the stacked pairwise-dot kernel).  Arguments as in the two calls
+ * above; emb_out, if not NULL, also receives the (B, K, D) pooled tensor.
+ *   dense    (B, D) float32
+ *   out      (B, D + F(F-1)/2) float32, F = K + 1
+ */
+DLRM_API int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
+                      const float *const *tables, const int64_t *rows,
+                      const int32_t *const *indices,
+                      const int32_t *const *offsets, const int64_t *n_idx,
+                      const float *dense, float *out, float *emb_out,
+                      void *stream);
+
+/*
+ * linear_bias_act -- fused linear layer ([FASTPATHS] matmul2d.rs, Activation
+ * epilogue; linear_bias / linear_bias_relu / linear_bias_sigmoid):
+ *
+ *   c[m, n] = act(bias[n] + sum_k a[m, k] * w[n, k])
+ *
+ *   m >= 0 (0: nothing to do), n >= 1, k >= 1
+ *   a        (m, k) float32 with row stride lda >= k
+ *   w        (n, k) float32, dense (the nn.Linear weight layout)
+ *   bias     (n,) float32, or NULL for no bias
+ *   act      a dlrm_act
+ *   c        (m, n) float32 with row stride ldc >= n
+ */
+DLRM_API int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a,
+                    int64_t lda, const float *w, const float *bias, int32_t act,
+                    float *c, int64_t ldc, void *stream);
+
+/* One MLP layer of a dlrm_model. */
+typedef struct dlrm_layer {
+  int32_t in_features;
+  int32_t out_features;
+  const float *weight; /* (out_features, in_features) float32, device */
+  const float *bias;   /* (out_features,) float32, device, or NULL    */
+  int32_t act;         /* a dlrm_act                                  */
+} dlrm_layer;
+
+/* A DLRMv1 model: bottom MLP, K embedding tables, top MLP.  All arrays of
+ * this struct are [host]; the weights and tables they point to are device
+ * memory owned by the caller. */
+typedef struct dlrm_model {
+  int32_t num_bottom;        /* >= 1                                       */
+  const dlrm_layer *bottom;  /* [host] bottom[last].out_features == dim    */
+  int32_t num_top;           /* >= 1                                       */
+  const dlrm_layer *top;     /* [host] top[0].in_features == dim + P       */
+  int32_t num_tables;        /* K                                          */
+  int32_t dim;               /* D                                          */
+  const float *const *tables;/* [host] K device pointers, (rows[k], D)     */
+  const int64_t *rows;       /* [host] K row counts                        */
+} dlrm_model;
+
+/* Bytes of device workspace dlrm_forward needs for `batch` samples. */
+DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t batch);
+
+/*
+ * dlrm_forward -- the DLRMv1 forward ([FASTPATHS] commit message and
+ * translator notes: bottom MLP on the dense features, one EmbeddingBag(sum)
+ * per table, pairwise-dot interaction with the bottom-MLP output as feature
+ * 0, top MLP on cat(dense, dots) ending in a sigmoid):
+ *
+ *   d   = bottom(dense_in)                      (B, D)
+ *   R   = dlrm_emb_interact(tables, indices, d) (B, D + P)
+ *   out = top(R)                                (B, top[last].out_features)
+ *
+ *   dense_in   (B, bottom[0].in_features) float32
+ *   indices, offsets, n_idx as in emb_bag_sum_multi
+ *   out        (B, top[last].out_features) float32
+ *   workspace  device memory of at least dlrm_forward_workspace_bytes bytes,
+ *              256-byte aligned; its contents are scratch
+ */
+DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
+                 const int32_t *const *indices, const int32_t *const *offsets,
+                 const int64_t *n_idx, float *out, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLRM_EMBEDDING_BAG_H */

@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, and rejects bad arguments before it
+enqueues any work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from dlrm_embedding_bag_amd import abi
+
+HEADER = os.path.join(ROOT, "include", "dlrm_embedding_bag.h")
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(abi.LIB_PATH):
+        from dlrm_embedding_bag_amd import build
+        build.build()
+    return abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^DLRM_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)
+
+
+def test_header_declares_the_binding_names():
+    assert sorted(declared_functions()) == sorted(abi.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.dlrm_abi_version() == 1
+    for code, name in abi.STATUS_NAMES.items():
+        assert lib.dlrm_status_string(code).decode().startswith(name)
+    assert lib.dlrm_status_string(99) == b"unknown dlrm_status"
+
+
+def _tables(K, rows=10):
+    t = (ctypes.c_void_p * K)(*[FAKE] * K)
+    r = (ctypes.c_int64 * K)(*[rows] * K)
+    i = (ctypes.c_void_p * K)(*[FAKE] * K)
+    return t, r, i
+
+
+def _n(K, n):
+    return (ctypes.c_int64 * K)(*[n] * K)
+
+
+def test_emb_bag_argument_errors(lib):
+    t, r, i = _tables(2)
+    f = lib.emb_bag_sum_multi
+    assert f(0, 4, 8, t, r, i, None, _n(2, 8), FAKE, None) == 2          # K < 1
+    assert f(65, 4, 8, t, r, i, None, _n(2, 8), FAKE, None) == 2         # K > max
+    assert f(2, -1, 8, t, r, i, None, _n(2, 8), FAKE, None) == 2         # B < 0
+    assert f(2, 4, 0, t, r, i, None, _n(2, 8), FAKE, None) == 2          # D < 1
+    assert f(2, 4, 1025, t, r, i, None, _n(2, 8), FAKE, None) == 2       # D > max
+    assert f(2, 4, 8, None, r, i, None, _n(2, 8), FAKE, None) == 1       # tables NULL
+    assert f(2, 4, 8, t, r, i, None, _n(2, 8), None, None) == 1          # out NULL
+    assert f(2, 4, 8, t, r, i, None, _n(2, 7), FAKE, None) == 2          # n_idx % B
+    t0, r0, i0 = _tables(2)
+    t0[1] = None
+    assert f(2, 4, 8, t0, r0, i0, None, _n(2, 8), FAKE, None) == 1       # tables[1] NULL
+    r0 = (ctypes.c_int64 * 2)(10, 0)
+    assert f(2, 4, 8, t, r0, i, None, _n(2, 8), FAKE, None) == 2         # rows < 1
+    assert f(2, 4, 8, t, r, i, None, _n(2, 2**31), FAKE, None) == 2      # n_idx > INT32_MAX
+    offs = (ctypes.c_void_p * 2)(FAKE, None)
+    assert f(2, 4, 8, t, r, i, offs, _n(2, 7), FAKE, None) == 1          # offsets[1] NULL
+    # B == 0 is a valid no-op that launches nothing
+    assert f(2, 0, 8, t, r, i, None, _n(2, 0), FAKE, None) == 0
+
+
+def test_interact_argument_errors(lib):
+    f = lib.dlrm_interact_lower_tri
+    assert f(4, 0, 8, FAKE, FAKE, FAKE, None) == 2
+    assert f(4, 65, 8, FAKE, FAKE, FAKE, None) == 2
+    assert f(4, 2, 0, FAKE, FAKE, FAKE, None) == 2
+    assert f(4, 2, 8, None, FAKE, FAKE, None) == 1
+    assert f(4, 2, 8, FAKE, FAKE, None, None) == 1
+    # one sample's F x D tile beyond the LDS budget: 65 x 1024 floats
+    assert f(4, 64, 1024, FAKE, FAKE, FAKE, None) == 3
+    assert f(0, 2, 8, FAKE, FAKE, FAKE, None) == 0
+
+
+def test_emb_interact_argument_errors(lib):
+    t, r, i = _tables(3)
+    f = lib.dlrm_emb_interact
+    assert f(3, 4, 8, t, r, i, None, _n(3, 8), None, FAKE, None, None) == 1   # dense NULL
+    assert f(3, 4, 8, t, r, i, None, _n(3, 8), FAKE, None, None, None) == 1   # out NULL
+    assert f(3, 4, 8, t, r, i, None, _n(3, 9), FAKE, FAKE, None, None) == 2   # n_idx % B
+    t64, r64, i64 = _tables(64)
+    assert f(64, 4, 1024, t64, r64, i64, None, _n(64, 8), FAKE, FAKE, None, None) == 3
+
+
+def test_linear_argument_errors(lib):
+    f = lib.linear_bias_act
+    assert f(4, 0, 3, FAKE, 3, FAKE, None, 0, FAKE, 1, None) == 2     # n < 1
+    assert f(4, 2, 0, FAKE, 3, FAKE, None, 0, FAKE, 2, None) == 2     # k < 1
+    assert f(4, 2, 3, FAKE, 2, FAKE, None, 0, FAKE, 2, None) == 2     # lda < k
+    assert f(4, 2, 3, FAKE, 3, FAKE, None, 0, FAKE, 1, None) == 2     # ldc < n
+    assert f(4, 2, 3, FAKE, 3, FAKE, None, 3, FAKE, 2, None) == 2     # bad act
+    assert f(4, 2, 3, None, 3, FAKE, None, 0, FAKE, 2, None) == 1     # a NULL
+    assert f(4, 2, 3, FAKE, 3, None, None, 0, FAKE, 2, None) == 1     # w NULL
+    assert f(4, 2, 3, FAKE, 3, FAKE, None, 0, None, 2, None) == 1     # c NULL
+    assert f(0, 2, 3, FAKE, 3, FAKE, None, 0, FAKE, 2, None) == 0     # m == 0: no-op
+
+
+def _model(bottom, top, K, D):
+    bl = (abi.Layer * len(bottom))()
+    for n, (i, o, act) in enumerate(bottom):
+        bl[n].in_features, bl[n].out_features, bl[n].weight, bl[n].act = i, o, FAKE, act
+    tl = (abi.Layer * len(top))()
+    for n, (i, o, act) in enumerate(top):
+        tl[n].in_features, tl[n].out_features, tl[n].weight, tl[n].act = i, o, FAKE, act
+    t, r, _ = _tables(K)
+    m = abi.Model(len(bottom), bl, len(top), tl, K, D, t, r)
+    m._keep = (bl, tl, t, r)
+    return m
+
+
+def test_forward_workspace_and_errors(lib):
+    K, D = 26, 64
+    P = 27 * 26 // 2
+    good = _model([(13, 512, 1), (512, 256, 1), (256, 64, 1)],
+                  [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D)
+    B = 8192
+    ws = lib.dlrm_forward_workspace_bytes(ctypes.byref(good), B)
+    # R (B x 416 floats) + two ping-pong buffers (B x 512 floats)
+    assert ws == B * 416 * 4 + 2 * B * 512 * 4
+    bad_chain = _model([(13, 512, 1), (500, 64, 1)], [(D + P, 1, 2)], K, D)
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(bad_chain), B) == 0
+    bad_dim = _model([(13, 32, 1)], [(D + P, 1, 2)], K, D)       # bottom out != D
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(bad_dim), B) == 0
+    bad_top = _model([(13, 64, 1)], [(D + P + 1, 1, 2)], K, D)   # top in != D + P
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(bad_top), B) == 0
+    f = lib.dlrm_forward
+    idx = (ctypes.c_void_p * K)(*[FAKE] * K)
+    n = _n(K, B * 20)
+    assert f(ctypes.byref(bad_chain), B, FAKE, idx, None, n, FAKE, FAKE, ws, None) == 2
+    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws - 1, None) == 4
+    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE + 16, ws, None) == 4
+    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, None, ws, None) == 1
+    assert f(ctypes.byref(good), B, None, idx, None, n, FAKE, FAKE, ws, None) == 1
+    assert f(None, B, FAKE, idx, None, n, FAKE, FAKE, ws, None) == 1
+    assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, FAKE, ws, None) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    t = torch.zeros(4, 2)
+    with pytest.raises(ValueError, match="no CPU path"):
+        abi.emb_bag_sum_multi([t], [torch.zeros(4, dtype=torch.int32)], batch=2)
+    with pytest.raises(ValueError, match="no CPU path"):
+        abi.dlrm_interact_lower_tri(torch.zeros(2, 2), torch.zeros(2, 1, 2))
