@@ -121,8 +121,8 @@ int emb_bag_sum_multi(int32_t num_tables, int32_t batch, int32_t dim,
   int rc = pack_tables(num_tables, batch, dim, tables, rows, indices, offsets, n_idx, ts, csr,
                        vec_ok);
   if (rc) return rc;
+  if (batch == 0) return DLRM_OK;  // nothing to write: out may be NULL
   if (!out) return DLRM_ERR_NULL;
-  if (batch == 0) return DLRM_OK;
   const bool vec4 = vec_ok && aligned16(out);
   return hip_status(launch_emb_bag(ts, csr, batch, num_tables, dim, vec4, out,
                                    (hipStream_t)stream));
@@ -132,8 +132,8 @@ int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim, const f
                             const float *emb, float *out, void *stream) {
   if (batch < 0 || num_emb < 1 || num_emb > DLRM_MAX_TABLES || dim < 1 || dim > DLRM_MAX_DIM)
     return DLRM_ERR_SHAPE;
+  if (batch == 0) return DLRM_OK;  // nothing to read or write
   if (!dense || !emb || !out) return DLRM_ERR_NULL;
-  if (batch == 0) return DLRM_OK;
   const bool vec4 = dim % 4 == 0 && aligned16(dense) && aligned16(emb);
   InteractParams ip{};
   int threads = 0;
@@ -159,8 +159,8 @@ int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
   int rc = pack_tables(num_tables, batch, dim, tables, rows, indices, offsets, n_idx, ts, csr,
                        vec_ok);
   if (rc) return rc;
+  if (batch == 0) return DLRM_OK;  // nothing to read or write
   if (!dense || !out) return DLRM_ERR_NULL;
-  if (batch == 0) return DLRM_OK;
   const bool vec4 = vec_ok && aligned16(dense) && (!emb_out || aligned16(emb_out));
   InteractParams ip{};
   int threads = 0;
@@ -180,8 +180,8 @@ int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda
                     const float *w, const float *bias, int32_t act, float *c, int64_t ldc,
                     void *stream) {
   if (m < 0 || n < 1 || k < 1 || lda < k || ldc < n || !valid_act(act)) return DLRM_ERR_SHAPE;
+  if (m == 0) return DLRM_OK;  // nothing to read or write
   if (!a || !w || !c) return DLRM_ERR_NULL;
-  if (m == 0) return DLRM_OK;
   return hip_status(launch_linear(m, n, k, a, lda, w, bias, act, c, ldc, (hipStream_t)stream));
 }
 
@@ -203,10 +203,10 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
   rc = pack_tables(model->num_tables, batch, model->dim, model->tables, model->rows, indices,
                    offsets, n_idx, ts, csr, vec_ok);
   if (rc) return rc;
+  if (batch == 0) return DLRM_OK;  // nothing to read or write
   if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
   if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return DLRM_ERR_WORKSPACE;
-  if (batch == 0) return DLRM_OK;
   hipStream_t st = (hipStream_t)stream;
   const int B = batch, D = model->dim, K = model->num_tables;
   char *ws = static_cast<char *>(workspace);

@@ -172,24 +172,39 @@ def table_device(w: Workload, table: int, seed: int = 0, device="cuda", rows: in
     return t.mul_(w.table_std)
 
 
-def dyadic(rng: np.random.Generator, shape, scale_bits: int = 8) -> np.ndarray:
-    """Values n / 2^scale_bits with n uniform in [-128, 127], as float32.
+def dyadic(rng: np.random.Generator, shape, scale_bits: int = 8,
+           max_int: int = 128) -> np.ndarray:
+    """Values n / 2^scale_bits with n uniform in [-max_int, max_int), float32.
 
-    Sums and products of such values stay exactly representable in float32
-    for the sizes the tests use, so every summation order gives the same bits.
+    While every partial sum, in units of the smallest product, stays below
+    2^24, sums and products of such values are exact in float32, so every
+    summation order gives the same bits (see dyadic_max_int).
     """
-    n = rng.integers(-128, 128, size=shape, dtype=np.int64)
+    n = rng.integers(-max_int, max_int, size=shape, dtype=np.int64)
     return (n.astype(np.float32) / np.float32(2 ** scale_bits)).astype(np.float32)
+
+
+def dyadic_max_int(dim: int, bag: int) -> int:
+    """Largest power-of-two integer range keeping pooled dot products exact.
+
+    A bag sum is at most bag * max_int units and a dot of two of them at most
+    dim * bag^2 * max_int^2 units squared; that must stay below 2^24.
+    """
+    m = 128
+    while m > 1 and dim * max(bag, 1) ** 2 * m * m >= 2 ** 24:
+        m //= 2
+    return m
 
 
 def table_dyadic(w: Workload, table: int, seed: int = 0, rows: int = None) -> np.ndarray:
     r = w.rows if rows is None else rows
-    return dyadic(_rng(seed, 1000 + table), (r, w.dim))
+    return dyadic(_rng(seed, 1000 + table), (r, w.dim), max_int=dyadic_max_int(w.dim, w.bag))
 
 
 def dense_dyadic(w: Workload, seed: int = 0, batch: int = None) -> np.ndarray:
     b = w.batch if batch is None else batch
-    return dyadic(_rng(seed, 3000), (b, w.dense_in if w.dense_in else w.dim))
+    return dyadic(_rng(seed, 3000), (b, w.dense_in if w.dense_in else w.dim),
+                  max_int=dyadic_max_int(w.dim, w.bag))
 
 
 def mlp(widths, seed: int = 0, first_stream: int = 4000, bias_std: float = 0.0):

@@ -22,7 +22,8 @@
  *    narrows int64 indices, as the pages' Python bridge does).
  *  - Outputs must not overlap inputs.
  *  - Return value: a dlrm_status.  Argument errors are reported before any
- *    work is enqueued; DLRM_ERR_HIP reports a failed launch.
+ *    work is enqueued; DLRM_ERR_HIP reports a failed launch.  A zero batch
+ *    (or m == 0) is a no-op that returns DLRM_OK and reads no data pointer.
  *  - Index values are trusted, as on the pages ([FASTPATHS] embedding_bag.rs:
  *    the kernel trusts user indices): every index of table k must lie in
  *    [0, rows[k]); an index outside it is undefined behaviour.  Explicit
