@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the DLRMv1 forward hot path on one MI355X.
+
+Default workload: the fused multi-table EmbeddingBag(sum) gather + strict-
+lower-triangle pairwise-dot interaction at B=2048, K=32 tables x 1,000,000
+rows x D=64, 20 Zipf(1.05) indices per bag (dlrm_emb_interact, one launch).
+
+A step is one pass of that hot path over one batch.  Steps rotate through
+several independently drawn index batches, and by default the caches are
+flushed before each step (a 1 GiB read, outside the timed region: it evicts
+L2 and the Infinity Cache without leaving dirty lines to write back), so the
+table rows come from HBM as they would for a fresh batch; each step's kernel
+time is taken with HIP events on the stream the kernel runs on.  `--warm`
+skips the flush.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value         samples/s = B / mean event-timed step time
+  ms_per_step   mean event-timed step time
+  roofline      achieved = algorithmic bytes per launch / mean launch time,
+                against MI355X's 8 TB/s HBM peak; traffic = HBM bytes from the
+                committed rocprofv3 counter summary when it matches the
+                current kernel source, else null
+  cpu_baseline  the CPU oracle timed on the host on the same workload
+
+Options: --workload {nc32,nc32-uniform,mid,tiny,large,dlrm}, --sweep,
+--warm, --no-cpu-baseline, --copy-calibration (a plain 1 GiB copy, the
+scale for rocprofv3 FETCH_SIZE / WRITE_SIZE).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense f32 matrix, published
+METRIC = ("samples/sec + µs/forward (emb-bag+interact, B=2048 nc=32); "
+          "achieved HBM GB/s")
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = ["dlrm_embedding_bag_amd/csrc/emb_interact.hip",
+                  "dlrm_embedding_bag_amd/csrc/common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ byte models --
+def emb_interact_bytes_per_sample(K, D, L):
+    """Algorithmic bytes of the fused gather + interaction for one sample:
+    gathered rows K*L*D*4 + indices K*L*4 + dense D*4 + output (D+P)*4."""
+    F = K + 1
+    P = F * (F - 1) // 2
+    return K * L * D * 4 + K * L * 4 + D * 4 + (D + P) * 4
+
+
+# ------------------------------------------------------------- workloads --
+class EmbInteractCase:
+    """Device inputs for dlrm_emb_interact plus prepared C-ABI arguments."""
+
+    def __init__(self, w, nbatches, seed, stream, batch=None, num_tables=None,
+                 tables=None):
+        import numpy as np
+        import torch
+        from dlrm_embedding_bag_amd import abi, inputs
+        self.w = w
+        self.B = batch or w.batch
+        self.K = num_tables or w.num_tables
+        self.D = w.dim
+        self.L = w.bag
+        if tables is None:
+            if w.table_source == "device":
+                tables = [inputs.table_device(w, k, seed) for k in range(self.K)]
+            else:
+                tables = [torch.from_numpy(inputs.table_host(w, k, seed)).cuda()
+                          for k in range(self.K)]
+        self.tables = tables[:self.K]
+        self.lib = abi.load()
+        self.stream = stream
+        self.batches = []
+        for nb in range(nbatches):
+            idx = [torch.from_numpy(inputs.indices(w, k, seed + 7919 * nb, batch=self.B)).cuda()
+                   for k in range(self.K)]
+            dense = torch.from_numpy(inputs.dense(w, seed + 7919 * nb, batch=self.B)).cuda()
+            out = torch.empty((self.B, self.D + self.P), dtype=torch.float32, device="cuda")
+            args = (self.K, self.B, self.D, abi._ptr_array(self.tables),
+                    abi._i64_array([t.shape[0] for t in self.tables]), abi._ptr_array(idx),
+                    None, abi._i64_array([i.numel() for i in idx]), dense.data_ptr(),
+                    out.data_ptr(), None, stream.cuda_stream)
+            self.batches.append((idx, dense, out, args))
+        self.np = np
+
+    @property
+    def P(self):
+        F = self.K + 1
+        return F * (F - 1) // 2
+
+    def run(self, nb):
+        rc = self.lib.dlrm_emb_interact(*self.batches[nb % len(self.batches)][3])
+        if rc != 0:
+            raise RuntimeError(f"dlrm_emb_interact failed with status {rc}")
+
+    def bytes_per_launch(self):
+        return self.B * emb_interact_bytes_per_sample(self.K, self.D, self.L)
+
+    def distinct_rows_fraction(self, nb=0):
+        idx = self.batches[nb][0]
+        n = sum(int(i.unique().numel()) for i in idx)
+        return n / (self.B * self.K * self.L)
+
+
+def time_steps(case, steps, warmup, cold, flush_buf, stream):
+    """Event-timed steps; returns (per-step ms list, wall seconds of the bracket)."""
+    import torch
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):   # the flush is ordered before each step
+        for s in range(warmup):
+            if cold:
+                flush_buf.max()
+            case.run(s)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            if cold:
+                flush_buf.max()
+            evs[s][0].record(stream)
+            case.run(warmup + s)
+            evs[s][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in evs], wall
+
+
+# ----------------------------------------------------------- CPU baseline --
+def cpu_baseline(case, max_seconds=20.0):
+    """The CPU oracle on this workload: the full batch, tables copied to the
+    host, single-threaded C with fp64 sums (one run; more while under 2 s)."""
+    import numpy as np
+    import oracle
+    idx, dense, out, _ = case.batches[0]
+    log("cpu_baseline: copying tables to the host ...")
+    tables = [t.cpu().numpy() for t in case.tables]
+    idx_h = [i.cpu().numpy() for i in idx]
+    dense_h = dense.cpu().numpy()
+    B = case.B
+    # sample size: the whole batch, unless one pass would exceed the bound
+    samples = B
+    t0 = time.perf_counter()
+    probe = max(1, min(B, 64))
+    oracle.interact(dense_h[:probe], oracle.emb_bag_sum(
+        tables, [x[:probe * case.L] for x in idx_h], batch=probe))
+    est = (time.perf_counter() - t0) / probe * B
+    if est > max_seconds:
+        samples = max(1, int(B * max_seconds / est))
+    idx_s = [x[:samples * case.L] for x in idx_h]
+    runs = []
+    while True:
+        t0 = time.perf_counter()
+        E = oracle.emb_bag_sum(tables, idx_s, batch=samples)
+        R = oracle.interact(dense_h[:samples], E)
+        runs.append(time.perf_counter() - t0)
+        if sum(runs) > 2.0 or len(runs) >= 5:
+            break
+    t = statistics.median(runs)
+    got = out.cpu().numpy()[:samples]
+    err = float(np.abs(got - R).max())
+    return {"value": samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+            "sample": f"{samples} of {B} samples of the same batch, full tables in host "
+                      f"memory, single-threaded C oracle (fp64 sums), median of {len(runs)} "
+                      f"run(s) of {t:.3f} s",
+            "max_abs_diff_vs_gpu": err}
+
+
+def read_traffic(kernel_hash, workload):
+    try:
+        with open(COUNTERS_JSON) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = c.get(workload)
+    if not entry or entry.get("kernel_source_hash") != kernel_hash:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ main --
+def bench_emb_interact(args, stream):
+    import torch
+    from dlrm_embedding_bag_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    log(f"workload {w.name}: {w.description}")
+    t0 = time.perf_counter()
+    case = EmbInteractCase(w, args.batches, args.seed, stream)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+    cold = not args.warm
+    times, wall = time_steps(case, args.steps, args.warmup, cold, flush, stream)
+    ms = statistics.mean(times)
+    med = statistics.median(times)
+    log(f"{'cold' if cold else 'warm'} step: mean {ms * 1000:.1f} us, median "
+        f"{med * 1000:.1f} us over {args.steps} steps")
+    nbytes = case.bytes_per_launch()
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    extra = {"median_ms_per_step": med, "min_ms_per_step": min(times),
+             "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
+             "distinct_row_fraction": case.distinct_rows_fraction()}
+    if cold and not args.profile_run:
+        wt, _ = time_steps(case, args.steps, 2, False, flush, stream)
+        wms = statistics.mean(wt)
+        extra["warm_ms_per_step"] = wms
+        extra["warm_samples_per_s"] = case.B / (wms * 1e-3)
+        extra["warm_algorithmic_gbps"] = nbytes / (wms * 1e-3) / 1e9
+        log(f"warm step: mean {wms * 1000:.1f} us")
+    khash = kernel_source_hash()
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS,
+                "traffic": read_traffic(khash, w.name),
+                "kernel": "interact_kernel<4, fused> (dlrm_emb_interact)",
+                "algorithmic_bytes_per_launch": nbytes,
+                "compulsory_bytes_per_launch": int(
+                    extra["distinct_row_fraction"] * case.B * case.K * case.L * case.D * 4),
+                "kernel_source_hash": khash}
+    res = {"metric": METRIC, "value": case.B / (ms * 1e-3), "unit": "samples/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "us_per_forward": ms * 1e3, "achieved_hbm_gbps": achieved,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded N(0, 0.01^2) tables, Zipf/uniform int32 indices, "
+                   "N(0,1) dense)",
+           "config": {"workload": f"{w.name}: {w.description}", "batch": case.B,
+                      "num_tables": case.K, "dim": case.D, "bag": case.L, "rows": w.rows,
+                      "index_dist": w.dist, "cache": "cold" if cold else "warm",
+                      "index_batches": args.batches},
+           "roofline": roofline, "extra": extra}
+    if not args.profile_run:
+        extra["copy_gbps"] = copy_rate(stream)
+    if not args.no_cpu_baseline and not args.profile_run:
+        res["cpu_baseline"] = cpu_baseline(case)
+        log(f"cpu baseline: {res['cpu_baseline']['value']:.0f} samples/s")
+    return res
+
+
+def copy_rate(stream, mib=1024, reps=10):
+    """Read + write rate of a plain 1 GiB device copy (a practical HBM figure)."""
+    import torch
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def copy_calibration(stream):
+    """A plain device copy of 1 GiB, the known-size reference for the HBM
+    byte counters (FETCH_SIZE should read 1 GiB, WRITE_SIZE 1 GiB)."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 5 copies of 1 GiB done")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="nc32")
+    ap.add_argument("--batches", type=int, default=4, help="distinct index batches to rotate")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--warm", action="store_true", help="do not flush caches between steps")
+    ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the cold timed steps (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    from dlrm_embedding_bag_amd import abi
+    if not os.path.exists(abi.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    stream = torch.cuda.Stream()
+    if args.copy_calibration:
+        copy_calibration(stream)
+        return
+    res = bench_emb_interact(args, stream)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

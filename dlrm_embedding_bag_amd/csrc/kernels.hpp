@@ -13,7 +13,9 @@ struct InteractParams {
   int B, K, D, P;   // batch, pooled vectors per sample, dim, pairs F(F-1)/2
   int S;            // samples per workgroup
   int DP;           // LDS row stride in floats
+  int FR;           // LDS tile rows per sample (F, or F rounded up to 4)
   int G;            // lanes per gathered row
+  int Q;            // quads per 4 x 4 dot block (blocked interaction)
   int lds_bytes;    // dynamic LDS per workgroup
   int copy_dense;   // write dense into out[:, 0:D]
   int out_vec;      // out rows are 16-byte aligned (vector dense copy)
