@@ -13,11 +13,15 @@
 // consecutive output columns of one row: the epilogue adds a float4 of bias,
 // applies the activation and stores a float4.
 //
-// Tiles: BM x BN per 256-thread workgroup (4 waves in 2 x 2), BK = 32 staged
-// through LDS (row stride 36 floats: the 16 rows a ds_read_b128 touches start
-// on different banks), with the next k-slab prefetched into registers while
-// the current one is multiplied.  Tiles are assigned to XCDs in contiguous
-// m-major runs so the workgroups that share rows of A share an L2.
+// Tiles: BM x BN per workgroup of GM x GN waves (128 x 128 on 2 x 4 waves,
+// 64 x 64 or 64 x 32 on 2 x 2), BK = 32 staged through two LDS buffers (row
+// stride 36 floats: the 16 rows a ds_read_b128 touches start on different
+// banks): the next k-slab is loaded into registers and stored to the other
+// buffer while the current one is multiplied, one barrier per slab.  Full
+// slabs load without bounds tests (rows past the matrix are clamped and their
+// outputs masked at the store); only the last, partial slab tests k.  Tiles
+// are assigned to XCDs in contiguous m-major runs so the workgroups that share
+// rows of A share an L2.
 //
 // Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
 // bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
@@ -41,37 +45,51 @@ __device__ __forceinline__ float apply_act(float x, int act) {
   return x;
 }
 
-// float4 of row `row`, columns k..k+3 of a (nrows, K) matrix with stride ld;
-// zero outside the matrix.
+// float4 of columns k..k+3 of row `row` (already clamped into the matrix) of
+// a matrix with stride ld, for a slab known to lie inside K: no bounds tests.
 template <bool VEC>
-__device__ __forceinline__ float4 load_k4(const float *__restrict__ base, int64_t ld, int row,
-                                          int nrows, int k, int K) {
-  if (row >= nrows) return make_float4(0.f, 0.f, 0.f, 0.f);
+__device__ __forceinline__ float4 load_full(const float *__restrict__ base, int64_t ld, int row,
+                                            int k) {
   const float *p = base + (int64_t)row * ld + k;
-  if (VEC && k + 3 < K) return *reinterpret_cast<const float4 *>(p);
-  float4 v;
-  v.x = (k + 0 < K) ? p[0] : 0.f;
-  v.y = (k + 1 < K) ? p[1] : 0.f;
-  v.z = (k + 2 < K) ? p[2] : 0.f;
-  v.w = (k + 3 < K) ? p[3] : 0.f;
-  return v;
+  if (VEC) return *reinterpret_cast<const float4 *>(p);
+  return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-template <int BM, int BN, bool VA, bool VW, bool VC>
-__global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K,
-                                                   const float *__restrict__ A, int64_t lda,
-                                                   const float *__restrict__ W,
-                                                   const float *__restrict__ bias, int act,
-                                                   float *__restrict__ C, int64_t ldc,
-                                                   int tiles_n, int xcd_chunk) {
-  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int A_V4 = BM * kBK / 4 / 256;  // float4 loads per thread per slab
-  constexpr int W_V4 = BN * kBK / 4 / 256;
-  static_assert(A_V4 >= 1 && W_V4 >= 1, "tile too small for 256 threads");
+// Same for the last, partial slab: columns at or past K read as zero.  The
+// addresses are clamped so every load stays inside the row.
+__device__ __forceinline__ float4 load_tail(const float *__restrict__ base, int64_t ld, int row,
+                                            int k, int K) {
+  const float *p = base + (int64_t)row * ld;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int kk = k + e;
+    const float x = p[kk < K ? kk : K - 1];
+    v[e] = kk < K ? x : 0.0f;
+  }
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
 
-  __shared__ float As[BM * kLdsStride];
-  __shared__ float Ws[BN * kLdsStride];
+template <int BM, int BN, int GM, int GN, bool VA, bool VW, bool VC>
+__global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
+                                                            const float *__restrict__ A,
+                                                            int64_t lda,
+                                                            const float *__restrict__ W,
+                                                            const float *__restrict__ bias,
+                                                            int act, float *__restrict__ C,
+                                                            int64_t ldc, int tiles_n,
+                                                            int xcd_chunk) {
+  constexpr int NT = 64 * GM * GN;         // threads
+  constexpr int WM = BM / GM, WN = BN / GN;  // wave tile (GM x GN waves)
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int A_V4 = BM * kBK / 4 / NT;  // float4 loads per thread per slab
+  constexpr int W_V4 = BN * kBK / 4 / NT;
+  static_assert(A_V4 >= 1 && W_V4 >= 1 && TM >= 1 && TN >= 1, "tile too small");
+  static_assert(A_V4 * NT * 4 == BM * kBK && W_V4 * NT * 4 == BN * kBK, "tile split");
+  constexpr int A_ELEMS = BM * kLdsStride, W_ELEMS = BN * kLdsStride;
+
+  // Two LDS buffers: slab s+1 is stored while slab s is multiplied.
+  __shared__ float lds[2 * (A_ELEMS + W_ELEMS)];
 
   // XCD-aware tile order: workgroup ids are dealt to the 8 XCDs round robin;
   // give XCD x the contiguous m-major tile range [x*chunk, (x+1)*chunk).
@@ -84,8 +102,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / GN, wn = wave - (wave / GN) * GN;
   const int l16 = lane & 15, lq = lane >> 4;
+
+  // Rows each thread stages; rows past the matrix are clamped to its last row
+  // (their products land in outputs that are never stored).
+  int arow[A_V4], wrow[W_V4], acol[A_V4], wcol[W_V4];
+#pragma unroll
+  for (int i = 0; i < A_V4; ++i) {
+    const int v = tid + NT * i;
+    arow[i] = min(m0 + (v >> 3), M - 1);
+    acol[i] = 4 * (v & 7);
+  }
+#pragma unroll
+  for (int i = 0; i < W_V4; ++i) {
+    const int v = tid + NT * i;
+    wrow[i] = min(n0 + (v >> 3), N - 1);
+    wcol[i] = 4 * (v & 7);
+  }
 
   floatx4 acc[TM][TN];
 #pragma unroll
@@ -94,67 +128,89 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int N, int K,
     for (int b = 0; b < TN; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   float4 ra[A_V4], rw[W_V4];
-  auto fetch = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < A_V4; ++i) {
-      const int v = tid + 256 * i;
-      const int row = v >> 3, c4 = v & 7;
-      ra[i] = load_k4<VA>(A, lda, m0 + row, M, kb + 4 * c4, K);
-    }
-#pragma unroll
-    for (int i = 0; i < W_V4; ++i) {
-      const int v = tid + 256 * i;
-      const int row = v >> 3, c4 = v & 7;
-      rw[i] = load_k4<VW>(W, K, n0 + row, N, kb + 4 * c4, K);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < A_V4; ++i) {
-      const int v = tid + 256 * i;
-      const int row = v >> 3, c4 = v & 7;
-      *reinterpret_cast<float4 *>(&As[row * kLdsStride + 4 * c4]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < W_V4; ++i) {
-      const int v = tid + 256 * i;
-      const int row = v >> 3, c4 = v & 7;
-      *reinterpret_cast<float4 *>(&Ws[row * kLdsStride + 4 * c4]) = rw[i];
-    }
-  };
-
+  const int nfull = K / kBK;                   // slabs inside K
   const int nslab = (K + kBK - 1) / kBK;
-  fetch(0);
-  stash();
-  __syncthreads();
-  for (int sl = 0; sl < nslab; ++sl) {
-    if (sl + 1 < nslab) fetch((sl + 1) * kBK);
+  auto fetch = [&](int sl) {
+    const int kb = sl * kBK;
+    if (sl < nfull) {
 #pragma unroll
-    for (int kq = 0; kq < kBK; kq += 16) {
-      float4 af[TM], wf[TN];
+      for (int i = 0; i < A_V4; ++i) ra[i] = load_full<VA>(A, lda, arow[i], kb + acol[i]);
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
-        af[a] = *reinterpret_cast<const float4 *>(
-            &As[(wm * WM + a * 16 + l16) * kLdsStride + kq + 4 * lq]);
+      for (int i = 0; i < W_V4; ++i) rw[i] = load_full<VW>(W, K, wrow[i], kb + wcol[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_V4; ++i) ra[i] = load_tail(A, lda, arow[i], kb + acol[i], K);
+#pragma unroll
+      for (int i = 0; i < W_V4; ++i) rw[i] = load_tail(W, K, wrow[i], kb + wcol[i], K);
+    }
+  };
+  auto stash = [&](int buf) {
+    float *As = lds + buf * (A_ELEMS + W_ELEMS);
+    float *Ws = As + A_ELEMS;
+#pragma unroll
+    for (int i = 0; i < A_V4; ++i) {
+      const int v = tid + NT * i;
+      *reinterpret_cast<float4 *>(&As[(v >> 3) * kLdsStride + acol[i]]) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < W_V4; ++i) {
+      const int v = tid + NT * i;
+      *reinterpret_cast<float4 *>(&Ws[(v >> 3) * kLdsStride + wcol[i]]) = rw[i];
+    }
+  };
+  // Fragments of one k-quad block (16 k) of the current slab.
+  auto frags = [&](const float *As, const float *Ws, int kq, float4 (&af)[TM],
+                   float4 (&wf)[TN]) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+      af[a] = *reinterpret_cast<const float4 *>(
+          &As[(wm * WM + a * 16 + l16) * kLdsStride + kq + 4 * lq]);
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+      wf[b] = *reinterpret_cast<const float4 *>(
+          &Ws[(wn * WN + b * 16 + l16) * kLdsStride + kq + 4 * lq]);
+  };
+  // 4 MFMA steps over the 4 k of each lane's float4, component-major so
+  // consecutive MFMAs never share an accumulator.
+  auto mfmas = [&](const float4 (&af)[TM], const float4 (&wf)[TN]) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
       for (int b = 0; b < TN; ++b)
-        wf[b] = *reinterpret_cast<const float4 *>(
-            &Ws[(wn * WN + b * 16 + l16) * kLdsStride + kq + 4 * lq]);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].x, af[a].x, acc[a][b], 0, 0, 0);
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].x, af[a].x, acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].y, af[a].y, acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].z, af[a].z, acc[a][b], 0, 0, 0);
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].w, af[a].w, acc[a][b], 0, 0, 0);
-        }
-    }
+      for (int b = 0; b < TN; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].y, af[a].y, acc[a][b], 0, 0, 0);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].z, af[a].z, acc[a][b], 0, 0, 0);
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].w, af[a].w, acc[a][b], 0, 0, 0);
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int sl = 0; sl < nslab; ++sl) {
+    const bool more = sl + 1 < nslab;
+    if (more) fetch(sl + 1);
+    const float *As = lds + (sl & 1) * (A_ELEMS + W_ELEMS);
+    const float *Ws = As + A_ELEMS;
+    // the second k-quad's fragments are read while the first one's MFMAs run
+    float4 af0[TM], wf0[TN], af1[TM], wf1[TN];
+    frags(As, Ws, 0, af0, wf0);
+    frags(As, Ws, 16, af1, wf1);
+    mfmas(af0, wf0);
+    mfmas(af1, wf1);
+    if (more) stash((sl + 1) & 1);
     __syncthreads();
-    if (sl + 1 < nslab) {
-      stash();
-      __syncthreads();
-    }
   }
 
   // Epilogue: lane holds C[m][n .. n+3] for m = .. + l16, n = .. + 4*lq.
@@ -218,17 +274,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K,
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int GM, int GN>
 hipError_t launch_gemm_cfg(int M, int N, int K, const float *A, int64_t lda, const float *W,
                            const float *bias, int act, float *C, int64_t ldc, bool va, bool vw,
                            bool vc, hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   const int xcd_chunk = (tiles % 8 == 0) ? (int)(tiles / 8) : 0;
-  dim3 grid((unsigned)tiles), block(256);
-#define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                     \
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, A_, W_, C_>), grid, block, 0, stream, M, N, K, A, \
-                     lda, W, bias, act, C, ldc, tiles_n, xcd_chunk)
+  dim3 grid((unsigned)tiles), block(64 * GM * GN);
+#define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                       \
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, GM, GN, A_, W_, C_>), grid, block, 0, stream, M, N, \
+                     K, A, lda, W, bias, act, C, ldc, tiles_n, xcd_chunk)
   if (va && vw && vc)
     DLRM_GEMM_LAUNCH(true, true, true);
   else if (va && !vw && vc)
@@ -263,13 +319,23 @@ hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const
                          act, C, ldc);
     return hipGetLastError();
   }
-  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  const int64_t t12864 = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
-  if (t128 >= 512)
-    return launch_gemm_cfg<128, 128>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc, stream);
-  if (t12864 >= 512)
-    return launch_gemm_cfg<128, 64>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc, stream);
-  return launch_gemm_cfg<64, 64>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc, stream);
+  // Tile shape: the largest tile that still gives every CU a workgroup.
+  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+#ifdef DLRM_GEMM_TILE
+  constexpr int forced = DLRM_GEMM_TILE;
+#else
+  constexpr int forced = 0;
+#endif
+  // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
+  // for every CU, else 64 x 64, else 64 x 32 on 4 waves.
+  if (forced == 1 || (forced == 0 && tiles(128, 128) >= 256))
+    return launch_gemm_cfg<128, 128, 2, 4>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                           stream);
+  if (forced == 3 || (forced == 0 && tiles(64, 64) >= 256))
+    return launch_gemm_cfg<64, 64, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                         stream);
+  return launch_gemm_cfg<64, 32, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                       stream);
 }
 
 }  // namespace dlrm

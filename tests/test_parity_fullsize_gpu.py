@@ -1,0 +1,125 @@
+"""GPU parity at the full sizes of the specified workloads, in the launch
+configuration bench.py times (one dlrm_emb_interact over the whole batch,
+uniform-stride bags, device tables; one dlrm_forward for the full forward).
+
+Where the oracle cannot run the whole batch in seconds, sampled samples are
+compared: the rows their bags touch are copied from the device tables into a
+compact host problem that the oracle solves sample by sample.  Properties
+that hold at any size (the dense columns are an exact copy, every output is
+finite) are checked on every row."""
+import numpy as np
+import pytest
+
+import oracle
+from conftest import gpu_available
+from gpu_helpers import assert_close, dev, host, sample_rows, sampled_subproblem
+from dlrm_embedding_bag_amd import abi, inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _release():
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _device_tables(w, seed=0):
+    if w.table_source == "device":
+        return [inputs.table_device(w, k, seed) for k in range(w.num_tables)]
+    return [dev(inputs.table_host(w, k, seed)) for k in range(w.num_tables)]
+
+
+def test_mid_workload_every_output():
+    """B=2048, K=8 tables x 100,000 rows x D=64, 20 uniform indices per bag."""
+    w = inputs.WORKLOADS["mid"]
+    tables = [inputs.table_host(w, k) for k in range(w.num_tables)]
+    idx = [inputs.indices(w, k) for k in range(w.num_tables)]
+    dense = inputs.dense(w)
+    E = oracle.emb_bag_sum(tables, idx, batch=w.batch)
+    want = oracle.interact(dense, E)
+    import torch
+    td = [dev(t) for t in tables]
+    xd = [dev(i) for i in idx]
+    emb_out = torch.empty((w.batch, w.num_tables, w.dim), device="cuda")
+    got = host(abi.dlrm_emb_interact(td, xd, dev(dense), emb_out=emb_out))
+    assert got.shape == (2048, 100)
+    assert_close(got, want, "mid fused")
+    assert np.array_equal(got[:, :w.dim], dense)
+    assert_close(host(emb_out), E, "mid pooled")
+    got_unfused = host(abi.dlrm_interact_lower_tri(dev(dense), dev(host(emb_out))))
+    assert np.array_equal(got_unfused, got), "unfused and fused paths agree bit for bit"
+    del td, xd, emb_out
+    _release()
+
+
+@pytest.mark.parametrize("name,nsamples", [("nc32", 96), ("nc32-uniform", 48), ("large", 24)])
+def test_full_size_sampled(name, nsamples):
+    """The benchmark's launch on the full batch; sampled rows against the oracle."""
+    w = inputs.WORKLOADS[name]
+    print(f"\n[{name}] {w.description}", flush=True)
+    import torch
+    tables = _device_tables(w)
+    idx = [inputs.indices(w, k) for k in range(w.num_tables)]
+    dense = inputs.dense(w)
+    xd = [dev(i) for i in idx]
+    out = torch.empty((w.batch, w.out_width), device="cuda")
+    abi.dlrm_emb_interact(tables, xd, dev(dense), out=out)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(got[:, :w.dim], dense), "dense columns are an exact copy"
+    samples = sample_rows(w.batch, nsamples, seed=len(name))
+    sub_tables, sub_idx = sampled_subproblem(tables, idx, w.bag, samples)
+    want = oracle.interact(dense[samples],
+                           oracle.emb_bag_sum(sub_tables, sub_idx, batch=len(samples)))
+    assert_close(got[samples], want, f"{name} sampled")
+    del tables, xd, out
+    _release()
+
+
+def test_full_forward_sampled():
+    """DLRMv1 forward at B=8192 (13-512-256-64, K=26 x 1M x 64, L=20 Zipf,
+    415-512-256-1) through one dlrm_forward call; sampled rows vs the oracle."""
+    w = inputs.WORKLOADS["dlrm"]
+    print(f"\n[dlrm] {w.description}", flush=True)
+    import torch
+    tables = _device_tables(w)
+    idx = [inputs.indices(w, k) for k in range(w.num_tables)]
+    dense = inputs.dense(w)
+    bottom, top = inputs.dlrm_layers(w, bias_std=0.1)
+    model = abi.DlrmModel([(dev(a), dev(b), act) for a, b, act in bottom],
+                          [(dev(a), dev(b), act) for a, b, act in top], tables)
+    got = host(abi.dlrm_forward(model, dev(dense), [dev(i) for i in idx]))
+    assert got.shape == (8192, 1) and np.all(np.isfinite(got))
+    assert np.all((got >= 0) & (got <= 1))
+    samples = sample_rows(w.batch, 48, seed=3)
+    sub_tables, sub_idx = sampled_subproblem(tables, idx, w.bag, samples)
+    want, _, _ = oracle.forward(dense[samples], bottom, top, sub_tables, sub_idx)
+    assert_close(got[samples], want, "dlrm forward sampled")
+    del tables, model
+    _release()
+
+
+def test_full_forward_matches_its_parts():
+    """dlrm_forward equals the composition of the separately called entry points
+    (linear_bias_act x3, dlrm_emb_interact, linear_bias_act x3) bit for bit."""
+    w = inputs.Workload("fwd-parts", batch=1000, num_tables=26, rows=20000, dim=64, bag=20,
+                        dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1))
+    import torch
+    tables = [dev(inputs.table_host(w, k)) for k in range(w.num_tables)]
+    idx = [dev(inputs.indices(w, k)) for k in range(w.num_tables)]
+    dense = dev(inputs.dense(w))
+    bottom, top = inputs.dlrm_layers(w, bias_std=0.1)
+    bl = [(dev(a), dev(b), act) for a, b, act in bottom]
+    tl = [(dev(a), dev(b), act) for a, b, act in top]
+    model = abi.DlrmModel(bl, tl, tables)
+    got = host(abi.dlrm_forward(model, dense, idx))
+    x = dense
+    for wt, b, act in bl:
+        x = abi.linear_bias_act(x, wt, b, act)
+    R = abi.dlrm_emb_interact(tables, idx, x)
+    y = R
+    for wt, b, act in tl:
+        y = abi.linear_bias_act(y, wt, b, act)
+    assert np.array_equal(got, host(y))
