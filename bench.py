@@ -22,9 +22,15 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                 current kernel source, else null
   cpu_baseline  the CPU oracle timed on the host on the same workload
 
-Options: --workload {nc32,nc32-uniform,mid,tiny,large,dlrm}, --sweep,
---warm, --no-cpu-baseline, --copy-calibration (a plain 1 GiB copy, the
-scale for rocprofv3 FETCH_SIZE / WRITE_SIZE).
+The JSON line also carries `forward`: the full DLRMv1 forward at B=8192
+(dlrm_forward), with each MLP layer timed alone against the f32 MFMA peak
+(or HBM for the layers below the ridge point).
+
+Options: --workload {nc32,nc32-uniform,mid,tiny,large}, --sweep (batch x
+num_tables grid instead of the default line), --warm, --no-cpu-baseline,
+--no-forward, --profile-run (timed cold steps only, for profilers),
+--copy-calibration (a plain 1 GiB copy, the scale for rocprofv3 FETCH_SIZE /
+WRITE_SIZE).
 """
 import argparse
 import ctypes
@@ -257,6 +263,145 @@ def bench_emb_interact(args, stream):
     return res
 
 
+def _event_time(fn, stream, steps, warmup, cold, flush):
+    """Median event time (ms) of fn() on `stream`, caches flushed before each
+    call when cold."""
+    import torch
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            if cold:
+                flush.max()
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for s in range(steps):
+            if cold:
+                flush.max()
+            evs[s][0].record(stream)
+            fn()
+            evs[s][1].record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
+def bench_forward(args, stream, flush):
+    """The full DLRMv1 forward (dlrm_forward, one C call, 7 launches) at
+    B=8192, with each MLP layer and the gather + interaction also timed alone
+    against its roofline."""
+    import torch
+    from dlrm_embedding_bag_amd import abi, inputs
+    w = inputs.WORKLOADS["dlrm"]
+    log(f"forward workload: {w.description}")
+    tables = [inputs.table_device(w, k, args.seed) for k in range(w.num_tables)]
+    idx = [torch.from_numpy(inputs.indices(w, k, args.seed)).cuda() for k in range(w.num_tables)]
+    dense_in = torch.from_numpy(inputs.dense(w, args.seed)).cuda()
+    bottom, top = inputs.dlrm_layers(w, args.seed)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    bl = [(dev(a), dev(b), act) for a, b, act in bottom]
+    tl = [(dev(a), dev(b), act) for a, b, act in top]
+    model = abi.DlrmModel(bl, tl, tables)
+    B = w.batch
+    ws = torch.empty(model.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, 1), device="cuda")
+    lib = abi.load()
+    fwd_args = (ctypes.byref(model.struct), B, dense_in.data_ptr(), abi._ptr_array(idx), None,
+                abi._i64_array([i.numel() for i in idx]), out.data_ptr(), ws.data_ptr(),
+                ws.numel(), stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    def fwd():
+        rc = lib.dlrm_forward(*fwd_args)
+        if rc != 0:
+            raise RuntimeError(f"dlrm_forward failed with status {rc}")
+    cold = not args.warm
+    t_fwd = _event_time(fwd, stream, args.steps, args.warmup, cold, flush)
+    log(f"forward: {t_fwd * 1000:.1f} us ({'cold' if cold else 'warm'})")
+    # each layer alone (warm: weights and activations are on-chip-sized)
+    layers = []
+    acts = {}
+    x = dense_in
+    specs = [("bottom", i, l) for i, l in enumerate(bl)] + [("top", i, l) for i, l in enumerate(tl)]
+    R = torch.empty((B, w.out_width), device="cuda")
+    for part, i, (wt, b, act) in specs:
+        if part == "top" and i == 0:
+            x = R
+        n, k = wt.shape
+        y = torch.empty((B, n), device="cuda")
+        largs = (B, n, k, x.data_ptr(), x.stride(0), wt.data_ptr(), b.data_ptr(),
+                 abi.ACTS[act], y.data_ptr(), n, stream.cuda_stream)
+        t = _event_time(lambda: lib.linear_bias_act(*largs), stream, args.steps, 3, False,
+                        flush)
+        flops = 2.0 * B * n * k
+        nbytes = 4.0 * (B * k + n * k + n + B * n)
+        tf = flops / (t * 1e-3) / 1e12
+        gbs = nbytes / (t * 1e-3) / 1e9
+        ai = flops / nbytes
+        mfma_bound = ai > F32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        layers.append({"layer": f"{part}{i}: {k}->{n} {act}", "k": k, "n": n, "us": t * 1e3,
+                       "tflops": tf,
+                       "gbps": gbs, "bound": "mfma" if mfma_bound else "hbm",
+                       "frac": (tf / F32_MFMA_PEAK_TFLOPS) if mfma_bound else gbs / HBM_PEAK_GBPS})
+        x = y
+    # the gather + interaction of this workload alone, cold
+    ecase = EmbInteractCase(inputs.Workload("dlrm-emb", B, w.num_tables, w.rows, w.dim, w.bag,
+                                            "zipf", table_source="device"),
+                            1, args.seed, stream, tables=tables)
+    torch.cuda.synchronize()
+    t_emb = _event_time(lambda: ecase.run(0), stream, args.steps, args.warmup, cold, flush)
+    emb_bytes = ecase.bytes_per_launch()
+    mlp_us = sum(l["us"] for l in layers)
+    mlp_flops = sum(2.0 * B * l["k"] * l["n"] for l in layers)
+    for l in layers:
+        log(f"  {l['layer']:28s} {l['us']:7.1f} us {l['tflops']:6.1f} TFLOP/s "
+            f"{l['gbps']:6.0f} GB/s ({l['bound']}, frac {l['frac']:.2f})")
+    log(f"  emb+interact {t_emb * 1000:.1f} us, {emb_bytes / (t_emb * 1e-3) / 1e9:.0f} GB/s")
+    return {"workload": f"dlrm: {w.description}", "batch": B, "cache": "cold" if cold else "warm",
+            "us_per_forward": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
+            "emb_interact_us": t_emb * 1e3,
+            "emb_interact_algorithmic_gbps": emb_bytes / (t_emb * 1e-3) / 1e9,
+            "mlp_layers": layers, "mlp_us_sum": mlp_us,
+            "mlp_tflops": mlp_flops / (mlp_us * 1e-6) / 1e12,
+            "mlp_frac_of_f32_mfma_peak": mlp_flops / (mlp_us * 1e-6) / 1e12 / F32_MFMA_PEAK_TFLOPS}
+
+
+def bench_sweep(args, stream, flush):
+    """batch x num_tables sweep of the fused gather + interaction (D=64,
+    1,000,000 rows per table, 20 Zipf(1.05) indices per bag), cold."""
+    import torch
+    from dlrm_embedding_bag_amd import abi, inputs
+    batches = [2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]
+    ntabs = [2, 4, 8, 16, 26, 32]
+    base = inputs.WORKLOADS["nc32"]
+    w = inputs.Workload("sweep", max(batches), max(ntabs), base.rows, base.dim, base.bag, "zipf",
+                        table_source="device")
+    tables = [inputs.table_device(w, k, args.seed) for k in range(w.num_tables)]
+    idx = [torch.from_numpy(inputs.indices(w, k, args.seed)).cuda() for k in range(w.num_tables)]
+    dense = torch.from_numpy(inputs.dense(w, args.seed)).cuda()
+    lib = abi.load()
+    cells = []
+    for K in ntabs:
+        for B in batches:
+            F = K + 1
+            P = F * (F - 1) // 2
+            out = torch.empty((B, w.dim + P), device="cuda")
+            xs = [i[: B * w.bag] for i in idx[:K]]
+            a = (K, B, w.dim, abi._ptr_array(tables[:K]),
+                 abi._i64_array([t.shape[0] for t in tables[:K]]), abi._ptr_array(xs), None,
+                 abi._i64_array([x.numel() for x in xs]), dense.data_ptr(), out.data_ptr(), None,
+                 stream.cuda_stream)
+            t = _event_time(lambda: lib.dlrm_emb_interact(*a), stream, args.sweep_steps, 3,
+                            not args.warm, flush)
+            nbytes = B * emb_interact_bytes_per_sample(K, w.dim, w.bag)
+            gbs = nbytes / (t * 1e-3) / 1e9
+            cells.append({"batch": B, "num_tables": K, "us": t * 1e3,
+                          "samples_per_s": B / (t * 1e-3), "algorithmic_gbps": gbs,
+                          "frac_hbm": gbs / HBM_PEAK_GBPS})
+            log(f"sweep K={K:2d} B={B:5d}: {t * 1000:8.1f} us {gbs:7.0f} GB/s")
+    return {"dim": w.dim, "rows": w.rows, "bag": w.bag, "index_dist": "zipf(1.05)",
+            "cache": "warm" if args.warm else "cold", "cells": cells}
+
+
 def copy_rate(stream, mib=1024, reps=10):
     """Read + write rate of a plain 1 GiB device copy (a practical HBM figure)."""
     import torch
@@ -298,6 +443,11 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-forward", action="store_true",
+                    help="skip the full-forward section (B=8192 DLRMv1)")
+    ap.add_argument("--sweep", action="store_true", help="batch x num_tables sweep instead")
+    ap.add_argument("--sweep-steps", type=int, default=10)
+    ap.add_argument("--sweep-out", default="")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the cold timed steps (for profiler runs)")
     args = ap.parse_args()
@@ -317,7 +467,20 @@ def main():
     if args.copy_calibration:
         copy_calibration(stream)
         return
+    if args.sweep:
+        import torch
+        flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+        res = bench_sweep(args, stream, flush)
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as f:
+                json.dump(res, f, indent=1)
+        print(json.dumps(res), flush=True)
+        return
     res = bench_emb_interact(args, stream)
+    if not args.profile_run and not args.no_forward:
+        import torch
+        flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+        res["forward"] = bench_forward(args, stream, flush)
     print(json.dumps(res), flush=True)
 
 
