@@ -16,8 +16,8 @@
 // Tiles: BM x BN per workgroup of GM x GN waves (128 x 128 on 2 x 4 waves,
 // 64 x 64 or 64 x 32 on 2 x 2), BK = 32 staged through two LDS buffers (row
 // stride 36 floats: the 16 rows a ds_read_b128 touches start on different
-// banks): the next k-slab is loaded into registers and stored to the other
-// buffer while the current one is multiplied, one barrier per slab.  Full
+// banks): k-slabs are loaded into registers two slabs ahead and stored to the
+// other LDS buffer while the current one is multiplied, one barrier per slab.  Full
 // slabs load without bounds tests (rows past the matrix are clamped and their
 // outputs masked at the store); only the last, partial slab tests k.  Tiles
 // are assigned to XCDs in contiguous m-major runs so the workgroups that share
@@ -36,7 +36,10 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 32;
+#ifndef DLRM_GEMM_BK
+#define DLRM_GEMM_BK 32
+#endif
+constexpr int kBK = DLRM_GEMM_BK;   // k per LDS slab
 constexpr int kLdsStride = kBK + 4;
 
 __device__ __forceinline__ float apply_act(float x, int act) {
@@ -111,14 +114,14 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
 #pragma unroll
   for (int i = 0; i < A_V4; ++i) {
     const int v = tid + NT * i;
-    arow[i] = min(m0 + (v >> 3), M - 1);
-    acol[i] = 4 * (v & 7);
+    arow[i] = min(m0 + v / (kBK / 4), M - 1);
+    acol[i] = 4 * (v % (kBK / 4));
   }
 #pragma unroll
   for (int i = 0; i < W_V4; ++i) {
     const int v = tid + NT * i;
-    wrow[i] = min(n0 + (v >> 3), N - 1);
-    wcol[i] = 4 * (v & 7);
+    wrow[i] = min(n0 + v / (kBK / 4), N - 1);
+    wcol[i] = 4 * (v % (kBK / 4));
   }
 
   floatx4 acc[TM][TN];
@@ -127,10 +130,9 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  float4 ra[A_V4], rw[W_V4];
   const int nfull = K / kBK;                   // slabs inside K
   const int nslab = (K + kBK - 1) / kBK;
-  auto fetch = [&](int sl) {
+  auto fetch = [&](int sl, float4 (&ra)[A_V4], float4 (&rw)[W_V4]) {
     const int kb = sl * kBK;
     if (sl < nfull) {
 #pragma unroll
@@ -144,18 +146,18 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
       for (int i = 0; i < W_V4; ++i) rw[i] = load_tail(W, K, wrow[i], kb + wcol[i], K);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, const float4 (&ra)[A_V4], const float4 (&rw)[W_V4]) {
     float *As = lds + buf * (A_ELEMS + W_ELEMS);
     float *Ws = As + A_ELEMS;
 #pragma unroll
     for (int i = 0; i < A_V4; ++i) {
       const int v = tid + NT * i;
-      *reinterpret_cast<float4 *>(&As[(v >> 3) * kLdsStride + acol[i]]) = ra[i];
+      *reinterpret_cast<float4 *>(&As[(v / (kBK / 4)) * kLdsStride + acol[i]]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < W_V4; ++i) {
       const int v = tid + NT * i;
-      *reinterpret_cast<float4 *>(&Ws[(v >> 3) * kLdsStride + wcol[i]]) = rw[i];
+      *reinterpret_cast<float4 *>(&Ws[(v / (kBK / 4)) * kLdsStride + wcol[i]]) = rw[i];
     }
   };
   // Fragments of one k-quad block (16 k) of the current slab.
@@ -194,22 +196,41 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
       for (int b = 0; b < TN; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[b].w, af[a].w, acc[a][b], 0, 0, 0);
   };
-
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int sl = 0; sl < nslab; ++sl) {
-    const bool more = sl + 1 < nslab;
-    if (more) fetch(sl + 1);
-    const float *As = lds + (sl & 1) * (A_ELEMS + W_ELEMS);
+  // All MFMAs of the slab in LDS buffer `buf`; the next k-quad's fragments are
+  // read while this one's MFMAs run.
+  auto compute = [&](int buf) {
+    const float *As = lds + buf * (A_ELEMS + W_ELEMS);
     const float *Ws = As + A_ELEMS;
-    // the second k-quad's fragments are read while the first one's MFMAs run
     float4 af0[TM], wf0[TN], af1[TM], wf1[TN];
     frags(As, Ws, 0, af0, wf0);
-    frags(As, Ws, 16, af1, wf1);
-    mfmas(af0, wf0);
-    mfmas(af1, wf1);
-    if (more) stash((sl + 1) & 1);
+#pragma unroll
+    for (int kq = 0; kq < kBK; kq += 32) {
+      frags(As, Ws, kq + 16, af1, wf1);
+      mfmas(af0, wf0);
+      if (kq + 32 < kBK) frags(As, Ws, kq + 32, af0, wf0);
+      mfmas(af1, wf1);
+    }
+  };
+
+  // Slab s is loaded into register set s & 1 two slabs ahead of its use and
+  // stored to LDS buffer s & 1 one slab ahead: each global load has two slabs
+  // of MFMA work to arrive.
+  float4 ra0[A_V4], rw0[W_V4], ra1[A_V4], rw1[W_V4];
+  fetch(0, ra0, rw0);
+  stash(0, ra0, rw0);
+  if (nslab > 1) fetch(1, ra1, rw1);
+  __syncthreads();
+  for (int sl = 0; sl < nslab; sl += 2) {
+    // even slab: buffer 0; register set 0 is free
+    if (sl + 2 < nslab) fetch(sl + 2, ra0, rw0);
+    compute(0);
+    if (sl + 1 < nslab) stash(1, ra1, rw1);
+    __syncthreads();
+    if (sl + 1 >= nslab) break;
+    // odd slab: buffer 1; register set 1 is free
+    if (sl + 3 < nslab) fetch(sl + 3, ra1, rw1);
+    compute(1);
+    if (sl + 2 < nslab) stash(0, ra0, rw0);
     __syncthreads();
   }
 
@@ -326,6 +347,18 @@ hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const
 #else
   constexpr int forced = 0;
 #endif
+  if (forced == 7)
+    return launch_gemm_cfg<128, 64, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                          stream);
+  if (forced == 8)
+    return launch_gemm_cfg<64, 128, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                          stream);
+  if (forced == 9)
+    return launch_gemm_cfg<128, 128, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                           stream);
+  if (forced == 10)
+    return launch_gemm_cfg<64, 64, 1, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
+                                         stream);
   // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
   // for every CU, else 64 x 64, else 64 x 32 on 4 waves.
   if (forced == 1 || (forced == 0 && tiles(128, 128) >= 256))
