@@ -343,6 +343,25 @@ def bench_forward(args, stream, flush):
                        "gbps": gbs, "bound": "mfma" if mfma_bound else "hbm",
                        "frac": (tf / F32_MFMA_PEAK_TFLOPS) if mfma_bound else gbs / HBM_PEAK_GBPS})
         x = y
+    # each MLP as one fused chain launch (what dlrm_forward runs)
+    chains = []
+    for part, spec, x_in, width_in in (("bottom", bl, dense_in, w.dense_in),
+                                       ("top", tl, R, w.out_width)):
+        arr = abi._layer_array(spec, part, [])
+        n_out = spec[-1][0].shape[0]
+        y = torch.empty((B, n_out), device="cuda")
+        cargs = (B, len(spec), arr, x_in.data_ptr(), x_in.stride(0), y.data_ptr(), n_out,
+                 stream.cuda_stream)
+        if lib.mlp_forward(*cargs) != 0:
+            continue
+        t = _event_time(lambda: lib.mlp_forward(*cargs), stream, args.steps, 3, False, flush)
+        flops = sum(2.0 * B * wt.shape[0] * wt.shape[1] for wt, _, _ in spec)
+        tf = flops / (t * 1e-3) / 1e12
+        chains.append({"mlp": f"{part}: " + "-".join(str(v) for v in
+                                                      [width_in] + [wt.shape[0] for wt, _, _ in spec]),
+                       "us": t * 1e3, "tflops": tf, "frac": tf / F32_MFMA_PEAK_TFLOPS})
+        log(f"  fused {chains[-1]['mlp']:24s} {t * 1000:7.1f} us {tf:6.1f} TFLOP/s "
+            f"(frac {tf / F32_MFMA_PEAK_TFLOPS:.2f})")
     # the gather + interaction of this workload alone, cold
     ecase = EmbInteractCase(inputs.Workload("dlrm-emb", B, w.num_tables, w.rows, w.dim, w.bag,
                                             "zipf", table_source="device"),
@@ -360,7 +379,7 @@ def bench_forward(args, stream, flush):
             "us_per_forward": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
             "emb_interact_us": t_emb * 1e3,
             "emb_interact_algorithmic_gbps": emb_bytes / (t_emb * 1e-3) / 1e9,
-            "mlp_layers": layers, "mlp_us_sum": mlp_us,
+            "mlp_chains": chains, "mlp_layers": layers, "mlp_us_sum": mlp_us,
             "mlp_tflops": mlp_flops / (mlp_us * 1e-6) / 1e12,
             "mlp_frac_of_f32_mfma_peak": mlp_flops / (mlp_us * 1e-6) / 1e12 / F32_MFMA_PEAK_TFLOPS}
 

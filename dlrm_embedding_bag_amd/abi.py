@@ -23,7 +23,7 @@ ACTS = {"none": 0, "relu": 1, "sigmoid": 2}
 MAX_TABLES = 64
 MAX_DIM = 1024
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
-           "dlrm_interact_lower_tri", "dlrm_emb_interact", "linear_bias_act",
+           "dlrm_interact_lower_tri", "dlrm_emb_interact", "linear_bias_act", "mlp_forward",
            "dlrm_forward_workspace_bytes", "dlrm_forward")
 
 _vp = ctypes.c_void_p
@@ -78,6 +78,8 @@ def load(path: str = LIB_PATH):
     lib.linear_bias_act.restype = ctypes.c_int
     lib.linear_bias_act.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _i64,
                                     _vp]
+    lib.mlp_forward.restype = ctypes.c_int
+    lib.mlp_forward.argtypes = [_i32, _i32, ctypes.POINTER(Layer), _vp, _i64, _vp, _i64, _vp]
     lib.dlrm_forward_workspace_bytes.restype = ctypes.c_size_t
     lib.dlrm_forward_workspace_bytes.argtypes = [ctypes.POINTER(Model), _i32]
     lib.dlrm_forward.restype = ctypes.c_int
@@ -246,6 +248,43 @@ def linear_bias_act(a, w, bias=None, act="none", out=None, stream=None):
     return out
 
 
+def _layer_array(spec, what, keep):
+    torch = _torch()
+    arr = (Layer * len(spec))()
+    for n, (wt, b, act) in enumerate(spec):
+        _dev(wt, torch.float32, f"{what}[{n}].weight")
+        if b is not None:
+            _dev(b, torch.float32, f"{what}[{n}].bias")
+        keep.extend([wt, b])
+        arr[n].in_features = wt.shape[1]
+        arr[n].out_features = wt.shape[0]
+        arr[n].weight = wt.data_ptr()
+        arr[n].bias = b.data_ptr() if b is not None else None
+        arr[n].act = ACTS[act] if isinstance(act, str) else int(act)
+    return arr
+
+
+def mlp_forward(a, layers, out=None, stream=None):
+    """A stack of (weight (out, in), bias or None, act) layers in one launch."""
+    torch = _torch()
+    lib = load()
+    if not isinstance(a, torch.Tensor) or a.device.type != "cuda" or a.dtype != torch.float32:
+        raise ValueError("a must be a float32 GPU tensor")
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise ValueError("a must be 2-D with unit column stride")
+    keep = []
+    arr = _layer_array(layers, "layers", keep)
+    M = a.shape[0]
+    N = layers[-1][0].shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape != (M, N):
+        raise ValueError("out must be (M, N) with unit column stride")
+    _check(lib.mlp_forward(M, len(layers), arr, a.data_ptr(), a.stride(0), out.data_ptr(),
+                           out.stride(0), _stream(stream)), "mlp_forward")
+    return out
+
+
 class DlrmModel:
     """Host description of a DLRMv1 model over caller-owned device tensors.
 
@@ -259,22 +298,8 @@ class DlrmModel:
         self.tables = [_dev(t, torch.float32, f"tables[{k}]") for k, t in enumerate(tables)]
         self.dim = self.tables[0].shape[1]
 
-        def layers(spec, what):
-            arr = (Layer * len(spec))()
-            for n, (wt, b, act) in enumerate(spec):
-                _dev(wt, torch.float32, f"{what}[{n}].weight")
-                if b is not None:
-                    _dev(b, torch.float32, f"{what}[{n}].bias")
-                self._keep.extend([wt, b])
-                arr[n].in_features = wt.shape[1]
-                arr[n].out_features = wt.shape[0]
-                arr[n].weight = wt.data_ptr()
-                arr[n].bias = b.data_ptr() if b is not None else None
-                arr[n].act = ACTS[act] if isinstance(act, str) else int(act)
-            return arr
-
-        self._bottom = layers(bottom, "bottom")
-        self._top = layers(top, "top")
+        self._bottom = _layer_array(bottom, "bottom", self._keep)
+        self._top = _layer_array(top, "top", self._keep)
         self._tables = _ptr_array(self.tables)
         self._rows = _i64_array([t.shape[0] for t in self.tables])
         self.out_features = top[-1][0].shape[0]

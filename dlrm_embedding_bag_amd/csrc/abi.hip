@@ -54,9 +54,32 @@ int pack_tables(int32_t K, int32_t B, int32_t D, const float *const *tables,
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DLRM_OK : DLRM_ERR_HIP; }
 
+// Packs a validated layer stack into chain parameters; false if the chain
+// kernel cannot run it.
+bool pack_chain(int32_t m, int32_t n, const dlrm_layer *layers, const float *a, int64_t lda,
+                float *c, int64_t ldc, ChainParams &cp) {
+  if (n < 1 || n > kMaxChainLayers) return false;
+  memset(&cp, 0, sizeof(cp));
+  cp.M = m;
+  cp.nlayers = n;
+  cp.A = a;
+  cp.lda = lda;
+  cp.C = c;
+  cp.ldc = ldc;
+  for (int l = 0; l < n; ++l) {
+    cp.layer[l].W = layers[l].weight;
+    cp.layer[l].bias = layers[l].bias;
+    cp.layer[l].K = layers[l].in_features;
+    cp.layer[l].N = layers[l].out_features;
+    cp.layer[l].act = layers[l].act;
+  }
+  return chain_supported(cp);
+}
+
 struct ForwardLayout {
   int64_t P = 0, ldR = 0, ld_buf = 0;
   size_t off_R = 0, off_buf0 = 0, off_buf1 = 0, total = 0;
+  bool bottom_chain = false, top_chain = false;  // MLPs run as one fused chain launch
 };
 
 // Checks the model's shapes and computes the workspace layout for batch B.
@@ -86,11 +109,25 @@ int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
     if (l + 1 < m->num_top) widest = widest > L.out_features ? widest : L.out_features;
   }
   if (m->top[0].in_features != m->dim + lay.P) return DLRM_ERR_SHAPE;
+  // An MLP runs as one fused chain launch when the chain kernel takes its
+  // widths and its first layer is at most kChainNarrowK wide.  The threshold is
+  // 0 (never): measured inside the full forward on MI355X, the 13-512-256-64
+  // chain made the forward 8-11 us slower than three tiled GEMM launches, and
+  // the 415-wide top MLP is faster as tiled GEMMs in any case.
+  ChainParams probe;
+  const float *fake = reinterpret_cast<const float *>(uintptr_t(256));
+  lay.bottom_chain = m->bottom[0].in_features <= kChainNarrowK &&
+                     pack_chain(B, m->num_bottom, m->bottom, fake, m->bottom[0].in_features,
+                                const_cast<float *>(fake), 4, probe);
+  lay.top_chain = m->top[0].in_features <= kChainNarrowK &&
+                  pack_chain(B, m->num_top, m->top, fake, 4, const_cast<float *>(fake), 4, probe);
   lay.ld_buf = round4(widest);
   lay.off_R = 0;
   lay.off_buf0 = round256((size_t)B * (size_t)lay.ldR * sizeof(float));
   lay.off_buf1 = lay.off_buf0 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
-  lay.total = lay.off_buf1 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
+  lay.total = (lay.bottom_chain && lay.top_chain)
+                  ? lay.off_buf0
+                  : lay.off_buf1 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
   return DLRM_OK;
 }
 
@@ -185,6 +222,25 @@ int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda
   return hip_status(launch_linear(m, n, k, a, lda, w, bias, act, c, ldc, (hipStream_t)stream));
 }
 
+int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers, const float *a,
+                int64_t lda, float *c, int64_t ldc, void *stream) {
+  if (m < 0 || num_layers < 1) return DLRM_ERR_SHAPE;
+  if (!layers) return DLRM_ERR_NULL;
+  for (int l = 0; l < num_layers; ++l) {
+    const dlrm_layer &L = layers[l];
+    if (L.in_features < 1 || L.out_features < 1 || !valid_act(L.act)) return DLRM_ERR_SHAPE;
+    if (l > 0 && L.in_features != layers[l - 1].out_features) return DLRM_ERR_SHAPE;
+    if (!L.weight) return DLRM_ERR_NULL;
+  }
+  if (lda < layers[0].in_features || ldc < layers[num_layers - 1].out_features)
+    return DLRM_ERR_SHAPE;
+  if (m == 0) return DLRM_OK;  // nothing to read or write
+  if (!a || !c) return DLRM_ERR_NULL;
+  ChainParams cp;
+  if (!pack_chain(m, num_layers, layers, a, lda, c, ldc, cp)) return DLRM_ERR_UNSUPPORTED;
+  return hip_status(launch_mlp_chain(cp, (hipStream_t)stream));
+}
+
 size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t batch) {
   ForwardLayout lay;
   if (plan_forward(model, batch, lay) != DLRM_OK) return 0;
@@ -217,6 +273,12 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
   // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
   const float *x = dense_in;
   int64_t ldx = model->bottom[0].in_features;
+  ChainParams cp;
+  if (lay.bottom_chain &&
+      pack_chain(B, model->num_bottom, model->bottom, dense_in, ldx, R, lay.ldR, cp)) {
+    rc = hip_status(launch_mlp_chain(cp, st));
+    if (rc) return rc;
+  } else {
   for (int l = 0; l < model->num_bottom; ++l) {
     const dlrm_layer &L = model->bottom[l];
     const bool last = l + 1 == model->num_bottom;
@@ -227,6 +289,7 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
     if (rc) return rc;
     x = y;
     ldx = ldy;
+  }
   }
 
   // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
@@ -248,6 +311,9 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
   // Top MLP on cat(dense, dots) = R.
   x = R;
   ldx = lay.ldR;
+  const int32_t out_w = model->top[model->num_top - 1].out_features;
+  if (lay.top_chain && pack_chain(B, model->num_top, model->top, R, lay.ldR, out, out_w, cp))
+    return hip_status(launch_mlp_chain(cp, st));
   for (int l = 0; l < model->num_top; ++l) {
     const dlrm_layer &L = model->top[l];
     const bool last = l + 1 == model->num_top;

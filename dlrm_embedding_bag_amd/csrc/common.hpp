@@ -103,6 +103,8 @@ __device__ __forceinline__ void pair_from_index(uint32_t p, int &i, int &j) {
   j = (int)(p - (uint32_t)i * (uint32_t)(i - 1) / 2u);
 }
 
-inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+__host__ __device__ inline bool aligned16(const void *p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
 
 }  // namespace dlrm

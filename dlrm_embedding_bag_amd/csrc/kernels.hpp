@@ -37,6 +37,38 @@ bool plan_interact(int B, int K, int D, bool vec4, InteractParams &ip, int &thre
 hipError_t launch_interact(const TableSet *ts, bool csr, const InteractParams &ip, int threads,
                            bool vec4, hipStream_t stream);
 
+constexpr int kMaxChainLayers = 4;
+constexpr int kMaxChainWidth = 512;  // widest layer the MLP chain keeps in LDS
+#ifndef DLRM_CHAIN_NARROW_K
+#define DLRM_CHAIN_NARROW_K 0
+#endif
+constexpr int kChainNarrowK = DLRM_CHAIN_NARROW_K;  // dlrm_forward chains an MLP whose first K <= this
+
+// One layer of an MLP chain: out = act(in W^T + bias), W (N, K) dense.
+struct ChainLayer {
+  const float *W;
+  const float *bias;  // (N,) or nullptr
+  int K, N, act;
+};
+
+// A stack of layers run by one launch over rows [0, M).
+struct ChainParams {
+  int M, nlayers;
+  const float *A;  // (M, layer[0].K), row stride lda
+  int64_t lda;
+  float *C;        // (M, layer[last].N), row stride ldc
+  int64_t ldc;
+  int c_vec;       // filled by the launcher
+  int ld_hidden;   // filled by the launcher
+  ChainLayer layer[kMaxChainLayers];
+};
+
+// True when the chain kernel can run these layers: every layer but a final
+// N <= 8 head has N a multiple of 64 with N/64 a power of two and N <= 512,
+// biases 16-byte aligned, widths chain.
+bool chain_supported(const ChainParams &p);
+hipError_t launch_mlp_chain(ChainParams p, hipStream_t stream);
+
 // C = act(A W^T + bias); A (M, K) stride lda, W (N, K) dense, C stride ldc.
 hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const float *W,
                          const float *bias, int act, float *C, int64_t ldc, hipStream_t stream);

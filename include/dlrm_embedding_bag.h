@@ -162,7 +162,7 @@ DLRM_API int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a,
                     int64_t lda, const float *w, const float *bias, int32_t act,
                     float *c, int64_t ldc, void *stream);
 
-/* One MLP layer of a dlrm_model. */
+/* One MLP layer (of a dlrm_model or an mlp_forward stack). */
 typedef struct dlrm_layer {
   int32_t in_features;
   int32_t out_features;
@@ -170,6 +170,27 @@ typedef struct dlrm_layer {
   const float *bias;   /* (out_features,) float32, device, or NULL    */
   int32_t act;         /* a dlrm_act                                  */
 } dlrm_layer;
+
+/*
+ * mlp_forward -- a stack of linear_bias_act layers in one launch, the hidden
+ * activations kept on chip ([FASTPATHS] matmul2d.rs, Activation epilogue;
+ * the DLRMv1 bottom and top MLPs):
+ *
+ *   h_0 = a;  h_{l+1} = act_l(h_l W_l^T + b_l);  c = h_{num_layers}
+ *
+ *   m           rows, >= 0 (0: nothing to do)
+ *   num_layers  1..4
+ *   layers      [host] num_layers layers; layer l+1's in_features equals
+ *               layer l's out_features
+ *   a           (m, layers[0].in_features) float32, row stride lda
+ *   c           (m, layers[last].out_features) float32, row stride ldc
+ * Supported widths: every layer but a last one of out_features <= 8 must
+ * have out_features in {64, 128, 256, 512}, and 16-byte aligned biases; at
+ * least one layer must precede an out_features <= 8 layer.  Anything else
+ * returns DLRM_ERR_UNSUPPORTED (linear_bias_act per layer always works).
+ */
+DLRM_API int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers,
+                         const float *a, int64_t lda, float *c, int64_t ldc, void *stream);
 
 /* A DLRMv1 model: bottom MLP, K embedding tables, top MLP.  All arrays of
  * this struct are [host]; the weights and tables they point to are device

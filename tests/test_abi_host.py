@@ -112,6 +112,27 @@ def test_linear_argument_errors(lib):
     assert f(0, 2, 3, FAKE, 3, FAKE, None, 0, FAKE, 2, None) == 0     # m == 0: no-op
 
 
+def test_mlp_forward_argument_errors(lib):
+    f = lib.mlp_forward
+    def layers(spec):
+        arr = (abi.Layer * len(spec))()
+        for n, (i, o, act) in enumerate(spec):
+            arr[n].in_features, arr[n].out_features, arr[n].weight, arr[n].act = i, o, FAKE, act
+        return arr
+    good = layers([(13, 512, 1), (512, 256, 1), (256, 64, 1)])
+    assert f(8, 0, good, FAKE, 13, FAKE, 64, None) == 2                 # no layers
+    assert f(8, 3, None, FAKE, 13, FAKE, 64, None) == 1                 # layers NULL
+    assert f(8, 3, layers([(13, 512, 1), (500, 64, 1), (64, 64, 1)]), FAKE, 13, FAKE, 64,
+             None) == 2                                                  # widths do not chain
+    assert f(8, 3, good, FAKE, 12, FAKE, 64, None) == 2                 # lda < in
+    assert f(8, 3, good, None, 13, FAKE, 64, None) == 1                 # a NULL
+    assert f(8, 2, layers([(13, 96, 1), (96, 64, 1)]), FAKE, 13, FAKE, 64,
+             None) == 3                                                  # width 96 unsupported
+    assert f(8, 1, layers([(13, 1, 2)]), FAKE, 13, FAKE, 1, None) == 3  # head needs a layer first
+    assert f(8, 5, layers([(64, 64, 1)] * 5), FAKE, 64, FAKE, 64, None) == 3   # > 4 layers
+    assert f(0, 3, good, None, 13, None, 64, None) == 0                 # m == 0: no-op
+
+
 def _model(bottom, top, K, D):
     bl = (abi.Layer * len(bottom))()
     for n, (i, o, act) in enumerate(bottom):
@@ -132,8 +153,12 @@ def test_forward_workspace_and_errors(lib):
                   [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D)
     B = 8192
     ws = lib.dlrm_forward_workspace_bytes(ctypes.byref(good), B)
-    # R (B x 416 floats) + two ping-pong buffers (B x 512 floats)
+    # the bottom MLP (first layer 13 wide) runs as one fused chain, the top one
+    # layer by layer: R (B x 416 floats) + two ping-pong buffers (B x 512)
     assert ws == B * 416 * 4 + 2 * B * 512 * 4
+    odd = _model([(13, 96, 1), (96, 64, 1)], [(D + P, 96, 1), (96, 1, 2)], K, D)
+    # widths the chain kernel does not take: R + two ping-pong buffers (B x 96)
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(odd), B) == B * 416 * 4 + 2 * B * 96 * 4
     bad_chain = _model([(13, 512, 1), (500, 64, 1)], [(D + P, 1, 2)], K, D)
     assert lib.dlrm_forward_workspace_bytes(ctypes.byref(bad_chain), B) == 0
     bad_dim = _model([(13, 32, 1)], [(D + P, 1, 2)], K, D)       # bottom out != D

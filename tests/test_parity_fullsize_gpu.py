@@ -101,9 +101,19 @@ def test_full_forward_sampled():
     _release()
 
 
+def _mlp(x, layers, chain):
+    if chain:
+        return abi.mlp_forward(x, layers)
+    for wt, b, act in layers:
+        x = abi.linear_bias_act(x, wt, b, act)
+    return x
+
+
 def test_full_forward_matches_its_parts():
-    """dlrm_forward equals the composition of the separately called entry points
-    (linear_bias_act x3, dlrm_emb_interact, linear_bias_act x3) bit for bit."""
+    """dlrm_forward equals its parts called one by one, bit for bit: both MLPs
+    layer by layer through linear_bias_act around dlrm_emb_interact.  The same
+    forward with the MLPs as mlp_forward chains agrees within the float
+    tolerance."""
     w = inputs.Workload("fwd-parts", batch=1000, num_tables=26, rows=20000, dim=64, bag=20,
                         dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1))
     import torch
@@ -115,11 +125,8 @@ def test_full_forward_matches_its_parts():
     tl = [(dev(a), dev(b), act) for a, b, act in top]
     model = abi.DlrmModel(bl, tl, tables)
     got = host(abi.dlrm_forward(model, dense, idx))
-    x = dense
-    for wt, b, act in bl:
-        x = abi.linear_bias_act(x, wt, b, act)
-    R = abi.dlrm_emb_interact(tables, idx, x)
-    y = R
-    for wt, b, act in tl:
-        y = abi.linear_bias_act(y, wt, b, act)
-    assert np.array_equal(got, host(y))
+    d = _mlp(dense, bl, chain=False)
+    R = abi.dlrm_emb_interact(tables, idx, d)
+    assert np.array_equal(got, host(_mlp(R, tl, chain=False)))
+    y = abi.dlrm_emb_interact(tables, idx, _mlp(dense, bl, chain=True))
+    assert_close(got, host(_mlp(y, tl, chain=True)), "forward vs chained MLPs")

@@ -241,6 +241,55 @@ def test_linear_strided_operands():
     assert np.all(host(cbuf)[:, N:] == -7.0), "columns beyond n must be untouched"
 
 
+# --------------------------------------------------------------------- mlp_forward --
+MLP_STACKS = [  # (M, widths, acts)
+    (300, (13, 512, 256, 64), ("relu", "relu", "relu")),
+    (300, (415, 512, 256, 1), ("relu", "relu", "sigmoid")),
+    (37, (64, 128), ("none",)),
+    (65, (100, 256, 4), ("relu", "sigmoid")),
+    (96, (32, 64, 128, 256, 512), ("relu", "none", "relu", "relu")),
+    (1, (13, 512, 256, 64), ("relu", "relu", "relu")),
+    (513, (7, 64, 8), ("relu", "none")),
+]
+
+
+@pytest.mark.parametrize("M,widths,acts", MLP_STACKS)
+def test_mlp_forward_parity(M, widths, acts):
+    rng = np.random.default_rng(M + len(widths))
+    a = rng.standard_normal((M, widths[0])).astype(np.float32)
+    layers = []
+    for i, act in enumerate(acts):
+        k, n = widths[i], widths[i + 1]
+        bound = np.sqrt(6.0 / (k + n))
+        layers.append((rng.uniform(-bound, bound, (n, k)).astype(np.float32),
+                       (rng.standard_normal(n) * 0.1).astype(np.float32), act))
+    want = a
+    for w, b, act in layers:
+        want = oracle.linear(want, w, b, act)
+    got = host(abi.mlp_forward(dev(a), [(dev(w), dev(b), act) for w, b, act in layers]))
+    assert_close(got, want, f"mlp {widths}")
+
+
+def test_mlp_forward_strided_and_no_bias():
+    import torch
+    rng = np.random.default_rng(8)
+    M = 77
+    abuf = dev(rng.standard_normal((M, 420)).astype(np.float32))
+    a = abuf[:, :415]
+    ws = [rng.standard_normal((512, 415)).astype(np.float32) * 0.05,
+          rng.standard_normal((256, 512)).astype(np.float32) * 0.05,
+          rng.standard_normal((64, 256)).astype(np.float32) * 0.05]
+    cbuf = torch.full((M, 72), -3.0, device="cuda")
+    c = cbuf[:, :64]
+    abi.mlp_forward(a, [(dev(ws[0]), None, "relu"), (dev(ws[1]), None, "relu"),
+                        (dev(ws[2]), None, "none")], out=c)
+    want = host(a)
+    for w, act in zip(ws, ("relu", "relu", "none")):
+        want = oracle.linear(want, w, None, act)
+    assert_close(host(c), want, "strided chain")
+    assert np.all(host(cbuf)[:, 64:] == -3.0)
+
+
 # -------------------------------------------------------------------- dlrm_forward --
 def _forward_case(w, seed, bias_std=0.1):
     import torch
