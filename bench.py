@@ -235,6 +235,19 @@ def bench_emb_interact(args, stream):
         extra["warm_samples_per_s"] = case.B / (wms * 1e-3)
         extra["warm_algorithmic_gbps"] = nbytes / (wms * 1e-3) / 1e9
         log(f"warm step: mean {wms * 1000:.1f} us")
+    # the same batch with the K tables carved out of one allocation (stacked
+    # layout): table k = base + row_offsets[k] * D, nothing else changes
+    if not args.profile_run:
+        import torch
+        stack = torch.empty((case.K * w.rows, case.D), device="cuda")
+        for k, t in enumerate(case.tables):
+            stack[k * w.rows:(k + 1) * w.rows] = t
+        scase = EmbInteractCase(w, args.batches, args.seed, stream,
+                                tables=[stack[k * w.rows:(k + 1) * w.rows] for k in range(case.K)])
+        st, _ = time_steps(scase, args.steps, args.warmup, cold, flush, stream)
+        extra["stacked_layout_ms_per_step"] = statistics.mean(st)
+        log(f"stacked layout: mean {statistics.mean(st) * 1000:.1f} us")
+        del scase, stack
     khash = kernel_source_hash()
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS,

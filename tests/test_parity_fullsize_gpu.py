@@ -78,6 +78,37 @@ def test_full_size_sampled(name, nsamples):
     _release()
 
 
+def test_stacked_single_allocation_large():
+    """All 26 tables of the B=16384, D=128 workload carved out of ONE 53 GB
+    allocation (the stacked layout: table k starts at row_offsets[k]); element
+    offsets from the base pass 2^31, so row addressing must be 64-bit.  Same
+    results as separate allocations, sampled rows against the oracle."""
+    import torch
+    w = inputs.WORKLOADS["large"]
+    K, rows, D = w.num_tables, w.rows, w.dim
+    row_offsets = [k * rows for k in range(K + 1)]
+    assert row_offsets[-1] * D > 2 ** 31
+    stack = torch.empty((row_offsets[-1], D), device="cuda")
+    for k in range(K):
+        stack[row_offsets[k]:row_offsets[k + 1]] = inputs.table_device(w, k)
+    tables = [stack[row_offsets[k]:row_offsets[k + 1]] for k in range(K)]
+    idx = [inputs.indices(w, k) for k in range(K)]
+    dense = inputs.dense(w)
+    out = torch.empty((w.batch, w.out_width), device="cuda")
+    abi.dlrm_emb_interact(tables, [dev(i) for i in idx], dev(dense), out=out)
+    got = host(out)
+    samples = sample_rows(w.batch, 24, seed=11)
+    sub_tables, sub_idx = sampled_subproblem(tables, idx, w.bag, samples)
+    want = oracle.interact(dense[samples],
+                           oracle.emb_bag_sum(sub_tables, sub_idx, batch=len(samples)))
+    assert_close(got[samples], want, "stacked large sampled")
+    # the last table sits past 2^31 floats from the base: check one of its rows
+    last = host(stack[row_offsets[K - 1] + idx[K - 1][0]])
+    assert np.array_equal(last, host(tables[K - 1][idx[K - 1][0]]))
+    del stack, tables, out
+    _release()
+
+
 def test_full_forward_sampled():
     """DLRMv1 forward at B=8192 (13-512-256-64, K=26 x 1M x 64, L=20 Zipf,
     415-512-256-1) through one dlrm_forward call; sampled rows vs the oracle."""
