@@ -55,6 +55,12 @@ def load(path: str = None):
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.POINTER(_f32p), _i64p, ctypes.POINTER(_i32p),
         ctypes.POINTER(_i32p), _i64p, _f32p]
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_emb_bag.argtypes = [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.POINTER(ctypes.c_void_p), _i64p, ctypes.POINTER(_i32p),
+        ctypes.POINTER(_i32p), ctypes.POINTER(_f32p), _i64p, ctypes.c_int32, _f32p]
     lib.oracle_interact.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     _f32p, _f32p, _f32p]
     lib.oracle_linear.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -155,6 +161,49 @@ def emb_bag_sum(tables, indices, offsets=None, batch=None, lib=None):
         _ptr_array(offsets, _i32p) if offsets is not None else None,
         _p(n_idx, _i64p), _p(out, _f32p))
     _check(rc, "emb_bag_sum")
+    return out
+
+
+POOLS = {"sum": 0, "mean": 1}
+
+
+def bf16_to_f32(bits, lib=None):
+    """float32 value of each uint16 bfloat16 bit pattern (elementwise)."""
+    lib = lib or load()
+    bits = np.asarray(bits, np.uint16)
+    return np.array([lib.oracle_bf16_to_f32(int(b)) for b in bits.ravel()],
+                    np.float32).reshape(bits.shape)
+
+
+def emb_bag(tables, indices, offsets=None, batch=None, weights=None, pool="sum",
+            lib=None):
+    """Pooled (B, K, D) float32 with mean pooling, per-sample weights and
+    bfloat16 tables (tables given as uint16 bit patterns are bfloat16)."""
+    lib = lib or load()
+    K = len(tables)
+    bf16 = tables[0].dtype == np.uint16
+    tables = [np.ascontiguousarray(t, np.uint16 if bf16 else np.float32) for t in tables]
+    indices = [_i32(i) for i in indices]
+    D = tables[0].shape[1]
+    if offsets is not None:
+        offsets = [_i32(o) for o in offsets]
+        B = offsets[0].shape[0]
+    else:
+        B = batch
+    rows = np.array([t.shape[0] for t in tables], np.int64)
+    n_idx = np.array([i.shape[0] for i in indices], np.int64)
+    idx_bufs = [i if i.size else np.zeros(1, np.int32) for i in indices]
+    tab_ptrs = (ctypes.c_void_p * K)(*[t.ctypes.data for t in tables])
+    w_ptrs = None
+    if weights is not None:
+        weights = [_f32(w) if np.asarray(w).size else np.zeros(1, np.float32) for w in weights]
+        w_ptrs = _ptr_array(weights, _f32p)
+    out = np.empty((B, K, D), np.float32)
+    rc = lib.oracle_emb_bag(
+        K, B, D, 1 if bf16 else 0, tab_ptrs, _p(rows, _i64p), _ptr_array(idx_bufs, _i32p),
+        _ptr_array(offsets, _i32p) if offsets is not None else None, w_ptrs,
+        _p(n_idx, _i64p), POOLS[pool], _p(out, _f32p))
+    _check(rc, "emb_bag")
     return out
 
 

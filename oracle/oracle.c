@@ -110,6 +110,66 @@ int oracle_emb_bag_sum(int32_t K, int32_t B, int32_t D,
   return 0;
 }
 
+float oracle_bf16_to_f32(uint16_t b) {
+  uint32_t bits = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+/* The sum of oracle_emb_bag_sum with the two torch.nn.EmbeddingBag options
+ * the pages' lowering rejects: mean pooling and per-sample weights, and with
+ * bfloat16 table storage.  Every term is formed and summed in double. */
+int oracle_emb_bag(int32_t K, int32_t B, int32_t D, int32_t table_dtype,
+                   const void *const *tables, const int64_t *rows,
+                   const int32_t *const *indices, const int32_t *const *offsets,
+                   const float *const *weights, const int64_t *n_idx, int32_t pool,
+                   float *out) {
+  if (K < 1 || B < 1 || D < 1 || !tables || !rows || !indices || !n_idx || !out)
+    return -1;
+  if (table_dtype != ORACLE_F32 && table_dtype != ORACLE_BF16) return -6;
+  if (pool != ORACLE_POOL_SUM && pool != ORACLE_POOL_MEAN) return -6;
+  if (weights && pool != ORACLE_POOL_SUM) return -6;
+  for (int32_t k = 0; k < K; ++k) {
+    if (!tables[k] || rows[k] < 1 || n_idx[k] < 0) return -1;
+    if (n_idx[k] > 0 && !indices[k]) return -1;
+    if (weights && n_idx[k] > 0 && !weights[k]) return -1;
+    if (offsets == NULL && n_idx[k] % B != 0) return -4;
+    if (offsets != NULL && !offsets[k]) return -1;
+  }
+  for (int32_t k = 0; k < K; ++k) {
+    const int32_t *idx = indices[k];
+    for (int32_t b = 0; b < B; ++b) {
+      int64_t start, end;
+      if (offsets == NULL) {
+        int64_t L = n_idx[k] / B;
+        start = (int64_t)b * L;
+        end = start + L;
+      } else {
+        start = offsets[k][b];
+        end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : n_idx[k];
+        if (start < 0 || end < start || end > n_idx[k]) return -3;
+      }
+      for (int32_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t l = start; l < end; ++l) {
+          int64_t r = idx[l];
+          if (r < 0 || r >= rows[k]) return -2;
+          int64_t e = r * (int64_t)D + d;
+          double v = table_dtype == ORACLE_BF16
+                         ? (double)oracle_bf16_to_f32(((const uint16_t *)tables[k])[e])
+                         : (double)((const float *)tables[k])[e];
+          double w = weights ? (double)weights[k][l] : 1.0;
+          acc += w * v;
+        }
+        if (pool == ORACLE_POOL_MEAN && end > start) acc /= (double)(end - start);
+        out[((int64_t)b * K + k) * D + d] = (float)acc;
+      }
+    }
+  }
+  return 0;
+}
+
 /* [FASTPATHS] translator dispatch, pairwise-dot peephole:
  *   T = cat([dense.unsqueeze(1)] + [e.unsqueeze(1) for e in ly], dim=1)
  *   Z = bmm(T, T^T);   dots = Z[:, li, lj] with (li, lj) = tril_indices(F, F, -1)

@@ -68,6 +68,29 @@ int oracle_emb_bag_sum(int32_t K, int32_t B, int32_t D,
                        const int32_t *const *offsets, const int64_t *n_idx,
                        float *out);
 
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_POOL_SUM = 0, ORACLE_POOL_MEAN = 1 };
+
+/* bfloat16 (the upper 16 bits of an IEEE float32) to float32: exact. */
+float oracle_bf16_to_f32(uint16_t b);
+
+/* Generalised EmbeddingBag pooling, the adjacent semantics of the pages'
+ * sum-only kernel ([FASTPATHS] translator dispatch, _embedding_bag lowering:
+ * mode must be sum, per_sample_weights are rejected; torch.nn.EmbeddingBag
+ * defines the rest):
+ *   sum:  out[b,k,:] = sum over l in bag of w_l * row(idx[l])
+ *   mean: out[b,k,:] = (sum over l in bag of row(idx[l])) / |bag|, 0 if empty
+ * with w_l = weights[k][l] when weights is not NULL (sum only, as in torch),
+ * else 1.  table_dtype ORACLE_BF16 means tables[k] holds uint16_t bfloat16
+ * values, converted exactly to f32 before use.  Bags as in
+ * oracle_emb_bag_sum.  Errors: as oracle_emb_bag_sum, and -6 for weights
+ * with mean pooling or an unknown dtype or pool. */
+int oracle_emb_bag(int32_t K, int32_t B, int32_t D, int32_t table_dtype,
+                   const void *const *tables, const int64_t *rows,
+                   const int32_t *const *indices, const int32_t *const *offsets,
+                   const float *const *weights, const int64_t *n_idx, int32_t pool,
+                   float *out);
+
 /* Strict-lower-triangle pairwise-dot interaction ([FASTPATHS]
  * dlrm_interact.rs, PairwiseDotLowerTriStackedKernel; translator dispatch,
  * the Z[:, li, lj] over bmm(cat, permute) pattern).  Per sample b:

@@ -9,6 +9,10 @@ What pins what:
   emb-bag      numpy/torch float64 library routines (count-matrix product,
                torch embedding_bag), L=1 row copy, k identical indices == k*row,
                linearity, arange offsets == uniform stride, hand-worked CSR case
+  emb-bag ext  torch's bfloat16->float32 conversion on all 65536 patterns, torch
+               float64 embedding_bag (mean; sum with per-sample weights; bf16
+               tables), unit weights == sum, mean of copies == row, hand-worked
+               mean / weighted case with an empty bag
   interaction  numpy float64 X X^T + tril_indices, torch bmm, symmetry of the
                Gram matrix, F=2 single dot, hand-worked F=3 case, dense copy
   linear       numpy float64 A W^T + b on non-square shapes, identity and zero
@@ -109,6 +113,73 @@ def pin_emb_bag(lib):
                              [np.array(g["indices"], np.int32)],
                              [np.array(g["offsets"], np.int32)], lib=lib)
     assert np.array_equal(got[:, 0, :], np.array(g["expected"], np.float32))
+
+
+# ------------------------------------- emb-bag: mean, weights, bf16 tables --
+def pin_emb_bag_ext(lib):
+    import torch
+    F = torch.nn.functional
+    rng = np.random.default_rng(21)
+    # bf16 -> f32 against torch's own conversion (every 16-bit pattern)
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.bf16_to_f32(bits, lib=lib)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(mine, ref, equal_nan=True)
+    B, D, L = 6, 5, 3
+    rows = [9, 13]
+    tables = [rng.standard_normal((r, D)).astype(np.float32) for r in rows]
+    idx = [rng.integers(0, r, B * L).astype(np.int32) for r in rows]
+    offs = torch.arange(0, B * L, L)
+    t64 = [torch.from_numpy(t.astype(np.float64)) for t in tables]
+    i64 = [torch.from_numpy(i.astype(np.int64)) for i in idx]
+    # f32 sum is exactly oracle_emb_bag_sum
+    assert np.array_equal(oracle.emb_bag(tables, idx, batch=B, lib=lib),
+                          oracle.emb_bag_sum(tables, idx, batch=B, lib=lib))
+    # mean against torch float64
+    got = oracle.emb_bag(tables, idx, batch=B, pool="mean", lib=lib)
+    for k in range(2):
+        want = F.embedding_bag(i64[k], t64[k], offs, mode="mean").numpy()
+        np.testing.assert_allclose(got[:, k], want, rtol=1e-6, atol=1e-7)
+    # per-sample weights against torch float64
+    wts = [rng.standard_normal(B * L).astype(np.float32) for _ in rows]
+    got = oracle.emb_bag(tables, idx, batch=B, weights=wts, lib=lib)
+    for k in range(2):
+        want = F.embedding_bag(i64[k], t64[k], offs, mode="sum",
+                               per_sample_weights=torch.from_numpy(wts[k].astype(np.float64))
+                               ).numpy()
+        np.testing.assert_allclose(got[:, k], want, rtol=1e-6, atol=1e-6)
+    # all-ones weights are the plain sum, bit for bit
+    ones = [np.ones(B * L, np.float32) for _ in rows]
+    assert np.array_equal(oracle.emb_bag(tables, idx, batch=B, weights=ones, lib=lib),
+                          oracle.emb_bag_sum(tables, idx, batch=B, lib=lib))
+    # the mean of k copies of one row is that row exactly
+    for kk in (1, 3, 7):
+        got = oracle.emb_bag([tables[0]], [np.full(kk, 2, np.int32)], batch=1, pool="mean",
+                             lib=lib)
+        assert np.array_equal(got[0, 0], tables[0][2]), kk
+    # bf16 tables: pooled like their exact f32 values (torch conversion)
+    tb = [(rng.integers(0, 1 << 16, (r, D)) & 0x7f7f).astype(np.uint16) for r in rows]
+    tb32 = [torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).double() for t in tb]
+    for pool in ("sum", "mean"):
+        got = oracle.emb_bag(tb, idx, batch=B, pool=pool, lib=lib)
+        for k in range(2):
+            want = F.embedding_bag(i64[k], tb32[k], offs, mode=pool).numpy()
+            np.testing.assert_allclose(got[:, k], want, rtol=1e-6, atol=1e-30)
+    # weights with mean pooling are rejected (torch rejects them too)
+    try:
+        oracle.emb_bag(tables, idx, batch=B, weights=wts, pool="mean", lib=lib)
+        raise AssertionError("weights with mean pooling must be rejected")
+    except oracle.OracleError:
+        pass
+    # hand-worked CSR case with an empty bag
+    g = _golden("emb_bag_mean_weights.json")
+    t = [np.array(g["table"], np.float32)]
+    i = [np.array(g["indices"], np.int32)]
+    o = [np.array(g["offsets"], np.int32)]
+    got = oracle.emb_bag(t, i, o, pool="mean", lib=lib)
+    assert np.array_equal(got[:, 0], np.array(g["expected_mean"], np.float32))
+    got = oracle.emb_bag(t, i, o, weights=[np.array(g["weights"], np.float32)], lib=lib)
+    assert np.array_equal(got[:, 0], np.array(g["expected_weighted_sum"], np.float32))
 
 
 # ------------------------------------------------------------- interaction --
@@ -247,4 +318,5 @@ def pin_forward(lib):
     assert np.array_equal(E, oracle.emb_bag_sum(tables, idx, batch=w.batch, lib=lib))
 
 
-ALL_PINS = (pin_pair_map, pin_emb_bag, pin_interact, pin_linear, pin_forward)
+ALL_PINS = (pin_pair_map, pin_emb_bag, pin_emb_bag_ext, pin_interact, pin_linear,
+            pin_forward)

@@ -14,17 +14,38 @@ ORACLE_DIR = os.path.dirname(oracle_build.SRC)
 
 MUTANTS = {
     "emb_drops_last_index": (
-        "for (int64_t l = start; l < end; ++l)",
-        "for (int64_t l = start; l + 1 < end; ++l)"),
+        "for (int64_t l = start; l < end; ++l) {\n"
+        "          int64_t r = idx[l];\n"
+        "          if (r < 0 || r >= rows[k]) return -2;\n"
+        "          acc += (double)W",
+        "for (int64_t l = start; l + 1 < end; ++l) {\n"
+        "          int64_t r = idx[l];\n"
+        "          if (r < 0 || r >= rows[k]) return -2;\n"
+        "          acc += (double)W"),
+    "emb_ext_drops_first_index": (
+        "for (int64_t l = start; l < end; ++l) {\n"
+        "          int64_t r = idx[l];\n"
+        "          if (r < 0 || r >= rows[k]) return -2;\n"
+        "          int64_t e",
+        "for (int64_t l = start + 1; l < end; ++l) {\n"
+        "          int64_t r = idx[l];\n"
+        "          if (r < 0 || r >= rows[k]) return -2;\n"
+        "          int64_t e"),
     "emb_wrong_column": (
         "acc += (double)W[r * (int64_t)D + d];",
         "acc += (double)W[r * (int64_t)D];"),
     "emb_transposed_output": (
         "out[((int64_t)b * K + k) * D + d] = (float)acc;",
-        "out[((int64_t)k * B + b) * D + d] = (float)acc;"),
+        "out[((int64_t)k * B + b) * D + d] = (float)acc;", 0),
+    "emb_ext_transposed_output": (
+        "out[((int64_t)b * K + k) * D + d] = (float)acc;",
+        "out[((int64_t)k * B + b) * D + d] = (float)acc;", 1),
     "emb_last_bag_empty": (
         "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : n_idx[k];",
-        "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : start;"),
+        "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : start;", 0),
+    "emb_ext_last_bag_empty": (
+        "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : n_idx[k];",
+        "end = (b + 1 < B) ? (int64_t)offsets[k][b + 1] : start;", 1),
     "pair_order_column_major": (
         "for (int64_t i = 1; i < F; ++i)\n"
         "      for (int64_t j = 0; j < i; ++j) row[D + p++] = (float)Z[i * F + j];",
@@ -54,6 +75,15 @@ MUTANTS = {
     "pair_column_formula": (
         "*j_out = p - i * (i - 1) / 2;",
         "*j_out = p - i * (i + 1) / 2;"),
+    "mean_wrong_count": (
+        "if (pool == ORACLE_POOL_MEAN && end > start) acc /= (double)(end - start);",
+        "if (pool == ORACLE_POOL_MEAN && end > start) acc /= (double)(end - start + 1);"),
+    "weights_first_only": (
+        "double w = weights ? (double)weights[k][l] : 1.0;",
+        "double w = weights ? (double)weights[k][start] : 1.0;"),
+    "bf16_wrong_shift": (
+        "uint32_t bits = (uint32_t)b << 16;",
+        "uint32_t bits = (uint32_t)b << 15;"),
     "pair_float_sqrt_no_fixups": (
         "  int64_t i = (int64_t)floor((1.0 + sqrt(1.0 + 8.0 * (double)p)) / 2.0);\n"
         "  while (i * (i - 1) / 2 > p) --i;\n"
@@ -64,12 +94,18 @@ MUTANTS = {
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
-    old, new = MUTANTS[name]
+    old, new, *which = MUTANTS[name]
     src = open(oracle_build.SRC).read()
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    if which:      # the site occurs once per emb-bag function: patch one of them
+        sites = src.split(old)
+        assert len(sites) == 3, f"mutation site for {name} not found exactly twice"
+        patched = old.join(sites[:which[0] + 1]) + new + old.join(sites[which[0] + 1:])
+    else:
+        assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+        patched = src.replace(old, new)
     shutil.copy(os.path.join(ORACLE_DIR, "oracle.h"), tmp_path / "oracle.h")
     mutant_c = tmp_path / "oracle.c"
-    mutant_c.write_text(src.replace(old, new))
+    mutant_c.write_text(patched)
     so = str(tmp_path / "liboracle_mutant.so")
     oracle_build.build(str(mutant_c), so, extra_flags=["-Wno-error"])
     lib = oracle.load(so)
