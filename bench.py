@@ -22,11 +22,15 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                 current kernel source, else null
   cpu_baseline  the CPU oracle timed on the host on the same workload
 
-The JSON line also carries `forward`: the full DLRMv1 forward at B=8192
+The JSON line also carries `variants`: the same fused launch with bfloat16
+tables, mean pooling, per-sample weights and CSR bags of size 0..40
+(dlrm_emb_interact_pool), and `forward`: the full DLRMv1 forward at B=8192
 (dlrm_forward), with each MLP layer timed alone against the f32 MFMA peak
 (or HBM for the layers below the ridge point).
 
-Options: --workload {nc32,nc32-uniform,mid,tiny,large}, --sweep (batch x
+Options: --workload {nc32,nc32-uniform,mid,tiny,large} (or one variant,
+nc32-bf16 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-variants,
+--sweep (batch x
 num_tables grid instead of the default line), --warm, --no-cpu-baseline,
 --no-forward, --profile-run (timed cold steps only, for profilers),
 --copy-calibration (a plain 1 GiB copy, the scale for rocprofv3 FETCH_SIZE /
@@ -74,7 +78,58 @@ def emb_interact_bytes_per_sample(K, D, L):
     return K * L * D * 4 + K * L * 4 + D * 4 + (D + P) * 4
 
 
+def pool_bytes_per_sample(w, K, n_idx_per_sample):
+    """Algorithmic bytes of the fused gather + interaction of a general bag
+    form for one sample: gathered rows (row bytes by storage type) + indices
+    + per-sample weights + CSR offsets + dense + output."""
+    F = K + 1
+    P = F * (F - 1) // 2
+    row = w.dim * (2 if w.table_dtype == "bf16" else 4)
+    return (n_idx_per_sample * (row + 4 + (4 if w.weighted else 0))
+            + (K * 4 if w.lengths != "fixed" else 0) + w.dim * 4 + (w.dim + P) * 4)
+
+
 # ------------------------------------------------------------- workloads --
+class PoolCase:
+    """Device inputs for dlrm_emb_interact_pool (bf16 tables, mean pooling,
+    per-sample weights, CSR bags) plus prepared C-ABI arguments."""
+
+    def __init__(self, w, nbatches, seed, stream):
+        import torch
+        from dlrm_embedding_bag_amd import abi, inputs
+        self.w = w
+        self.B, self.K, self.D = w.batch, w.num_tables, w.dim
+        self.tables = [inputs.table_device_typed(w, k, seed) for k in range(self.K)]
+        self.lib = abi.load()
+        self.stream = stream
+        self.batches = []
+        self.n_idx = 0
+        for nb in range(nbatches):
+            sd = seed + 7919 * nb
+            idx = [inputs.indices(w, k, sd) for k in range(self.K)]
+            offs = ([torch.from_numpy(inputs.csr_offsets(w, k, sd)).cuda() for k in range(self.K)]
+                    if w.lengths != "fixed" else None)
+            wts = ([torch.from_numpy(inputs.sample_weights(w, k, idx[k].shape[0], sd)).cuda()
+                    for k in range(self.K)] if w.weighted else None)
+            idx_d = [torch.from_numpy(i).cuda() for i in idx]
+            dense = torch.from_numpy(inputs.dense(w, sd)).cuda()
+            out = torch.empty((self.B, w.out_width), dtype=torch.float32, device="cuda")
+            g = abi._BagsArg(self.tables, idx_d, offs, wts, w.pool, self.B)
+            args = (ctypes.byref(g.struct), dense.data_ptr(), out.data_ptr(), None,
+                    stream.cuda_stream)
+            self.batches.append((g, dense, out, args))
+            self.n_idx += sum(i.shape[0] for i in idx)
+        self.n_idx /= nbatches
+
+    def run(self, nb):
+        rc = self.lib.dlrm_emb_interact_pool(*self.batches[nb % len(self.batches)][3])
+        if rc != 0:
+            raise RuntimeError(f"dlrm_emb_interact_pool failed with status {rc}")
+
+    def bytes_per_launch(self):
+        return self.B * pool_bytes_per_sample(self.w, self.K, self.n_idx / self.B)
+
+
 class EmbInteractCase:
     """Device inputs for dlrm_emb_interact plus prepared C-ABI arguments."""
 
@@ -276,6 +331,25 @@ def bench_emb_interact(args, stream):
     return res
 
 
+def bench_variant_line(args, stream):
+    """One variant workload alone (--workload nc32-bf16 etc.): its cold
+    timed steps only, for profiler runs of the variant kernels."""
+    import torch
+    from dlrm_embedding_bag_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    log(f"workload {w.name}: {w.description}")
+    case = PoolCase(w, args.batches, args.seed, stream)
+    flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+    times, _ = time_steps(case, args.steps, args.warmup, not args.warm, flush, stream)
+    ms = statistics.mean(times)
+    nbytes = case.bytes_per_launch()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"{w.name}: mean {ms * 1000:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": f"{w.name}: {w.description}", "ms_per_step": ms,
+            "samples_per_s": case.B / (ms * 1e-3), "algorithmic_gbps": gbs,
+            "frac_hbm": gbs / HBM_PEAK_GBPS, "steps": args.steps}
+
+
 def _event_time(fn, stream, steps, warmup, cold, flush):
     """Median event time (ms) of fn() on `stream`, caches flushed before each
     call when cold."""
@@ -397,6 +471,37 @@ def bench_forward(args, stream, flush):
             "mlp_frac_of_f32_mfma_peak": mlp_flops / (mlp_us * 1e-6) / 1e12 / F32_MFMA_PEAK_TFLOPS}
 
 
+VARIANTS = ("nc32-bf16", "nc32-mean", "nc32-weighted", "nc32-csr")
+
+
+def bench_variants(args, stream, flush):
+    """The fused gather + interaction of the general bag forms on the nc32
+    shape (B=2048, K=32 x 1,000,000 x D=64, Zipf(1.05)): bfloat16 tables,
+    mean pooling, per-sample weights, CSR bags of size 0..40; cold, through
+    dlrm_emb_interact_pool."""
+    import torch
+    from dlrm_embedding_bag_amd import inputs
+    rows = []
+    for name in VARIANTS:
+        w = inputs.WORKLOADS[name]
+        case = PoolCase(w, args.batches, args.seed, stream)
+        torch.cuda.synchronize()
+        times, _ = time_steps(case, args.steps, args.warmup, not args.warm, flush, stream)
+        ms = statistics.mean(times)
+        nbytes = case.bytes_per_launch()
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows.append({"workload": f"{name}: {w.description}", "us": ms * 1e3,
+                     "samples_per_s": case.B / (ms * 1e-3),
+                     "algorithmic_bytes_per_launch": nbytes, "algorithmic_gbps": gbs,
+                     "frac_hbm": gbs / HBM_PEAK_GBPS})
+        log(f"variant {name:14s} {ms * 1000:7.1f} us {case.B / (ms * 1e-3) / 1e6:6.1f} M "
+            f"samples/s {gbs:6.0f} GB/s")
+        del case
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return rows
+
+
 def bench_sweep(args, stream, flush):
     """batch x num_tables sweep of the fused gather + interaction (D=64,
     1,000,000 rows per table, 20 Zipf(1.05) indices per bag), cold."""
@@ -477,6 +582,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the full-forward section (B=8192 DLRMv1)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the bf16 / mean / weighted / CSR variant lines")
     ap.add_argument("--sweep", action="store_true", help="batch x num_tables sweep instead")
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--sweep-out", default="")
@@ -508,11 +615,18 @@ def main():
                 json.dump(res, f, indent=1)
         print(json.dumps(res), flush=True)
         return
+    if args.workload in VARIANTS:
+        res = bench_variant_line(args, stream)
+        print(json.dumps(res), flush=True)
+        return
     res = bench_emb_interact(args, stream)
-    if not args.profile_run and not args.no_forward:
+    if not args.profile_run:
         import torch
         flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
-        res["forward"] = bench_forward(args, stream, flush)
+        if not args.no_variants:
+            res["variants"] = bench_variants(args, stream, flush)
+        if not args.no_forward:
+            res["forward"] = bench_forward(args, stream, flush)
     print(json.dumps(res), flush=True)
 
 

@@ -1,8 +1,8 @@
 """ctypes binding of libdlrm_mi355x.so -- argument marshalling only.
 
 Every function here has the name of the C entry point it calls and does no
-arithmetic of its own: it checks that tensors are float32/int32 device
-tensors, passes their device pointers and the current HIP stream, and turns a
+arithmetic of its own: it checks that tensors are device tensors of the
+documented types (float32 or bfloat16 tables, int32 indices), passes their device pointers and the current HIP stream, and turns a
 non-zero dlrm_status into a DlrmError.  There is no CPU fallback: without the
 built library, or with tensors off the GPU, calls raise.
 
@@ -22,8 +22,11 @@ STATUS_NAMES = {0: "DLRM_OK", 1: "DLRM_ERR_NULL", 2: "DLRM_ERR_SHAPE",
 ACTS = {"none": 0, "relu": 1, "sigmoid": 2}
 MAX_TABLES = 64
 MAX_DIM = 1024
+DTYPES = {"f32": 0, "bf16": 1}
+POOLS = {"sum": 0, "mean": 1}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
-           "dlrm_interact_lower_tri", "dlrm_emb_interact", "linear_bias_act", "mlp_forward",
+           "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
+           "dlrm_emb_interact_pool", "linear_bias_act", "mlp_forward",
            "dlrm_forward_workspace_bytes", "dlrm_forward")
 
 _vp = ctypes.c_void_p
@@ -41,6 +44,14 @@ class DlrmError(RuntimeError):
 class Layer(ctypes.Structure):
     _fields_ = [("in_features", _i32), ("out_features", _i32),
                 ("weight", _vp), ("bias", _vp), ("act", _i32)]
+
+
+class Bags(ctypes.Structure):
+    _fields_ = [("num_tables", _i32), ("batch", _i32), ("dim", _i32),
+                ("table_dtype", _i32), ("pool", _i32),
+                ("tables", ctypes.POINTER(_vp)), ("rows", ctypes.POINTER(_i64)),
+                ("indices", ctypes.POINTER(_vp)), ("offsets", ctypes.POINTER(_vp)),
+                ("n_idx", ctypes.POINTER(_i64)), ("weights", ctypes.POINTER(_vp))]
 
 
 class Model(ctypes.Structure):
@@ -75,6 +86,10 @@ def load(path: str = LIB_PATH):
     lib.dlrm_emb_interact.restype = ctypes.c_int
     lib.dlrm_emb_interact.argtypes = [_i32, _i32, _i32, ptrs, ctypes.POINTER(_i64), ptrs,
                                       ptrs, ctypes.POINTER(_i64), _vp, _vp, _vp, _vp]
+    lib.emb_bag_pool.restype = ctypes.c_int
+    lib.emb_bag_pool.argtypes = [ctypes.POINTER(Bags), _vp, _vp]
+    lib.dlrm_emb_interact_pool.restype = ctypes.c_int
+    lib.dlrm_emb_interact_pool.argtypes = [ctypes.POINTER(Bags), _vp, _vp, _vp, _vp]
     lib.linear_bias_act.restype = ctypes.c_int
     lib.linear_bias_act.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _i64,
                                     _vp]
@@ -215,6 +230,90 @@ def dlrm_emb_interact(tables, indices, dense, offsets=None, out=None, emb_out=No
         eo = emb_out.data_ptr()
     _check(lib.dlrm_emb_interact(K, B, D, tp, rows, ip, op, nidx, dense.data_ptr(),
                                  out.data_ptr(), eo, _stream(stream)), "dlrm_emb_interact")
+    return out
+
+
+class _BagsArg:
+    """A dlrm_bags struct and the host arrays it points to (kept alive)."""
+
+    def __init__(self, tables, indices, offsets, weights, pool, batch):
+        torch = _torch()
+        if len(tables) == 0:
+            raise ValueError("at least one table is required")
+        dt = tables[0].dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise TypeError("tables must be float32 or bfloat16")
+        self.tables = [_dev(t, dt, f"tables[{k}]") for k, t in enumerate(tables)]
+        self.indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
+        if len(self.tables) != len(self.indices):
+            raise ValueError("tables and indices must have the same length")
+        self.offsets = None
+        if offsets is not None:
+            self.offsets = [_dev(o, torch.int32, f"offsets[{k}]") for k, o in enumerate(offsets)]
+            if len(self.offsets) != len(self.tables):
+                raise ValueError("offsets must have one entry per table")
+            batch = self.offsets[0].shape[0]
+        if batch is None:
+            raise ValueError("batch is required with uniform-stride (offsets=None) bags")
+        self.weights = None
+        if weights is not None:
+            self.weights = [_dev(w, torch.float32, f"weights[{k}]") for k, w in enumerate(weights)]
+            if len(self.weights) != len(self.tables):
+                raise ValueError("weights must have one entry per table")
+        self.K = len(self.tables)
+        self.B = int(batch)
+        self.D = self.tables[0].shape[1]
+        self._arrays = (_ptr_array(self.tables), _i64_array([t.shape[0] for t in self.tables]),
+                        _ptr_array(self.indices),
+                        _ptr_array(self.offsets) if self.offsets is not None else None,
+                        _i64_array([i.numel() for i in self.indices]),
+                        _ptr_array(self.weights) if self.weights is not None else None)
+        tp, rows, ip, op, nidx, wp = self._arrays
+        self.struct = Bags(self.K, self.B, self.D, 1 if dt == torch.bfloat16 else 0,
+                           POOLS[pool], tp, rows, ip, op, nidx, wp)
+
+
+def emb_bag_pool(tables, indices, offsets=None, weights=None, pool="sum", batch=None, out=None,
+                 stream=None):
+    """(B, K, D) float32 pooled bags of float32 or bfloat16 tables, sum or mean
+    pooling, optional per-sample weights; see include/dlrm_embedding_bag.h."""
+    torch = _torch()
+    lib = load()
+    g = _BagsArg(tables, indices, offsets, weights, pool, batch)
+    if out is None:
+        out = torch.empty((g.B, g.K, g.D), dtype=torch.float32, device=g.tables[0].device)
+    _dev(out, torch.float32, "out")
+    if out.shape != (g.B, g.K, g.D):
+        raise ValueError("out must be (B, K, D)")
+    _check(lib.emb_bag_pool(ctypes.byref(g.struct), out.data_ptr(), _stream(stream)),
+           "emb_bag_pool")
+    return out
+
+
+def dlrm_emb_interact_pool(tables, indices, dense, offsets=None, weights=None, pool="sum",
+                           out=None, emb_out=None, stream=None):
+    """Fused gather + interaction over any dlrm_bags form: (B, D + F(F-1)/2)."""
+    torch = _torch()
+    lib = load()
+    _dev(dense, torch.float32, "dense")
+    g = _BagsArg(tables, indices, offsets, weights, pool, dense.shape[0])
+    B, D = dense.shape
+    if D != g.D:
+        raise ValueError("dense must be (B, D)")
+    P = (g.K + 1) * g.K // 2
+    if out is None:
+        out = torch.empty((B, D + P), dtype=torch.float32, device=dense.device)
+    _dev(out, torch.float32, "out")
+    if out.shape != (B, D + P):
+        raise ValueError("out must be (B, D + F(F-1)/2)")
+    eo = None
+    if emb_out is not None:
+        _dev(emb_out, torch.float32, "emb_out")
+        if emb_out.shape != (B, g.K, D):
+            raise ValueError("emb_out must be (B, K, D)")
+        eo = emb_out.data_ptr()
+    _check(lib.dlrm_emb_interact_pool(ctypes.byref(g.struct), dense.data_ptr(), out.data_ptr(),
+                                      eo, _stream(stream)), "dlrm_emb_interact_pool")
     return out
 
 

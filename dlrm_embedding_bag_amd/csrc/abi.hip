@@ -12,6 +12,7 @@
 using namespace dlrm;
 
 static_assert(DLRM_MAX_TABLES == kMaxTables, "table limit mismatch");
+static_assert(DLRM_F32 == kF32 && DLRM_BF16 == kBF16, "dtype codes mismatch");
 
 namespace {
 
@@ -22,35 +23,63 @@ bool valid_act(int act) {
 int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Validates the table arguments shared by the gather entry points and packs
-// them into the by-value kernel argument.
-int pack_tables(int32_t K, int32_t B, int32_t D, const float *const *tables,
-                const int64_t *rows, const int32_t *const *indices,
-                const int32_t *const *offsets, const int64_t *n_idx, TableSet &ts, bool &csr,
-                bool &vec_ok) {
+// Validates the bag arguments shared by the gather entry points and packs
+// them into the by-value kernel argument.  gc.vec says whether the dim and
+// the tables allow the 16-byte chunk path (outputs are checked by the caller).
+int pack_bags(const dlrm_bags &g, TableSet &ts, GatherConfig &gc) {
+  const int32_t K = g.num_tables, B = g.batch, D = g.dim;
   if (K < 1 || K > DLRM_MAX_TABLES || B < 0 || D < 1 || D > DLRM_MAX_DIM) return DLRM_ERR_SHAPE;
-  if (!tables || !rows || !indices || !n_idx) return DLRM_ERR_NULL;
+  if (g.table_dtype != DLRM_F32 && g.table_dtype != DLRM_BF16) return DLRM_ERR_SHAPE;
+  if (g.pool != DLRM_POOL_SUM && g.pool != DLRM_POOL_MEAN) return DLRM_ERR_SHAPE;
+  if (!g.tables || !g.rows || !g.indices || !g.n_idx) return DLRM_ERR_NULL;
+  if (g.weights && g.pool != DLRM_POOL_SUM) return DLRM_ERR_UNSUPPORTED;
   memset(&ts, 0, sizeof(ts));
-  csr = offsets != nullptr;
-  vec_ok = (D % 4) == 0;
+  gc.dtype = g.table_dtype;
+  gc.csr = g.offsets != nullptr;
+  gc.psw = g.weights != nullptr;
+  gc.vec = (D % (g.table_dtype == DLRM_BF16 ? 8 : 4)) == 0;
+  ts.mean = g.pool == DLRM_POOL_MEAN;
   for (int k = 0; k < K; ++k) {
-    if (!tables[k]) return DLRM_ERR_NULL;
-    if (rows[k] < 1 || n_idx[k] < 0 || n_idx[k] > INT32_MAX) return DLRM_ERR_SHAPE;
-    if (n_idx[k] > 0 && !indices[k]) return DLRM_ERR_NULL;
-    if (csr) {
-      if (!offsets[k] && B > 0) return DLRM_ERR_NULL;
-    } else if (B > 0 && n_idx[k] % B != 0) {
+    if (!g.tables[k]) return DLRM_ERR_NULL;
+    if (g.rows[k] < 1 || g.n_idx[k] < 0 || g.n_idx[k] > INT32_MAX) return DLRM_ERR_SHAPE;
+    if (g.n_idx[k] > 0 && !g.indices[k]) return DLRM_ERR_NULL;
+    if (gc.psw && g.n_idx[k] > 0 && !g.weights[k]) return DLRM_ERR_NULL;
+    if (gc.csr) {
+      if (!g.offsets[k] && B > 0) return DLRM_ERR_NULL;
+    } else if (B > 0 && g.n_idx[k] % B != 0) {
       return DLRM_ERR_SHAPE;
     }
-    ts.table[k] = tables[k];
-    ts.idx[k] = indices[k];
-    ts.off[k] = csr ? offsets[k] : nullptr;
-    ts.bag[k] = (!csr && B > 0) ? (int32_t)(n_idx[k] / B) : 0;
-    ts.nidx[k] = (int32_t)n_idx[k];
-    vec_ok = vec_ok && aligned16(tables[k]);
+    ts.table[k] = g.tables[k];
+    ts.idx[k] = g.indices[k];
+    ts.off[k] = gc.csr ? g.offsets[k] : nullptr;
+    ts.wt[k] = gc.psw ? g.weights[k] : nullptr;
+    ts.bag[k] = (!gc.csr && B > 0) ? (int32_t)(g.n_idx[k] / B) : 0;
+    ts.nidx[k] = (int32_t)g.n_idx[k];
+    gc.vec = gc.vec && aligned16(g.tables[k]);
   }
   return DLRM_OK;
 }
+
+// The dlrm_bags form of float32 sum lookups.
+dlrm_bags f32_sum_bags(int32_t K, int32_t B, int32_t D, const float *const *tables,
+                       const int64_t *rows, const int32_t *const *indices,
+                       const int32_t *const *offsets, const int64_t *n_idx) {
+  dlrm_bags g;
+  g.num_tables = K;
+  g.batch = B;
+  g.dim = D;
+  g.table_dtype = DLRM_F32;
+  g.pool = DLRM_POOL_SUM;
+  g.tables = reinterpret_cast<const void *const *>(tables);
+  g.rows = rows;
+  g.indices = indices;
+  g.offsets = offsets;
+  g.n_idx = n_idx;
+  g.weights = nullptr;
+  return g;
+}
+
+int chunk_elems(const GatherConfig &gc) { return gc.vec ? (gc.dtype == kBF16 ? 8 : 4) : 1; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DLRM_OK : DLRM_ERR_HIP; }
 
@@ -149,20 +178,26 @@ const char *dlrm_status_string(int status) {
 
 int dlrm_abi_version(void) { return DLRM_ABI_VERSION; }
 
+int emb_bag_pool(const dlrm_bags *bags, float *out, void *stream) {
+  if (!bags) return DLRM_ERR_NULL;
+  TableSet ts;
+  GatherConfig gc;
+  int rc = pack_bags(*bags, ts, gc);
+  if (rc) return rc;
+  if (bags->batch == 0) return DLRM_OK;  // nothing to write: out may be NULL
+  if (!out) return DLRM_ERR_NULL;
+  gc.vec = gc.vec && aligned16(out);
+  return hip_status(launch_emb_bag(ts, gc, bags->batch, bags->num_tables, bags->dim, out,
+                                   (hipStream_t)stream));
+}
+
 int emb_bag_sum_multi(int32_t num_tables, int32_t batch, int32_t dim,
                       const float *const *tables, const int64_t *rows,
                       const int32_t *const *indices, const int32_t *const *offsets,
                       const int64_t *n_idx, float *out, void *stream) {
-  TableSet ts;
-  bool csr, vec_ok;
-  int rc = pack_tables(num_tables, batch, dim, tables, rows, indices, offsets, n_idx, ts, csr,
-                       vec_ok);
-  if (rc) return rc;
-  if (batch == 0) return DLRM_OK;  // nothing to write: out may be NULL
-  if (!out) return DLRM_ERR_NULL;
-  const bool vec4 = vec_ok && aligned16(out);
-  return hip_status(launch_emb_bag(ts, csr, batch, num_tables, dim, vec4, out,
-                                   (hipStream_t)stream));
+  const dlrm_bags g =
+      f32_sum_bags(num_tables, batch, dim, tables, rows, indices, offsets, n_idx);
+  return emb_bag_pool(&g, out, stream);
 }
 
 int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim, const float *dense,
@@ -171,10 +206,12 @@ int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim, const f
     return DLRM_ERR_SHAPE;
   if (batch == 0) return DLRM_OK;  // nothing to read or write
   if (!dense || !emb || !out) return DLRM_ERR_NULL;
-  const bool vec4 = dim % 4 == 0 && aligned16(dense) && aligned16(emb);
+  GatherConfig gc;
+  gc.vec = dim % 4 == 0 && aligned16(dense) && aligned16(emb);
   InteractParams ip{};
   int threads = 0;
-  if (!plan_interact(batch, num_emb, dim, vec4, ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  if (!plan_interact(batch, num_emb, dim, gc.vec, gc.vec ? 4 : 1, ip, threads))
+    return DLRM_ERR_UNSUPPORTED;
   ip.copy_dense = 1;
   ip.dense = dense;
   ip.ld_dense = dim;
@@ -183,25 +220,24 @@ int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim, const f
   ip.out_vec = aligned16(out) && ip.ld_out % 4 == 0;
   ip.emb_out = nullptr;
   ip.emb_in = emb;
-  return hip_status(launch_interact(nullptr, false, ip, threads, vec4, (hipStream_t)stream));
+  return hip_status(launch_interact(nullptr, gc, ip, threads, (hipStream_t)stream));
 }
 
-int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
-                      const float *const *tables, const int64_t *rows,
-                      const int32_t *const *indices, const int32_t *const *offsets,
-                      const int64_t *n_idx, const float *dense, float *out, float *emb_out,
-                      void *stream) {
+int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, float *out,
+                           float *emb_out, void *stream) {
+  if (!bags) return DLRM_ERR_NULL;
   TableSet ts;
-  bool csr, vec_ok;
-  int rc = pack_tables(num_tables, batch, dim, tables, rows, indices, offsets, n_idx, ts, csr,
-                       vec_ok);
+  GatherConfig gc;
+  int rc = pack_bags(*bags, ts, gc);
   if (rc) return rc;
+  const int32_t batch = bags->batch, K = bags->num_tables, dim = bags->dim;
   if (batch == 0) return DLRM_OK;  // nothing to read or write
   if (!dense || !out) return DLRM_ERR_NULL;
-  const bool vec4 = vec_ok && aligned16(dense) && (!emb_out || aligned16(emb_out));
+  gc.vec = gc.vec && aligned16(dense) && (!emb_out || aligned16(emb_out));
   InteractParams ip{};
   int threads = 0;
-  if (!plan_interact(batch, num_tables, dim, vec4, ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  if (!plan_interact(batch, K, dim, gc.vec, chunk_elems(gc), ip, threads))
+    return DLRM_ERR_UNSUPPORTED;
   ip.copy_dense = 1;
   ip.dense = dense;
   ip.ld_dense = dim;
@@ -210,7 +246,17 @@ int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
   ip.out_vec = aligned16(out) && ip.ld_out % 4 == 0;
   ip.emb_out = emb_out;
   ip.emb_in = nullptr;
-  return hip_status(launch_interact(&ts, csr, ip, threads, vec4, (hipStream_t)stream));
+  return hip_status(launch_interact(&ts, gc, ip, threads, (hipStream_t)stream));
+}
+
+int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
+                      const float *const *tables, const int64_t *rows,
+                      const int32_t *const *indices, const int32_t *const *offsets,
+                      const int64_t *n_idx, const float *dense, float *out, float *emb_out,
+                      void *stream) {
+  const dlrm_bags g =
+      f32_sum_bags(num_tables, batch, dim, tables, rows, indices, offsets, n_idx);
+  return dlrm_emb_interact_pool(&g, dense, out, emb_out, stream);
 }
 
 int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda,
@@ -255,9 +301,10 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
   int rc = plan_forward(model, batch, lay);
   if (rc) return rc;
   TableSet ts;
-  bool csr, vec_ok;
-  rc = pack_tables(model->num_tables, batch, model->dim, model->tables, model->rows, indices,
-                   offsets, n_idx, ts, csr, vec_ok);
+  GatherConfig gc;
+  const dlrm_bags g = f32_sum_bags(model->num_tables, batch, model->dim, model->tables,
+                                   model->rows, indices, offsets, n_idx);
+  rc = pack_bags(g, ts, gc);
   if (rc) return rc;
   if (batch == 0) return DLRM_OK;  // nothing to read or write
   if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
@@ -293,10 +340,10 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
   }
 
   // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
-  const bool vec4 = vec_ok && lay.ldR % 4 == 0;
+  gc.vec = gc.vec && lay.ldR % 4 == 0;
   InteractParams ip{};
   int threads = 0;
-  if (!plan_interact(B, K, D, vec4, ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  if (!plan_interact(B, K, D, gc.vec, chunk_elems(gc), ip, threads)) return DLRM_ERR_UNSUPPORTED;
   ip.copy_dense = 0;
   ip.dense = R;
   ip.ld_dense = lay.ldR;
@@ -305,7 +352,7 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
   ip.out_vec = 1;
   ip.emb_out = nullptr;
   ip.emb_in = nullptr;
-  rc = hip_status(launch_interact(&ts, csr, ip, threads, vec4, st));
+  rc = hip_status(launch_interact(&ts, gc, ip, threads, st));
   if (rc) return rc;
 
   // Top MLP on cat(dense, dots) = R.

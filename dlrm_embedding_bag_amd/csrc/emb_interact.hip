@@ -31,6 +31,8 @@
 // scalar path keeps one quad per dot with p -> (i, j) in closed form.
 // The fused kernel pools straight into the LDS tile, so the (B, K, D) pooled
 // tensor never round-trips through HBM.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -78,111 +80,234 @@ __device__ __forceinline__ void bag_bounds(const TableSet &ts, int k, int b, int
   }
 }
 
-// Generic path: pools bag [s, e) of `tab` for column chunk c (VW floats wide)
-// of a row of nvec chunks, each lane reading the indices itself.
-template <int VW>
-__device__ __forceinline__ typename Vec<VW>::T pool_chunk(const float *__restrict__ tab,
-                                                          const int32_t *__restrict__ idx,
-                                                          int s, int e, int nvec, int c) {
-  using V = typename Vec<VW>::T;
-  const V *col = reinterpret_cast<const V *>(tab) + c;
-  V acc = vzero<V>();
+// A row chunk: what one lane loads per row.  On the vector path it is 16
+// bytes (4 float32 or 8 bfloat16 elements), on the scalar path one element.
+// bfloat16 is widened to float32 exactly (its bits are the high half of the
+// float32), and the bag is accumulated in float32.
+template <typename TT, int VW>
+struct RowChunk;
+
+template <>
+struct RowChunk<float, 4> {
+  using Raw = float4;
+  static constexpr int EL = 4;
+  static __device__ __forceinline__ Raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ __forceinline__ void add(float *a, Raw r) {
+    a[0] += r.x;
+    a[1] += r.y;
+    a[2] += r.z;
+    a[3] += r.w;
+  }
+  static __device__ __forceinline__ void fma(float *a, float w, Raw r) {
+    a[0] = __builtin_fmaf(w, r.x, a[0]);
+    a[1] = __builtin_fmaf(w, r.y, a[1]);
+    a[2] = __builtin_fmaf(w, r.z, a[2]);
+    a[3] = __builtin_fmaf(w, r.w, a[3]);
+  }
+};
+
+template <>
+struct RowChunk<float, 1> {
+  using Raw = float;
+  static constexpr int EL = 1;
+  static __device__ __forceinline__ Raw zero() { return 0.f; }
+  static __device__ __forceinline__ void add(float *a, Raw r) { a[0] += r; }
+  static __device__ __forceinline__ void fma(float *a, float w, Raw r) {
+    a[0] = __builtin_fmaf(w, r, a[0]);
+  }
+};
+
+// bfloat16 element 2i of a chunk is the low half of 32-bit word i.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <>
+struct RowChunk<uint16_t, 4> {
+  using Raw = uint4;
+  static constexpr int EL = 8;
+  static __device__ __forceinline__ Raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  static __device__ __forceinline__ void add(float *a, Raw r) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] += bf16_lo(w[i]);
+      a[2 * i + 1] += bf16_hi(w[i]);
+    }
+  }
+  static __device__ __forceinline__ void fma(float *a, float wt, Raw r) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] = __builtin_fmaf(wt, bf16_lo(w[i]), a[2 * i]);
+      a[2 * i + 1] = __builtin_fmaf(wt, bf16_hi(w[i]), a[2 * i + 1]);
+    }
+  }
+};
+
+template <>
+struct RowChunk<uint16_t, 1> {
+  using Raw = uint16_t;
+  static constexpr int EL = 1;
+  static __device__ __forceinline__ Raw zero() { return 0; }
+  static __device__ __forceinline__ void add(float *a, Raw r) { a[0] += bf16_lo(r); }
+  static __device__ __forceinline__ void fma(float *a, float w, Raw r) {
+    a[0] = __builtin_fmaf(w, bf16_lo(r), a[0]);
+  }
+};
+
+// Stores chunk c (EL floats) of a float32 row.
+template <int EL>
+__device__ __forceinline__ void store_chunk(float *row, int c, const float *a) {
+  if constexpr (EL == 1) {
+    row[c] = a[0];
+  } else if constexpr (EL == 4) {
+    reinterpret_cast<float4 *>(row)[c] = make_float4(a[0], a[1], a[2], a[3]);
+  } else {
+    float4 *p = reinterpret_cast<float4 *>(row) + 2 * c;
+    p[0] = make_float4(a[0], a[1], a[2], a[3]);
+    p[1] = make_float4(a[4], a[5], a[6], a[7]);
+  }
+}
+
+// Adds row chunk v, weighted by w when PSW.
+template <typename RC, bool PSW>
+__device__ __forceinline__ void accumulate(float *acc, float w, typename RC::Raw v) {
+  if constexpr (PSW)
+    RC::fma(acc, w, v);
+  else
+    RC::add(acc, v);
+}
+
+// Generic path: pools bag [s, e) of `tab` for chunk c of a row of nvec chunks,
+// each lane reading the indices (and weights) itself.
+template <typename TT, int VW, bool PSW>
+__device__ __forceinline__ void pool_chunk(const TT *__restrict__ tab,
+                                           const int32_t *__restrict__ idx,
+                                           const float *__restrict__ wt, int s, int e, int nvec,
+                                           int c, float *acc) {
+  using RC = RowChunk<TT, VW>;
+  using Raw = typename RC::Raw;
+  const Raw *col = reinterpret_cast<const Raw *>(tab) + c;
+#pragma unroll
+  for (int i = 0; i < RC::EL; ++i) acc[i] = 0.f;
   int l = s;
   for (; l + kUnroll <= e; l += kUnroll) {
     int r[kUnroll];
+    float w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) r[u] = idx[l + u];
-    V v[kUnroll];
+    for (int u = 0; u < kUnroll; ++u) {
+      r[u] = idx[l + u];
+      w[u] = PSW ? wt[l + u] : 1.f;
+    }
+    Raw v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) v[u] = col[(size_t)(uint32_t)r[u] * (size_t)nvec];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc = operator_add(acc, v[u]);
+    for (int u = 0; u < kUnroll; ++u) accumulate<RC, PSW>(acc, w[u], v[u]);
   }
   const int rem = e - l;
   if (rem > 0) {
     int r[kUnroll - 1];
+    float w[kUnroll - 1];
 #pragma unroll
-    for (int u = 0; u < kUnroll - 1; ++u) r[u] = (u < rem) ? idx[l + u] : 0;
-    V v[kUnroll - 1];
+    for (int u = 0; u < kUnroll - 1; ++u) {
+      r[u] = (u < rem) ? idx[l + u] : 0;
+      w[u] = (PSW && u < rem) ? wt[l + u] : 1.f;
+    }
+    Raw v[kUnroll - 1];
 #pragma unroll
     for (int u = 0; u < kUnroll - 1; ++u)
-      v[u] = (u < rem) ? col[(size_t)(uint32_t)r[u] * (size_t)nvec] : vzero<V>();
+      v[u] = (u < rem) ? col[(size_t)(uint32_t)r[u] * (size_t)nvec] : RC::zero();
 #pragma unroll
     for (int u = 0; u < kUnroll - 1; ++u)
-      if (u < rem) acc = operator_add(acc, v[u]);
+      if (u < rem) accumulate<RC, PSW>(acc, w[u], v[u]);
   }
-  return acc;
 }
 
 // Shuffle path (G lanes per group, G a power of two <= 64, nvec % G == 0):
-// pools bag [s, e) for column chunk c of float4 width.  Every lane of the
-// group must call this together (the index broadcast reads the other lanes);
-// gbase is the wave lane of the group's first lane.
-template <int G>
-__device__ __forceinline__ float4 pool_group(const float *__restrict__ tab,
-                                             const int32_t *__restrict__ idx, int s, int e,
-                                             int nvec, int c_lane, int c, int gbase) {
+// pools bag [s, e) for 16-byte chunk c.  Every lane of the group must call
+// this together (the index and weight broadcasts read the other lanes); gbase
+// is the wave lane of the group's first lane.
+template <typename TT, int G, bool PSW>
+__device__ __forceinline__ void pool_group(const TT *__restrict__ tab,
+                                           const int32_t *__restrict__ idx,
+                                           const float *__restrict__ wt, int s, int e, int nvec,
+                                           int c_lane, int c, int gbase, float *acc) {
+  using RC = RowChunk<TT, 4>;
+  using Raw = typename RC::Raw;
   constexpr int T = (kRound + G - 1) / G;  // index registers per lane
-  const float4 *col = reinterpret_cast<const float4 *>(tab) + c;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const Raw *col = reinterpret_cast<const Raw *>(tab) + c;
+#pragma unroll
+  for (int i = 0; i < RC::EL; ++i) acc[i] = 0.f;
   for (int l0 = s; l0 < e; l0 += kRound) {
     const int n = min(kRound, e - l0);
     int mine[T];
+    float mine_w[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int l = c_lane + G * t;
       mine[t] = (l < n) ? idx[l0 + l] : 0;
+      mine_w[t] = (PSW && l < n) ? wt[l0 + l] : 0.f;
     }
-    float4 v[kRound];
+    Raw v[kRound];
+    float w[kRound];
 #pragma unroll
     for (int u = 0; u < kRound; ++u) {
-      const int r = __builtin_amdgcn_ds_bpermute((gbase + (u % G)) << 2, mine[u / G]);
+      const int src = (gbase + (u % G)) << 2;
+      const int r = __builtin_amdgcn_ds_bpermute(src, mine[u / G]);
+      w[u] = PSW ? __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(mine_w[u / G])))
+                 : 1.f;
 #if DLRM_ROW_NT
       typedef float f4v __attribute__((ext_vector_type(4)));
+      static_assert(sizeof(Raw) == sizeof(f4v), "16-byte chunks");
       f4v tv = (u < n) ? __builtin_nontemporal_load(reinterpret_cast<const f4v *>(
                              col + (size_t)(uint32_t)r * (size_t)nvec))
                        : f4v{0.f, 0.f, 0.f, 0.f};
-      v[u] = make_float4(tv.x, tv.y, tv.z, tv.w);
+      v[u] = __builtin_bit_cast(Raw, tv);
 #else
-      v[u] = (u < n) ? col[(size_t)(uint32_t)r * (size_t)nvec] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = (u < n) ? col[(size_t)(uint32_t)r * (size_t)nvec] : RC::zero();
 #endif
     }
 #pragma unroll
     for (int u = 0; u < kRound; ++u)
-      if (u < n) acc = operator_add(acc, v[u]);
+      if (u < n) accumulate<RC, PSW>(acc, w[u], v[u]);
   }
-  return acc;
 }
 
-// Pools bag (b, k) into `row` (nvec chunks of VW floats) and optionally `eo`.
-// All G lanes of the group call it together.
-template <int VW, int GS, bool CSR>
+// Pools bag (b, k) into `row` (nvec chunks) and optionally `eo`, dividing by
+// the bag size for mean pooling.  All G lanes of the group call it together.
+template <typename TT, int VW, int GS, bool CSR, bool PSW>
 __device__ __forceinline__ void pool_bag(const TableSet &ts, int k, int b, int B, int nvec,
-                                         int G, int c0, typename Vec<VW>::T *row,
-                                         typename Vec<VW>::T *eo) {
-  using V = typename Vec<VW>::T;
+                                         int G, int c0, float *row, float *eo) {
+  constexpr int EL = RowChunk<TT, VW>::EL;
   int bs, be;
   bag_bounds<CSR>(ts, k, b, B, bs, be);
+  const TT *tab = static_cast<const TT *>(ts.table[k]);
+  const float *wt = PSW ? ts.wt[k] : nullptr;
   for (int c = c0; c < nvec; c += G) {
-    V v;
+    float acc[EL];
     if constexpr (GS > 0) {
       const int gbase = (threadIdx.x & 63) & ~(GS - 1);
-      v = pool_group<GS>(ts.table[k], ts.idx[k], bs, be, nvec, c0, c, gbase);
+      pool_group<TT, GS, PSW>(tab, ts.idx[k], wt, bs, be, nvec, c0, c, gbase, acc);
     } else {
-      v = pool_chunk<VW>(ts.table[k], ts.idx[k], bs, be, nvec, c);
+      pool_chunk<TT, VW, PSW>(tab, ts.idx[k], wt, bs, be, nvec, c, acc);
     }
-    row[c] = v;
-    if (eo) eo[c] = v;
+    if (ts.mean && be > bs) {
+      const float n = (float)(be - bs);
+#pragma unroll
+      for (int i = 0; i < EL; ++i) acc[i] = acc[i] / n;
+    }
+    store_chunk<EL>(row, c, acc);
+    if (eo) store_chunk<EL>(eo, c, acc);
   }
 }
 
 // ---------------------------------------------------------------------------
-// emb_bag_sum_multi: grid over bags, one group of G lanes per bag (b, k).
+// emb_bag_pool: grid over bags, one group of G lanes per bag (b, k).
 // ---------------------------------------------------------------------------
-template <int VW, int GS, bool CSR>
+template <typename TT, int VW, int GS, bool CSR, bool PSW>
 __global__ __launch_bounds__(256) void emb_bag_kernel(TableSet ts, int B, int K, int D,
                                                       int G, float *__restrict__ out) {
-  using V = typename Vec<VW>::T;
   const int groups = blockDim.x / G;
   const int g = threadIdx.x / G;
   const int c0 = threadIdx.x - g * G;
@@ -191,8 +316,8 @@ __global__ __launch_bounds__(256) void emb_bag_kernel(TableSet ts, int B, int K,
   if (task >= (int64_t)B * K) return;
   const int b = (int)(task / K);
   const int k = (int)(task - (int64_t)b * K);
-  V *dst = reinterpret_cast<V *>(out + task * D);
-  pool_bag<VW, GS, CSR>(ts, k, b, B, D / VW, G, c0, dst, nullptr);
+  pool_bag<TT, VW, GS, CSR, PSW>(ts, k, b, B, D / RowChunk<TT, VW>::EL, G, c0, out + task * D,
+                                 nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -328,7 +453,7 @@ __device__ __forceinline__ void dots_blocked(const float *X, const InteractParam
   }
 }
 
-template <int VW, int MODE, bool CSR, int GS>
+template <typename TT, int VW, int MODE, bool CSR, int GS, bool PSW>
 __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractParams ip) {
   using V = typename Vec<VW>::T;
   extern __shared__ float4 lds_raw[];
@@ -367,13 +492,14 @@ __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractPar
       const int k = t - s * K;
       const int b = b0 + s;
       if (b >= B) continue;
-      V *row = reinterpret_cast<V *>(X + (size_t)(s * FR + 1 + k) * DP);
+      float *row = X + (size_t)(s * FR + 1 + k) * DP;
       if (MODE == MODE_FUSED) {
-        V *eo = ip.emb_out ? reinterpret_cast<V *>(ip.emb_out + ((int64_t)b * K + k) * D) : nullptr;
-        pool_bag<VW, GS, CSR>(ts, k, b, B, nvec, G, c0, row, eo);
+        float *eo = ip.emb_out ? ip.emb_out + ((int64_t)b * K + k) * D : nullptr;
+        pool_bag<TT, VW, GS, CSR, PSW>(ts, k, b, B, D / RowChunk<TT, VW>::EL, G, c0, row, eo);
       } else {
         const V *src = reinterpret_cast<const V *>(ip.emb_in + ((int64_t)b * K + k) * D);
-        for (int c = c0; c < nvec; c += G) row[c] = src[c];
+        V *dst = reinterpret_cast<V *>(row);
+        for (int c = c0; c < nvec; c += G) dst[c] = src[c];
       }
     }
   }
@@ -401,52 +527,92 @@ int shuffle_group(int nvec) {
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-static int lanes_per_row(int D, int VW) {
-  const int nvec = D / VW;
+static int lanes_per_row(int D, int el) {
+  const int nvec = D / el;
   return nvec < kWave ? nvec : kWave;
 }
 
-#define DLRM_GS_SWITCH(gs, BODY)            \
-  switch (gs) {                             \
-    case 4: { constexpr int GSV = 4; BODY; } break;   \
-    case 8: { constexpr int GSV = 8; BODY; } break;   \
-    case 16: { constexpr int GSV = 16; BODY; } break; \
-    case 32: { constexpr int GSV = 32; BODY; } break; \
-    case 64: { constexpr int GSV = 64; BODY; } break; \
-    default: { constexpr int GSV = 0; BODY; } break;  \
-  }
+// Elements per row chunk: 4 (float32) or 8 (bfloat16) on the vector path, 1
+// on the scalar path.
+static int chunk_elems(int dtype, bool vec) { return vec ? (dtype == kBF16 ? 8 : 4) : 1; }
 
-hipError_t launch_emb_bag(const TableSet &ts, bool csr, int B, int K, int D, bool vec4,
+template <typename T>
+struct TypeTag {
+  using type = T;
+};
+template <int V>
+using IntC = std::integral_constant<int, V>;
+template <bool V>
+using BoolC = std::integral_constant<bool, V>;
+
+// Calls fn(TypeTag<TT>, IntC<VW>, BoolC<CSR>, IntC<GS>, BoolC<PSW>) with the
+// compile-time form of the runtime gather configuration.
+template <typename TT, int VW, bool CSR, bool PSW, typename Fn>
+static void dispatch_gs(int gs, Fn &&fn) {
+  const auto t = TypeTag<TT>{};
+  if constexpr (VW == 1) {
+    fn(t, IntC<1>{}, BoolC<CSR>{}, IntC<0>{}, BoolC<PSW>{});
+  } else {
+    switch (gs) {
+      case 4: fn(t, IntC<4>{}, BoolC<CSR>{}, IntC<4>{}, BoolC<PSW>{}); break;
+      case 8: fn(t, IntC<4>{}, BoolC<CSR>{}, IntC<8>{}, BoolC<PSW>{}); break;
+      case 16: fn(t, IntC<4>{}, BoolC<CSR>{}, IntC<16>{}, BoolC<PSW>{}); break;
+      case 32: fn(t, IntC<4>{}, BoolC<CSR>{}, IntC<32>{}, BoolC<PSW>{}); break;
+      case 64: fn(t, IntC<4>{}, BoolC<CSR>{}, IntC<64>{}, BoolC<PSW>{}); break;
+      default: fn(t, IntC<4>{}, BoolC<CSR>{}, IntC<0>{}, BoolC<PSW>{}); break;
+    }
+  }
+}
+
+template <typename TT, int VW, typename Fn>
+static void dispatch_flags(bool csr, bool psw, int gs, Fn &&fn) {
+  if (csr) {
+    if (psw)
+      dispatch_gs<TT, VW, true, true>(gs, fn);
+    else
+      dispatch_gs<TT, VW, true, false>(gs, fn);
+  } else {
+    if (psw)
+      dispatch_gs<TT, VW, false, true>(gs, fn);
+    else
+      dispatch_gs<TT, VW, false, false>(gs, fn);
+  }
+}
+
+template <typename Fn>
+static void dispatch_gather(const GatherConfig &gc, int D, Fn &&fn) {
+  const int gs = gc.vec ? shuffle_group(D / chunk_elems(gc.dtype, true)) : 0;
+  if (gc.dtype == kBF16) {
+    if (gc.vec)
+      dispatch_flags<uint16_t, 4>(gc.csr, gc.psw, gs, fn);
+    else
+      dispatch_flags<uint16_t, 1>(gc.csr, gc.psw, gs, fn);
+  } else {
+    if (gc.vec)
+      dispatch_flags<float, 4>(gc.csr, gc.psw, gs, fn);
+    else
+      dispatch_flags<float, 1>(gc.csr, gc.psw, gs, fn);
+  }
+}
+
+hipError_t launch_emb_bag(const TableSet &ts, const GatherConfig &gc, int B, int K, int D,
                           float *out, hipStream_t stream) {
-  const int VW = vec4 ? 4 : 1;
-  const int G = lanes_per_row(D, VW);
+  const int G = lanes_per_row(D, chunk_elems(gc.dtype, gc.vec));
   const int threads = 256;
   const int groups = threads / G;
   const int64_t tasks = (int64_t)B * K;
   const int64_t blocks = (tasks + groups - 1) / groups;
   dim3 grid((unsigned)blocks), block(threads);
-  if (vec4) {
-    const int gs = shuffle_group(D / 4);
-    if (csr) {
-      DLRM_GS_SWITCH(gs, hipLaunchKernelGGL((emb_bag_kernel<4, GSV, true>), grid, block, 0,
-                                            stream, ts, B, K, D, G, out));
-    } else {
-      DLRM_GS_SWITCH(gs, hipLaunchKernelGGL((emb_bag_kernel<4, GSV, false>), grid, block, 0,
-                                            stream, ts, B, K, D, G, out));
-    }
-  } else {
-    if (csr)
-      hipLaunchKernelGGL((emb_bag_kernel<1, 0, true>), grid, block, 0, stream, ts, B, K, D, G,
-                         out);
-    else
-      hipLaunchKernelGGL((emb_bag_kernel<1, 0, false>), grid, block, 0, stream, ts, B, K, D, G,
-                         out);
-  }
+  dispatch_gather(gc, D, [&](auto tt, auto vw, auto csr, auto gs, auto psw) {
+    using TT = typename decltype(tt)::type;
+    hipLaunchKernelGGL((emb_bag_kernel<TT, decltype(vw)::value, decltype(gs)::value,
+                                       decltype(csr)::value, decltype(psw)::value>),
+                       grid, block, 0, stream, ts, B, K, D, G, out);
+  });
   return hipGetLastError();
 }
 
-bool plan_interact(int B, int K, int D, bool vec4, InteractParams &ip, int &threads) {
-  const int VW = vec4 ? 4 : 1;
+bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, int &threads) {
   const int F = K + 1;
   ip.B = B;
   ip.K = K;
@@ -454,7 +620,7 @@ bool plan_interact(int B, int K, int D, bool vec4, InteractParams &ip, int &thre
   ip.P = F * (F - 1) / 2;
   ip.DP = D + (vec4 ? 4 : 1);
   ip.FR = vec4 ? ((F + 3) & ~3) : F;
-  ip.G = lanes_per_row(D, VW);
+  ip.G = lanes_per_row(D, el);
   const size_t per_sample = (size_t)ip.FR * ip.DP * sizeof(float);
   if (per_sample > kLdsBudget) return false;
   const int lanes_per_sample = K * ip.G;
@@ -479,37 +645,26 @@ bool plan_interact(int B, int K, int D, bool vec4, InteractParams &ip, int &thre
   return true;
 }
 
-hipError_t launch_interact(const TableSet *ts, bool csr, const InteractParams &ip, int threads,
-                           bool vec4, hipStream_t stream) {
+hipError_t launch_interact(const TableSet *ts, const GatherConfig &gc, const InteractParams &ip,
+                           int threads, hipStream_t stream) {
   dim3 grid((unsigned)((ip.B + ip.S - 1) / ip.S)), block(threads);
   const size_t lds = (size_t)ip.lds_bytes;
-  TableSet empty{};
-  const TableSet &t = ts ? *ts : empty;
   if (ts) {
-    if (vec4) {
-      const int gs = shuffle_group(ip.D / 4);
-      if (csr) {
-        DLRM_GS_SWITCH(gs, hipLaunchKernelGGL((interact_kernel<4, MODE_FUSED, true, GSV>), grid,
-                                              block, lds, stream, t, ip));
-      } else {
-        DLRM_GS_SWITCH(gs, hipLaunchKernelGGL((interact_kernel<4, MODE_FUSED, false, GSV>), grid,
-                                              block, lds, stream, t, ip));
-      }
-    } else {
-      if (csr)
-        hipLaunchKernelGGL((interact_kernel<1, MODE_FUSED, true, 0>), grid, block, lds, stream, t,
-                           ip);
-      else
-        hipLaunchKernelGGL((interact_kernel<1, MODE_FUSED, false, 0>), grid, block, lds, stream,
-                           t, ip);
-    }
+    dispatch_gather(gc, ip.D, [&](auto tt, auto vw, auto csr, auto gs, auto psw) {
+      using TT = typename decltype(tt)::type;
+      hipLaunchKernelGGL((interact_kernel<TT, decltype(vw)::value, MODE_FUSED,
+                                          decltype(csr)::value, decltype(gs)::value,
+                                          decltype(psw)::value>),
+                         grid, block, lds, stream, *ts, ip);
+    });
   } else {
-    if (vec4)
-      hipLaunchKernelGGL((interact_kernel<4, MODE_LOAD, false, 0>), grid, block, lds, stream, t,
-                         ip);
+    TableSet empty{};
+    if (gc.vec)
+      hipLaunchKernelGGL((interact_kernel<float, 4, MODE_LOAD, false, 0, false>), grid, block,
+                         lds, stream, empty, ip);
     else
-      hipLaunchKernelGGL((interact_kernel<1, MODE_LOAD, false, 0>), grid, block, lds, stream, t,
-                         ip);
+      hipLaunchKernelGGL((interact_kernel<float, 1, MODE_LOAD, false, 0, false>), grid, block,
+                         lds, stream, empty, ip);
   }
   return hipGetLastError();
 }

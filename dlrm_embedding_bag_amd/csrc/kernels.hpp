@@ -27,15 +27,26 @@ struct InteractParams {
   const float *emb_in;   // (B, K, D) input of the interaction-only kernel
 };
 
-hipError_t launch_emb_bag(const TableSet &ts, bool csr, int B, int K, int D, bool vec4,
+// How a gather reads its bags: table storage type, vector (16-byte chunk) or
+// scalar path, CSR offsets, per-sample weights.
+struct GatherConfig {
+  int dtype = kF32;
+  bool vec = false;
+  bool csr = false;
+  bool psw = false;
+};
+
+hipError_t launch_emb_bag(const TableSet &ts, const GatherConfig &gc, int B, int K, int D,
                           float *out, hipStream_t stream);
 
-// Fills the geometry fields of `ip`; false if one sample's tile exceeds LDS.
-bool plan_interact(int B, int K, int D, bool vec4, InteractParams &ip, int &threads);
+// Fills the geometry fields of `ip` for a gather whose row chunks hold `el`
+// elements (1 when there is no gather); false if one sample's tile exceeds LDS.
+bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, int &threads);
 
-// ts == nullptr: interaction over ip.emb_in; otherwise fused gather + interaction.
-hipError_t launch_interact(const TableSet *ts, bool csr, const InteractParams &ip, int threads,
-                           bool vec4, hipStream_t stream);
+// ts == nullptr: interaction over ip.emb_in (gc.vec selects the vector path);
+// otherwise fused gather + interaction.
+hipError_t launch_interact(const TableSet *ts, const GatherConfig &gc, const InteractParams &ip,
+                           int threads, hipStream_t stream);
 
 constexpr int kMaxChainLayers = 4;
 constexpr int kMaxChainWidth = 512;  // widest layer the MLP chain keeps in LDS

@@ -9,6 +9,13 @@ Recipe (every stream is seeded from a base seed and a fixed stream number):
   indices of k   stream 2000 + k   int32, uniform on [0, rows) or bounded Zipf
   dense input    stream 3000       N(0, 1) float32
   MLP layer i    stream 4000 + i   Xavier-uniform weight, zero bias
+  weights of k   stream 5000 + k   per-sample weights, U[0, 1) float32
+  lengths of k   stream 6000 + k   CSR bag sizes, uniform integers on [0, 2L]
+bfloat16 tables keep the high 16 bits of the float32 draw (truncation), as
+bit patterns (uint16 on the host, torch.bfloat16 on the device).
+CSR workloads draw one bag size per (sample, table), mean L, empty bags
+included; the indices of table k then number the sum of its sizes and the
+offsets are the exclusive prefix sums of the sizes.
 Bounded Zipf(s) draws rank r in 1..N with probability proportional to r^-s
 by inverse CDF, then scatters ranks over rows with the bijection
 row = (a (r - 1) + 7919 k) mod N, a = 999983 (prime), so hot rows are not
@@ -47,6 +54,10 @@ class Workload:
     bottom: tuple = ()             # bottom MLP widths after dense_in
     top: tuple = ()                # top MLP widths after the interaction
     table_source: str = "host"     # "host" (numpy) or "device" (torch CUDA)
+    table_dtype: str = "f32"       # "f32" or "bf16" table storage
+    pool: str = "sum"              # "sum" or "mean"
+    weighted: bool = False         # per-sample weights (sum only)
+    lengths: str = "fixed"         # "fixed" (L per bag) or "uniform" (0..2L, CSR)
     description: str = field(default="", compare=False)
 
     @property
@@ -86,6 +97,22 @@ WORKLOADS = {
         dist="zipf", table_source="device",
         description="B=16384, K=26 tables x 4,000,000 rows x D=128 (~53 GB), "
                     "40 indices/bag Zipf(1.05)"),
+    "nc32-bf16": Workload(
+        "nc32-bf16", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
+        dist="zipf", table_source="device", table_dtype="bf16",
+        description="nc32 with bfloat16 tables (128-byte rows)"),
+    "nc32-mean": Workload(
+        "nc32-mean", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
+        dist="zipf", table_source="device", pool="mean",
+        description="nc32 with mean pooling"),
+    "nc32-weighted": Workload(
+        "nc32-weighted", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
+        dist="zipf", table_source="device", weighted=True,
+        description="nc32 with per-sample weights U[0, 1)"),
+    "nc32-csr": Workload(
+        "nc32-csr", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
+        dist="zipf", table_source="device", lengths="uniform",
+        description="nc32 with CSR bags of uniform size on [0, 40] (mean 20)"),
     "dlrm": Workload(
         "dlrm", batch=8192, num_tables=26, rows=1_000_000, dim=64, bag=20,
         dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1),
@@ -127,10 +154,26 @@ def scatter_ranks(ranks: np.ndarray, n: int, table: int) -> np.ndarray:
     return (ranks.astype(np.int64) * a + ZIPF_SCATTER_ADD * table) % n
 
 
-def indices(w: Workload, table: int, seed: int = 0, batch: int = None) -> np.ndarray:
-    """(B*L,) int32 row indices of table `table`."""
+def bag_lengths(w: Workload, table: int, seed: int = 0, batch: int = None) -> np.ndarray:
+    """(B,) int64 bag sizes of table `table`: L each, or uniform on [0, 2L]."""
     b = w.batch if batch is None else batch
-    count = b * w.bag
+    if w.lengths == "fixed":
+        return np.full(b, w.bag, np.int64)
+    if w.lengths == "uniform":
+        return _rng(seed, 6000 + table).integers(0, 2 * w.bag + 1, size=b, dtype=np.int64)
+    raise ValueError(f"unknown bag-length mix {w.lengths!r}")
+
+
+def csr_offsets(w: Workload, table: int, seed: int = 0, batch: int = None) -> np.ndarray:
+    """(B,) int32 bag starts: exclusive prefix sums of bag_lengths."""
+    lens = bag_lengths(w, table, seed, batch)
+    return np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32)
+
+
+def indices(w: Workload, table: int, seed: int = 0, batch: int = None) -> np.ndarray:
+    """(n_idx,) int32 row indices of table `table` (n_idx = B*L for fixed bags)."""
+    b = w.batch if batch is None else batch
+    count = int(bag_lengths(w, table, seed, b).sum())
     rng = _rng(seed, 2000 + table)
     if w.dist == "uniform":
         idx = rng.integers(0, w.rows, size=count, dtype=np.int64)
@@ -170,6 +213,33 @@ def table_device(w: Workload, table: int, seed: int = 0, device="cuda", rows: in
     g.manual_seed(torch_seed(seed, 1000 + table))
     t = torch.randn((r, w.dim), generator=g, device=device, dtype=torch.float32)
     return t.mul_(w.table_std)
+
+
+def sample_weights(w: Workload, table: int, n: int, seed: int = 0) -> np.ndarray:
+    """(n,) float32 per-sample weights U[0, 1) of table `table`."""
+    return _rng(seed, 5000 + table).random(n, dtype=np.float32)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) holding the high half of float32 x."""
+    x = np.ascontiguousarray(x, np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def table_host_typed(w: Workload, table: int, seed: int = 0, rows: int = None) -> np.ndarray:
+    """table_host in the workload's storage type (uint16 bit patterns for bf16)."""
+    t = table_host(w, table, seed, rows)
+    return bf16_bits(t) if w.table_dtype == "bf16" else t
+
+
+def table_device_typed(w: Workload, table: int, seed: int = 0, device="cuda",
+                       rows: int = None):
+    """table_device in the workload's storage type (torch.bfloat16 for bf16)."""
+    import torch
+    t = table_device(w, table, seed, device, rows)
+    if w.table_dtype != "bf16":
+        return t
+    return (t.view(torch.int32) >> 16).to(torch.int16).view(torch.bfloat16)
 
 
 def dyadic(rng: np.random.Generator, shape, scale_bits: int = 8,

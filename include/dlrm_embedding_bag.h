@@ -145,6 +145,82 @@ DLRM_API int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
                       const float *dense, float *out, float *emb_out,
                       void *stream);
 
+/* Storage type of embedding-table rows. */
+typedef enum dlrm_dtype {
+  DLRM_F32 = 0,  /* IEEE float32                                            */
+  DLRM_BF16 = 1  /* bfloat16: the high 16 bits of a float32, widened exactly */
+} dlrm_dtype;
+
+/* How a bag's rows are combined (the modes of torch.nn.EmbeddingBag). */
+typedef enum dlrm_pool {
+  DLRM_POOL_SUM = 0,  /* sum of the rows (times their weights, if given)   */
+  DLRM_POOL_MEAN = 1  /* sum divided by the bag size; an empty bag gives 0 */
+} dlrm_pool;
+
+/*
+ * A set of K EmbeddingBag lookups over one batch, the general form of the
+ * arguments of emb_bag_sum_multi.  Every array of this struct is [host]; the
+ * tables, indices, offsets and weights they point to are device memory.
+ *
+ *   num_tables   K, 1 <= K <= DLRM_MAX_TABLES
+ *   batch        B >= 0
+ *   dim          D, 1 <= D <= DLRM_MAX_DIM
+ *   table_dtype  a dlrm_dtype, shared by all K tables
+ *   pool         a dlrm_pool
+ *   tables       K device pointers; table k is (rows[k], D) of table_dtype
+ *   rows, indices, offsets, n_idx   as in emb_bag_sum_multi (offsets NULL:
+ *                uniform stride; else CSR bag starts)
+ *   weights      NULL, or K device pointers: weights[k] is (n_idx[k],)
+ *                float32, the per-sample weight of each index (the
+ *                per_sample_weights of torch.nn.EmbeddingBag); sum pooling
+ *                only (with DLRM_POOL_MEAN it is DLRM_ERR_UNSUPPORTED, as in
+ *                torch)
+ *
+ * Pooling ([FASTPATHS] translator dispatch, aten._embedding_bag lowering:
+ * the pages' path takes sum mode only and rejects per-sample weights; the
+ * other options follow torch.nn.EmbeddingBag):
+ *   sum   out[b, k, :] = sum_{l in bag(b,k)} w_l * row(tables[k], indices[k][l])
+ *         with w_l = weights[k][l], or 1 without weights
+ *   mean  out[b, k, :] = (sum_{l in bag(b,k)} row(...)) / |bag(b,k)|, 0 if empty
+ * Rows of bfloat16 tables are widened to float32 exactly; accumulation is
+ * float32 in bag order.
+ * The vector path needs dim % 4 == 0 (float32) or dim % 8 == 0 (bfloat16)
+ * and 16-byte aligned tables and outputs; anything else takes the scalar path.
+ */
+typedef struct dlrm_bags {
+  int32_t num_tables;
+  int32_t batch;
+  int32_t dim;
+  int32_t table_dtype;
+  int32_t pool;
+  const void *const *tables;
+  const int64_t *rows;
+  const int32_t *const *indices;
+  const int32_t *const *offsets;
+  const int64_t *n_idx;
+  const float *const *weights;
+} dlrm_bags;
+
+/*
+ * emb_bag_pool -- K EmbeddingBag lookups of any dlrm_bags form in one launch.
+ *   bags   [host] the lookups
+ *   out    (B, K, D) float32
+ * A zero batch is a no-op.  emb_bag_sum_multi is this call with float32
+ * tables, sum pooling and no weights.
+ */
+DLRM_API int emb_bag_pool(const dlrm_bags *bags, float *out, void *stream);
+
+/*
+ * dlrm_emb_interact_pool -- emb_bag_pool fused with dlrm_interact_lower_tri
+ * in one launch, as dlrm_emb_interact is for float32 sum bags.
+ *   bags     [host] the lookups (K = bags->num_tables, D = bags->dim)
+ *   dense    (B, D) float32
+ *   out      (B, D + F(F-1)/2) float32, F = K + 1
+ *   emb_out  NULL, or (B, K, D) float32 receiving the pooled vectors
+ */
+DLRM_API int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, float *out,
+                                    float *emb_out, void *stream);
+
 /*
  * linear_bias_act -- fused linear layer ([FASTPATHS] matmul2d.rs, Activation
  * epilogue; linear_bias / linear_bias_relu / linear_bias_sigmoid):

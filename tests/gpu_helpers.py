@@ -57,6 +57,47 @@ def sampled_subproblem(tables_dev, idx_host, bag, samples):
     return sub_tables, sub_idx
 
 
+def host_table(t):
+    """Host copy of a device table: float32, or uint16 bit patterns for bfloat16."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return host(t)
+
+
+def sampled_bags(tables_dev, idx_host, samples, bag=None, offsets_host=None,
+                 weights_host=None):
+    """Cut the bags of `samples` out of a full-size problem, CSR or uniform.
+
+    Returns host (tables, indices, offsets, weights) of a problem with one
+    sample per entry of `samples`, whose pooled bags equal the full
+    problem's: each table keeps only the rows its sampled bags touch (copied
+    from the device in its storage type), indices are renumbered into it and
+    the sampled bags are laid out back to back with CSR offsets.  weights is
+    None when weights_host is None.
+    """
+    import torch
+    sub_tables, sub_idx, sub_offs, sub_w = [], [], [], []
+    for k, (t_dev, idx) in enumerate(zip(tables_dev, idx_host)):
+        n = idx.shape[0]
+        if offsets_host is None:
+            bounds = [(s * bag, (s + 1) * bag) for s in samples]
+        else:
+            o = offsets_host[k]
+            bounds = [(int(o[s]), int(o[s + 1]) if s + 1 < len(o) else n) for s in samples]
+        picks = np.concatenate([np.arange(a, b) for a, b in bounds]).astype(np.int64)
+        lens = np.array([b - a for a, b in bounds], np.int64)
+        bags = idx[picks]
+        rows = np.unique(bags) if bags.size else np.zeros(1, np.int64)
+        sub = t_dev.index_select(0, torch.from_numpy(rows.astype(np.int64)).to(t_dev.device))
+        sub_tables.append(host_table(sub))
+        sub_idx.append(np.searchsorted(rows, bags).astype(np.int32))
+        sub_offs.append(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32))
+        if weights_host is not None:
+            sub_w.append(weights_host[k][picks])
+    return sub_tables, sub_idx, sub_offs, (sub_w if weights_host is not None else None)
+
+
 def sample_rows(B, count, seed=0):
     """Sorted sample ids: first, last and a seeded spread in between."""
     rng = np.random.default_rng(seed)

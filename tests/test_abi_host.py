@@ -99,6 +99,47 @@ def test_emb_interact_argument_errors(lib):
     assert f(64, 4, 1024, t64, r64, i64, None, _n(64, 8), FAKE, FAKE, None, None) == 3
 
 
+def _bags(K=2, B=4, D=8, dtype=0, pool=0, n=8, weights=False, offsets=False):
+    t, r, i = _tables(K)
+    keep = [t, r, i, _n(K, n)]
+    w = (ctypes.c_void_p * K)(*[FAKE] * K) if weights else None
+    o = (ctypes.c_void_p * K)(*[FAKE] * K) if offsets else None
+    keep += [w, o]
+    g = abi.Bags(K, B, D, dtype, pool, ctypes.cast(t, ctypes.POINTER(ctypes.c_void_p)), r,
+                 ctypes.cast(i, ctypes.POINTER(ctypes.c_void_p)),
+                 ctypes.cast(o, ctypes.POINTER(ctypes.c_void_p)) if o else None, keep[3],
+                 ctypes.cast(w, ctypes.POINTER(ctypes.c_void_p)) if w else None)
+    g._keep = keep
+    return g
+
+
+def test_emb_bag_pool_argument_errors(lib):
+    f = lib.emb_bag_pool
+    ok = _bags()
+    assert f(None, FAKE, None) == 1                                     # bags NULL
+    assert f(ctypes.byref(_bags(dtype=2)), FAKE, None) == 2             # unknown dtype
+    assert f(ctypes.byref(_bags(pool=2)), FAKE, None) == 2              # unknown pool
+    assert f(ctypes.byref(_bags(pool=1, weights=True)), FAKE, None) == 3  # mean + weights
+    assert f(ctypes.byref(_bags(n=7)), FAKE, None) == 2                 # n_idx % B
+    assert f(ctypes.byref(_bags(K=0)), FAKE, None) == 2                 # K < 1
+    assert f(ctypes.byref(ok), None, None) == 1                         # out NULL
+    g = _bags(weights=True)
+    g.weights[1] = None
+    assert f(ctypes.byref(g), FAKE, None) == 1                          # weights[1] NULL
+    g = _bags(offsets=True, n=7)
+    g.offsets[0] = None
+    assert f(ctypes.byref(g), FAKE, None) == 1                          # offsets[0] NULL
+    assert f(ctypes.byref(_bags(B=0, n=0, dtype=1, pool=1)), None, None) == 0  # B == 0
+    fi = lib.dlrm_emb_interact_pool
+    assert fi(None, FAKE, FAKE, None, None) == 1
+    assert fi(ctypes.byref(ok), None, FAKE, None, None) == 1            # dense NULL
+    assert fi(ctypes.byref(ok), FAKE, None, None, None) == 1            # out NULL
+    assert fi(ctypes.byref(_bags(pool=1, weights=True)), FAKE, FAKE, None, None) == 3
+    big = _bags(K=64, D=1024, dtype=1)
+    assert fi(ctypes.byref(big), FAKE, FAKE, None, None) == 3           # tile beyond LDS
+    assert fi(ctypes.byref(_bags(B=0, n=0)), None, None, None, None) == 0
+
+
 def test_linear_argument_errors(lib):
     f = lib.linear_bias_act
     assert f(4, 0, 3, FAKE, 3, FAKE, None, 0, FAKE, 1, None) == 2     # n < 1
