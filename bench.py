@@ -24,12 +24,15 @@ Prints ONE JSON line on stdout (progress goes to stderr):
 
 The JSON line also carries `variants`: the same fused launch with bfloat16
 tables, mean pooling, per-sample weights and CSR bags of size 0..40
-(dlrm_emb_interact_pool), and `forward`: the full DLRMv1 forward at B=8192
+(dlrm_emb_interact_pool), `cells`: the pages' small DLRMv1 cells (nc x
+batch) per call, eager dlrm_forward against a graph-replayed plan, and
+`forward`: the full DLRMv1 forward at B=8192
 (dlrm_forward), with each MLP layer timed alone against the f32 MFMA peak
 (or HBM for the layers below the ridge point).
 
 Options: --workload {nc32,nc32-uniform,mid,tiny,large} (or one variant,
 nc32-bf16 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-variants,
+--no-cells,
 --sweep (batch x
 num_tables grid instead of the default line), --warm, --no-cpu-baseline,
 --no-forward, --profile-run (timed cold steps only, for profilers),
@@ -404,6 +407,12 @@ def bench_forward(args, stream, flush):
     cold = not args.warm
     t_fwd = _event_time(fwd, stream, args.steps, args.warmup, cold, flush)
     log(f"forward: {t_fwd * 1000:.1f} us ({'cold' if cold else 'warm'})")
+    plan = abi.DlrmPlan(model, dense_in, idx, out=torch.empty((B, 1), device="cuda"),
+                        workspace=torch.empty_like(ws))
+    t_plan = _event_time(lambda: plan.run(stream), stream, args.steps, args.warmup, cold, flush)
+    plan_same = bool(torch.equal(plan.out, out))
+    plan.close()
+    log(f"forward as a plan (graph replay): {t_plan * 1000:.1f} us, same output: {plan_same}")
     # each layer alone (warm: weights and activations are on-chip-sized)
     layers = []
     acts = {}
@@ -464,11 +473,87 @@ def bench_forward(args, stream, flush):
     log(f"  emb+interact {t_emb * 1000:.1f} us, {emb_bytes / (t_emb * 1e-3) / 1e9:.0f} GB/s")
     return {"workload": f"dlrm: {w.description}", "batch": B, "cache": "cold" if cold else "warm",
             "us_per_forward": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
+            "plan_us_per_forward": t_plan * 1e3, "plan_equals_eager": plan_same,
             "emb_interact_us": t_emb * 1e3,
             "emb_interact_algorithmic_gbps": emb_bytes / (t_emb * 1e-3) / 1e9,
             "mlp_chains": chains, "mlp_layers": layers, "mlp_us_sum": mlp_us,
             "mlp_tflops": mlp_flops / (mlp_us * 1e-6) / 1e12,
             "mlp_frac_of_f32_mfma_peak": mlp_flops / (mlp_us * 1e-6) / 1e12 / F32_MFMA_PEAK_TFLOPS}
+
+
+def bench_cells(args, stream):
+    """The pages' small DLRMv1 cells (3 dense, D=16, L=2, 4096-row tables,
+    MLPs 3-16 and (16+P)-16-1), nc x batch, warm: the whole forward per call
+    through dlrm_forward (7 launches, host validation each call) and through
+    a plan (one graph launch).  Each call is bracketed by events on the
+    stream without synchronizing in between, so a host-bound call shows its
+    host time; the pages' harness is mirrored (10 warmup, 5 rounds x 20
+    calls, median of round medians)."""
+    import torch
+    from dlrm_embedding_bag_amd import abi, inputs
+    lib = abi.load()
+    cells = []
+    for nc in (2, 4, 8, 16, 32):
+        for b in (2, 16, 64, 256, 1024, 2048):
+            w = inputs.cell_workload(nc, b)
+            tables = [torch.from_numpy(inputs.table_host(w, k, args.seed)).cuda()
+                      for k in range(nc)]
+            bottom, top = inputs.dlrm_layers(w, args.seed)
+            dv = lambda a: torch.from_numpy(a).cuda()
+            model = abi.DlrmModel([(dv(a), dv(x), act) for a, x, act in bottom],
+                                  [(dv(a), dv(x), act) for a, x, act in top], tables)
+            idx = [dv(inputs.indices(w, k, args.seed)) for k in range(nc)]
+            dense = dv(inputs.dense(w, args.seed))
+            out = torch.empty((b, 1), device="cuda")
+            ws = torch.empty(model.workspace_bytes(b), dtype=torch.uint8, device="cuda")
+            fargs = (ctypes.byref(model.struct), b, dense.data_ptr(), abi._ptr_array(idx), None,
+                     abi._i64_array([i.numel() for i in idx]), out.data_ptr(), ws.data_ptr(),
+                     ws.numel(), stream.cuda_stream)
+            plan = abi.DlrmPlan(model, dense, idx, out=torch.empty((b, 1), device="cuda"),
+                                workspace=torch.empty_like(ws))
+            handle, sptr = plan._handle, stream.cuda_stream
+
+            def eager():
+                lib.dlrm_forward(*fargs)
+
+            def replay():
+                lib.dlrm_plan_run(handle, sptr)
+            row = {"num_tables": nc, "batch": b}
+            for name, fn in (("eager", eager), ("plan", replay)):
+                row[f"{name}_us"] = _rounds_time(fn, stream) * 1e3
+            torch.cuda.synchronize()
+            same = bool(torch.equal(plan.out, out))
+            row["plan_equals_eager"] = same
+            cells.append(row)
+            log(f"cell nc={nc:2d} b={b:5d}: eager {row['eager_us']:6.1f} us, plan "
+                f"{row['plan_us']:6.1f} us (same output: {same})")
+            plan.close()
+            del model, tables, plan
+    return {"model": "pages' cell: 3 dense, D=16, L=2, 4096-row tables, MLPs 3-16 and "
+                     "(16+P)-16-1, uniform indices, warm",
+            "timing": "events around each call, no sync between calls; 10 warmup, 5 rounds x 20 "
+                      "calls, median of round medians",
+            "cells": cells}
+
+
+def _rounds_time(fn, stream, warmup=10, rounds=5, per_round=20):
+    """Median of round medians of event-bracketed calls (ms)."""
+    import torch
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        meds = []
+        for _ in range(rounds):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(per_round + 1)]
+            evs[0].record(stream)
+            for i in range(per_round):
+                fn()
+                evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            meds.append(statistics.median(evs[i].elapsed_time(evs[i + 1])
+                                          for i in range(per_round)))
+    return statistics.median(meds)
 
 
 VARIANTS = ("nc32-bf16", "nc32-mean", "nc32-weighted", "nc32-csr")
@@ -584,6 +669,8 @@ def main():
                     help="skip the full-forward section (B=8192 DLRMv1)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the bf16 / mean / weighted / CSR variant lines")
+    ap.add_argument("--no-cells", action="store_true",
+                    help="skip the pages' small-cell forward latency grid (eager vs plan)")
     ap.add_argument("--sweep", action="store_true", help="batch x num_tables sweep instead")
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--sweep-out", default="")
@@ -625,6 +712,8 @@ def main():
         flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
         if not args.no_variants:
             res["variants"] = bench_variants(args, stream, flush)
+        if not args.no_cells:
+            res["cells"] = bench_cells(args, stream)
         if not args.no_forward:
             res["forward"] = bench_forward(args, stream, flush)
     print(json.dumps(res), flush=True)

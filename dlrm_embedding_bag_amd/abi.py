@@ -27,7 +27,8 @@ POOLS = {"sum": 0, "mean": 1}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
            "dlrm_emb_interact_pool", "linear_bias_act", "mlp_forward",
-           "dlrm_forward_workspace_bytes", "dlrm_forward")
+           "dlrm_forward_workspace_bytes", "dlrm_forward", "dlrm_plan_create",
+           "dlrm_plan_update", "dlrm_plan_run", "dlrm_plan_destroy")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -100,6 +101,16 @@ def load(path: str = LIB_PATH):
     lib.dlrm_forward.restype = ctypes.c_int
     lib.dlrm_forward.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
                                  ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t, _vp]
+    lib.dlrm_plan_create.restype = ctypes.c_int
+    lib.dlrm_plan_create.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
+                                     ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t,
+                                     ctypes.POINTER(_vp)]
+    lib.dlrm_plan_update.restype = ctypes.c_int
+    lib.dlrm_plan_update.argtypes = [_vp, _vp, ptrs, ptrs, ctypes.POINTER(_i64), _vp]
+    lib.dlrm_plan_run.restype = ctypes.c_int
+    lib.dlrm_plan_run.argtypes = [_vp, _vp]
+    lib.dlrm_plan_destroy.restype = ctypes.c_int
+    lib.dlrm_plan_destroy.argtypes = [_vp]
     if path == LIB_PATH:
         _LIB = lib
     return lib
@@ -437,3 +448,70 @@ def dlrm_forward(model: DlrmModel, dense_in, indices, offsets=None, out=None, wo
                             workspace.numel() * workspace.element_size(), _stream(stream)),
            "dlrm_forward")
     return out
+
+
+class DlrmPlan:
+    """A dlrm_forward recorded into a HIP graph for fixed buffers
+    (dlrm_plan_create); run() replays it (dlrm_plan_run).  The caller writes
+    each batch into the bound dense_in / indices tensors and reads `out`."""
+
+    def __init__(self, model: DlrmModel, dense_in, indices, offsets=None, out=None,
+                 workspace=None):
+        torch = _torch()
+        self._lib = load()
+        self.model = model
+        self.dense_in = _dev(dense_in, torch.float32, "dense_in")
+        self.batch = dense_in.shape[0]
+        if out is None:
+            out = torch.empty((self.batch, model.out_features), dtype=torch.float32,
+                              device=dense_in.device)
+        self.out = _dev(out, torch.float32, "out")
+        need = model.workspace_bytes(self.batch)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dense_in.device)
+        self.workspace = workspace
+        self._handle = _vp()
+        self._bind(indices, offsets)
+        _check(self._lib.dlrm_plan_create(
+            ctypes.byref(model.struct), self.batch, self.dense_in.data_ptr(), self._ip,
+            self._op, self._nidx, self.out.data_ptr(), self.workspace.data_ptr(),
+            self.workspace.numel() * self.workspace.element_size(), ctypes.byref(self._handle)),
+            "dlrm_plan_create")
+
+    def _bind(self, indices, offsets):
+        torch = _torch()
+        self.indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
+        self.offsets = None
+        if offsets is not None:
+            self.offsets = [_dev(o, torch.int32, f"offsets[{k}]") for k, o in enumerate(offsets)]
+        self._ip = _ptr_array(self.indices)
+        self._op = _ptr_array(self.offsets) if self.offsets is not None else None
+        self._nidx = _i64_array([i.numel() for i in self.indices])
+
+    def update(self, dense_in=None, indices=None, offsets=None, out=None):
+        """Rebind the per-batch buffers (dlrm_plan_update)."""
+        torch = _torch()
+        if dense_in is not None:
+            self.dense_in = _dev(dense_in, torch.float32, "dense_in")
+        if out is not None:
+            self.out = _dev(out, torch.float32, "out")
+        if indices is not None:
+            self._bind(indices, offsets)
+        _check(self._lib.dlrm_plan_update(self._handle, self.dense_in.data_ptr(), self._ip,
+                                          self._op, self._nidx, self.out.data_ptr()),
+               "dlrm_plan_update")
+
+    def run(self, stream=None):
+        _check(self._lib.dlrm_plan_run(self._handle, _stream(stream)), "dlrm_plan_run")
+        return self.out
+
+    def close(self):
+        if self._handle:
+            _check(self._lib.dlrm_plan_destroy(self._handle), "dlrm_plan_destroy")
+            self._handle = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -5,6 +5,9 @@
 #include <limits.h>
 #include <string.h>
 
+#include <new>
+#include <vector>
+
 #include "../../include/dlrm_embedding_bag.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -160,6 +163,127 @@ int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
   return DLRM_OK;
 }
 
+// Checks every argument of a forward (nothing is enqueued).
+int validate_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
+                     const int32_t *const *indices, const int32_t *const *offsets,
+                     const int64_t *n_idx, const float *out, const void *workspace,
+                     size_t workspace_bytes) {
+  ForwardLayout lay;
+  int rc = plan_forward(model, batch, lay);
+  if (rc) return rc;
+  TableSet ts;
+  GatherConfig gc;
+  const dlrm_bags g = f32_sum_bags(model->num_tables, batch, model->dim, model->tables,
+                                   model->rows, indices, offsets, n_idx);
+  rc = pack_bags(g, ts, gc);
+  if (rc) return rc;
+  if (batch == 0) return DLRM_OK;
+  if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
+  if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return DLRM_ERR_WORKSPACE;
+  return DLRM_OK;
+}
+
+int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
+                    const int32_t *const *indices, const int32_t *const *offsets,
+                    const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
+                    hipStream_t st) {
+  ForwardLayout lay;
+  int rc = plan_forward(model, batch, lay);
+  if (rc) return rc;
+  TableSet ts;
+  GatherConfig gc;
+  const dlrm_bags g = f32_sum_bags(model->num_tables, batch, model->dim, model->tables,
+                                   model->rows, indices, offsets, n_idx);
+  rc = pack_bags(g, ts, gc);
+  if (rc) return rc;
+  if (batch == 0) return DLRM_OK;  // nothing to read or write
+  if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
+  if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return DLRM_ERR_WORKSPACE;
+  const int B = batch, D = model->dim, K = model->num_tables;
+  char *ws = static_cast<char *>(workspace);
+  float *R = reinterpret_cast<float *>(ws + lay.off_R);
+  float *buf[2] = {reinterpret_cast<float *>(ws + lay.off_buf0),
+                   reinterpret_cast<float *>(ws + lay.off_buf1)};
+
+  // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
+  const float *x = dense_in;
+  int64_t ldx = model->bottom[0].in_features;
+  ChainParams cp;
+  if (lay.bottom_chain &&
+      pack_chain(B, model->num_bottom, model->bottom, dense_in, ldx, R, lay.ldR, cp)) {
+    rc = hip_status(launch_mlp_chain(cp, st));
+    if (rc) return rc;
+  } else {
+  for (int l = 0; l < model->num_bottom; ++l) {
+    const dlrm_layer &L = model->bottom[l];
+    const bool last = l + 1 == model->num_bottom;
+    float *y = last ? R : buf[l & 1];
+    const int64_t ldy = last ? lay.ldR : lay.ld_buf;
+    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
+                                  L.act, y, ldy, st));
+    if (rc) return rc;
+    x = y;
+    ldx = ldy;
+  }
+  }
+
+  // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
+  gc.vec = gc.vec && lay.ldR % 4 == 0;
+  InteractParams ip{};
+  int threads = 0;
+  if (!plan_interact(B, K, D, gc.vec, chunk_elems(gc), ip, threads)) return DLRM_ERR_UNSUPPORTED;
+  ip.copy_dense = 0;
+  ip.dense = R;
+  ip.ld_dense = lay.ldR;
+  ip.out = R;
+  ip.ld_out = lay.ldR;
+  ip.out_vec = 1;
+  ip.emb_out = nullptr;
+  ip.emb_in = nullptr;
+  rc = hip_status(launch_interact(&ts, gc, ip, threads, st));
+  if (rc) return rc;
+
+  // Top MLP on cat(dense, dots) = R.
+  x = R;
+  ldx = lay.ldR;
+  const int32_t out_w = model->top[model->num_top - 1].out_features;
+  if (lay.top_chain && pack_chain(B, model->num_top, model->top, R, lay.ldR, out, out_w, cp))
+    return hip_status(launch_mlp_chain(cp, st));
+  for (int l = 0; l < model->num_top; ++l) {
+    const dlrm_layer &L = model->top[l];
+    const bool last = l + 1 == model->num_top;
+    float *y = last ? out : buf[l & 1];
+    const int64_t ldy = last ? L.out_features : lay.ld_buf;
+    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
+                                  L.act, y, ldy, st));
+    if (rc) return rc;
+    x = y;
+    ldx = ldy;
+  }
+  return DLRM_OK;
+}
+
+// Records the forward's launches on `st` (a capturing stream) into a graph.
+int capture_forward(const dlrm_model &model, int32_t batch, const float *dense_in,
+                    const int32_t *const *indices, const int32_t *const *offsets,
+                    const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
+                    hipStream_t st, hipGraph_t *graph) {
+  *graph = nullptr;
+  if (hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed) != hipSuccess) return DLRM_ERR_HIP;
+  const int rc = enqueue_forward(&model, batch, dense_in, indices, offsets, n_idx, out, workspace,
+                                 workspace_bytes, st);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(st, &g);
+  if (rc || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc ? rc : DLRM_ERR_HIP;
+  }
+  *graph = g;
+  return DLRM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -297,82 +421,113 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  const int32_t *const *indices, const int32_t *const *offsets,
                  const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
                  void *stream) {
-  ForwardLayout lay;
-  int rc = plan_forward(model, batch, lay);
-  if (rc) return rc;
-  TableSet ts;
-  GatherConfig gc;
-  const dlrm_bags g = f32_sum_bags(model->num_tables, batch, model->dim, model->tables,
-                                   model->rows, indices, offsets, n_idx);
-  rc = pack_bags(g, ts, gc);
-  if (rc) return rc;
-  if (batch == 0) return DLRM_OK;  // nothing to read or write
-  if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
-  if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return DLRM_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  const int B = batch, D = model->dim, K = model->num_tables;
-  char *ws = static_cast<char *>(workspace);
-  float *R = reinterpret_cast<float *>(ws + lay.off_R);
-  float *buf[2] = {reinterpret_cast<float *>(ws + lay.off_buf0),
-                   reinterpret_cast<float *>(ws + lay.off_buf1)};
+  return enqueue_forward(model, batch, dense_in, indices, offsets, n_idx, out, workspace,
+                         workspace_bytes, (hipStream_t)stream);
+}
 
-  // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
-  const float *x = dense_in;
-  int64_t ldx = model->bottom[0].in_features;
-  ChainParams cp;
-  if (lay.bottom_chain &&
-      pack_chain(B, model->num_bottom, model->bottom, dense_in, ldx, R, lay.ldR, cp)) {
-    rc = hip_status(launch_mlp_chain(cp, st));
-    if (rc) return rc;
-  } else {
-  for (int l = 0; l < model->num_bottom; ++l) {
-    const dlrm_layer &L = model->bottom[l];
-    const bool last = l + 1 == model->num_bottom;
-    float *y = last ? R : buf[l & 1];
-    const int64_t ldy = last ? lay.ldR : lay.ld_buf;
-    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
-                                  L.act, y, ldy, st));
-    if (rc) return rc;
-    x = y;
-    ldx = ldy;
-  }
-  }
+// ---------------------------------------------------------------------------
+// Plans: the forward captured once into a HIP graph, replayed per call.
+// ---------------------------------------------------------------------------
+struct dlrm_plan {
+  // The model, copied so that a plan does not depend on the caller's host
+  // arrays after creation (the layers and tables it points to stay the
+  // caller's device memory).
+  std::vector<dlrm_layer> bottom, top;
+  std::vector<const float *> tables;
+  std::vector<int64_t> rows;
+  dlrm_model model;
+  int32_t batch = 0;
+  void *workspace = nullptr;
+  size_t workspace_bytes = 0;
+  hipStream_t capture = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
 
-  // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
-  gc.vec = gc.vec && lay.ldR % 4 == 0;
-  InteractParams ip{};
-  int threads = 0;
-  if (!plan_interact(B, K, D, gc.vec, chunk_elems(gc), ip, threads)) return DLRM_ERR_UNSUPPORTED;
-  ip.copy_dense = 0;
-  ip.dense = R;
-  ip.ld_dense = lay.ldR;
-  ip.out = R;
-  ip.ld_out = lay.ldR;
-  ip.out_vec = 1;
-  ip.emb_out = nullptr;
-  ip.emb_in = nullptr;
-  rc = hip_status(launch_interact(&ts, gc, ip, threads, st));
+int dlrm_plan_create(const dlrm_model *model, int32_t batch, const float *dense_in,
+                     const int32_t *const *indices, const int32_t *const *offsets,
+                     const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
+                     dlrm_plan **plan_out) {
+  if (!plan_out) return DLRM_ERR_NULL;
+  *plan_out = nullptr;
+  int rc = validate_forward(model, batch, dense_in, indices, offsets, n_idx, out, workspace,
+                            workspace_bytes);
   if (rc) return rc;
-
-  // Top MLP on cat(dense, dots) = R.
-  x = R;
-  ldx = lay.ldR;
-  const int32_t out_w = model->top[model->num_top - 1].out_features;
-  if (lay.top_chain && pack_chain(B, model->num_top, model->top, R, lay.ldR, out, out_w, cp))
-    return hip_status(launch_mlp_chain(cp, st));
-  for (int l = 0; l < model->num_top; ++l) {
-    const dlrm_layer &L = model->top[l];
-    const bool last = l + 1 == model->num_top;
-    float *y = last ? out : buf[l & 1];
-    const int64_t ldy = last ? L.out_features : lay.ld_buf;
-    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
-                                  L.act, y, ldy, st));
-    if (rc) return rc;
-    x = y;
-    ldx = ldy;
+  if (batch < 1) return DLRM_ERR_SHAPE;  // a plan of nothing is not useful
+  dlrm_plan *p = new (std::nothrow) dlrm_plan;
+  if (!p) return DLRM_ERR_UNSUPPORTED;
+  p->bottom.assign(model->bottom, model->bottom + model->num_bottom);
+  p->top.assign(model->top, model->top + model->num_top);
+  p->tables.assign(model->tables, model->tables + model->num_tables);
+  p->rows.assign(model->rows, model->rows + model->num_tables);
+  p->model = *model;
+  p->model.bottom = p->bottom.data();
+  p->model.top = p->top.data();
+  p->model.tables = p->tables.data();
+  p->model.rows = p->rows.data();
+  p->batch = batch;
+  p->workspace = workspace;
+  p->workspace_bytes = workspace_bytes;
+  if (hipStreamCreateWithFlags(&p->capture, hipStreamNonBlocking) != hipSuccess) {
+    delete p;
+    return DLRM_ERR_HIP;
   }
+  rc = capture_forward(p->model, batch, dense_in, indices, offsets, n_idx, out, workspace,
+                       workspace_bytes, p->capture, &p->graph);
+  if (rc == DLRM_OK &&
+      hipGraphInstantiate(&p->exec, p->graph, nullptr, nullptr, 0) != hipSuccess)
+    rc = DLRM_ERR_HIP;
+  if (rc) {
+    dlrm_plan_destroy(p);
+    return rc;
+  }
+  *plan_out = p;
   return DLRM_OK;
+}
+
+int dlrm_plan_update(dlrm_plan *plan, const float *dense_in, const int32_t *const *indices,
+                     const int32_t *const *offsets, const int64_t *n_idx, float *out) {
+  if (!plan) return DLRM_ERR_NULL;
+  int rc = validate_forward(&plan->model, plan->batch, dense_in, indices, offsets, n_idx, out,
+                            plan->workspace, plan->workspace_bytes);
+  if (rc) return rc;
+  hipGraph_t g = nullptr;
+  rc = capture_forward(plan->model, plan->batch, dense_in, indices, offsets, n_idx, out,
+                       plan->workspace, plan->workspace_bytes, plan->capture, &g);
+  if (rc) return rc;
+  hipGraphNode_t err_node = nullptr;
+  hipGraphExecUpdateResult res = hipGraphExecUpdateError;
+  if (hipGraphExecUpdate(plan->exec, g, &err_node, &res) != hipSuccess ||
+      res != hipGraphExecUpdateSuccess) {
+    // The launch shapes changed (e.g. other offsets switch the gather's
+    // kernel): instantiate the new graph instead.
+    (void)hipGetLastError();
+    hipGraphExec_t fresh = nullptr;
+    if (hipGraphInstantiate(&fresh, g, nullptr, nullptr, 0) != hipSuccess) {
+      (void)hipGraphDestroy(g);
+      return DLRM_ERR_HIP;
+    }
+    (void)hipGraphExecDestroy(plan->exec);
+    plan->exec = fresh;
+  }
+  (void)hipGraphDestroy(plan->graph);
+  plan->graph = g;
+  return DLRM_OK;
+}
+
+int dlrm_plan_run(dlrm_plan *plan, void *stream) {
+  if (!plan) return DLRM_ERR_NULL;
+  return hip_status(hipGraphLaunch(plan->exec, (hipStream_t)stream));
+}
+
+int dlrm_plan_destroy(dlrm_plan *plan) {
+  if (!plan) return DLRM_OK;
+  int rc = DLRM_OK;
+  if (plan->exec && hipGraphExecDestroy(plan->exec) != hipSuccess) rc = DLRM_ERR_HIP;
+  if (plan->graph && hipGraphDestroy(plan->graph) != hipSuccess) rc = DLRM_ERR_HIP;
+  if (plan->capture && hipStreamDestroy(plan->capture) != hipSuccess) rc = DLRM_ERR_HIP;
+  delete plan;
+  return rc;
 }
 
 }  // extern "C"

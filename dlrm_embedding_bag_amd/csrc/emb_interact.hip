@@ -50,8 +50,14 @@ namespace {
 #define DLRM_MIN_THREADS 256
 #endif
 
-constexpr int kUnroll = 8;                  // generic path: loads in flight per lane
-constexpr int kRound = DLRM_GATHER_ROUND;   // shuffle path: row loads in flight per lane
+#ifndef DLRM_GATHER_ROUND_BF16
+#define DLRM_GATHER_ROUND_BF16 12
+#endif
+
+constexpr int kUnroll = 8;  // generic path: loads in flight per lane
+// Shuffle path: row loads in flight per lane, by table storage type.
+template <typename TT>
+constexpr int kRound = sizeof(TT) == 2 ? DLRM_GATHER_ROUND_BF16 : DLRM_GATHER_ROUND;
 
 __device__ __forceinline__ void store_unaligned(float *p, float4 v) {
   p[0] = v.x;
@@ -235,12 +241,13 @@ __device__ __forceinline__ void pool_group(const TT *__restrict__ tab,
                                            int c_lane, int c, int gbase, float *acc) {
   using RC = RowChunk<TT, 4>;
   using Raw = typename RC::Raw;
-  constexpr int T = (kRound + G - 1) / G;  // index registers per lane
+  constexpr int R = kRound<TT>;
+  constexpr int T = (R + G - 1) / G;  // index registers per lane
   const Raw *col = reinterpret_cast<const Raw *>(tab) + c;
 #pragma unroll
   for (int i = 0; i < RC::EL; ++i) acc[i] = 0.f;
-  for (int l0 = s; l0 < e; l0 += kRound) {
-    const int n = min(kRound, e - l0);
+  for (int l0 = s; l0 < e; l0 += R) {
+    const int n = min(R, e - l0);
     int mine[T];
     float mine_w[T];
 #pragma unroll
@@ -249,10 +256,10 @@ __device__ __forceinline__ void pool_group(const TT *__restrict__ tab,
       mine[t] = (l < n) ? idx[l0 + l] : 0;
       mine_w[t] = (PSW && l < n) ? wt[l0 + l] : 0.f;
     }
-    Raw v[kRound];
-    float w[kRound];
+    Raw v[R];
+    float w[R];
 #pragma unroll
-    for (int u = 0; u < kRound; ++u) {
+    for (int u = 0; u < R; ++u) {
       const int src = (gbase + (u % G)) << 2;
       const int r = __builtin_amdgcn_ds_bpermute(src, mine[u / G]);
       w[u] = PSW ? __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(mine_w[u / G])))
@@ -269,7 +276,7 @@ __device__ __forceinline__ void pool_group(const TT *__restrict__ tab,
 #endif
     }
 #pragma unroll
-    for (int u = 0; u < kRound; ++u)
+    for (int u = 0; u < R; ++u)
       if (u < n) accumulate<RC, PSW>(acc, w[u], v[u]);
   }
 }

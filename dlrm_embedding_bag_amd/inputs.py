@@ -123,6 +123,17 @@ WORKLOADS = {
 }
 
 
+def cell_workload(num_tables: int, batch: int) -> Workload:
+    """The pages' small DLRMv1 cell: 3 dense features, D=16, 2 indices per bag
+    uniform over 4096-row tables; bottom MLP 3-16 and top MLP (16+P)-16-1
+    (the pages do not print the MLP widths)."""
+    return Workload(f"cell-nc{num_tables}-b{batch}", batch=batch, num_tables=num_tables,
+                    rows=4096, dim=16, bag=2, dist="uniform", dense_in=3, bottom=(16,),
+                    top=(16, 1),
+                    description=f"pages' cell: nc={num_tables}, b={batch}, 3 dense, D=16, "
+                                f"L=2, 4096 rows, MLPs 3-16 and (16+P)-16-1")
+
+
 def _rng(seed: int, stream: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([int(seed), int(stream)]))
 

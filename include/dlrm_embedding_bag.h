@@ -306,6 +306,50 @@ DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *d
                  const int64_t *n_idx, float *out, void *workspace,
                  size_t workspace_bytes, void *stream);
 
+/*
+ * Plans -- the forward recorded once into a HIP graph and replayed
+ * ([FASTPATHS] runtime.rs and the commit message: the runtime captures the
+ * whole graph and replays it on every execute, and the per-iteration host
+ * overhead of re-registering input pointers dominated small cells until
+ * pointers were cached).  A plan binds one model, one batch size and one
+ * set of caller buffers; the caller writes each new batch into those same
+ * buffers and calls dlrm_plan_run.
+ *
+ * dlrm_plan_create -- validates exactly as dlrm_forward does (same argument
+ *   meanings; batch >= 1), then records the forward's launches into a graph
+ *   on a private stream and instantiates it.  The model's host arrays are
+ *   copied into the plan; every device pointer (weights, tables, dense_in,
+ *   indices, offsets, out, workspace) must stay valid while the plan lives.
+ *   Allocates host memory and HIP graph objects, no device buffers.
+ *   On success *plan receives the plan; on error it is set to NULL.
+ *
+ * dlrm_plan_update -- rebinds the per-batch buffers (dense_in, indices,
+ *   offsets, n_idx, out) of a plan, same model, batch and workspace: the
+ *   forward is recorded again and the executable graph updated in place
+ *   (re-instantiated if the launch shapes changed).  Must not race a run of
+ *   the same plan.
+ *
+ * dlrm_plan_run -- enqueues one forward on `stream` (one graph launch); no
+ *   host work besides the launch and no synchronization.  Runs of one plan
+ *   share its workspace and output, so runs on different streams must be
+ *   ordered by the caller.
+ *
+ * dlrm_plan_destroy -- releases the plan (NULL is a no-op).  Pending runs on
+ *   a stream complete normally; the caller must not destroy a plan that a
+ *   graph still being recorded refers to.
+ */
+typedef struct dlrm_plan dlrm_plan;
+
+DLRM_API int dlrm_plan_create(const dlrm_model *model, int32_t batch, const float *dense_in,
+                              const int32_t *const *indices, const int32_t *const *offsets,
+                              const int64_t *n_idx, float *out, void *workspace,
+                              size_t workspace_bytes, dlrm_plan **plan);
+DLRM_API int dlrm_plan_update(dlrm_plan *plan, const float *dense_in,
+                              const int32_t *const *indices, const int32_t *const *offsets,
+                              const int64_t *n_idx, float *out);
+DLRM_API int dlrm_plan_run(dlrm_plan *plan, void *stream);
+DLRM_API int dlrm_plan_destroy(dlrm_plan *plan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -194,8 +194,8 @@ def test_forward_workspace_and_errors(lib):
                   [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D)
     B = 8192
     ws = lib.dlrm_forward_workspace_bytes(ctypes.byref(good), B)
-    # the bottom MLP (first layer 13 wide) runs as one fused chain, the top one
-    # layer by layer: R (B x 416 floats) + two ping-pong buffers (B x 512)
+    # both MLPs run layer by layer: R (B x 416 floats) + two ping-pong
+    # buffers as wide as the widest hidden layer (B x 512)
     assert ws == B * 416 * 4 + 2 * B * 512 * 4
     odd = _model([(13, 96, 1), (96, 64, 1)], [(D + P, 96, 1), (96, 1, 2)], K, D)
     # widths the chain kernel does not take: R + two ping-pong buffers (B x 96)
@@ -216,6 +216,35 @@ def test_forward_workspace_and_errors(lib):
     assert f(ctypes.byref(good), B, None, idx, None, n, FAKE, FAKE, ws, None) == 1
     assert f(None, B, FAKE, idx, None, n, FAKE, FAKE, ws, None) == 1
     assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, FAKE, ws, None) == 0
+
+
+def test_plan_argument_errors(lib):
+    """dlrm_plan_create validates like dlrm_forward before touching HIP."""
+    K, D = 26, 64
+    P = 27 * 26 // 2
+    good = _model([(13, 512, 1), (512, 256, 1), (256, 64, 1)],
+                  [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D)
+    bad_dim = _model([(13, 32, 1)], [(D + P, 1, 2)], K, D)
+    B = 64
+    ws = lib.dlrm_forward_workspace_bytes(ctypes.byref(good), B)
+    idx = (ctypes.c_void_p * K)(*[FAKE] * K)
+    n = _n(K, B * 20)
+    f = lib.dlrm_plan_create
+    h = ctypes.c_void_p(FAKE)
+    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws, None) == 1
+    assert f(ctypes.byref(bad_dim), B, FAKE, idx, None, n, FAKE, FAKE, ws,
+             ctypes.byref(h)) == 2
+    assert h.value is None, "a failed create leaves NULL in *plan"
+    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws - 1,
+             ctypes.byref(h)) == 4
+    assert f(ctypes.byref(good), B, None, idx, None, n, FAKE, FAKE, ws, ctypes.byref(h)) == 1
+    assert f(ctypes.byref(good), B, FAKE, idx, None, _n(K, B * 20 + 1), FAKE, FAKE, ws,
+             ctypes.byref(h)) == 2
+    assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, FAKE, ws,
+             ctypes.byref(h)) == 2                                      # batch 0: no plan
+    assert lib.dlrm_plan_run(None, None) == 1
+    assert lib.dlrm_plan_update(None, FAKE, idx, None, n, FAKE) == 1
+    assert lib.dlrm_plan_destroy(None) == 0
 
 
 def test_binding_refuses_cpu_tensors(lib):
