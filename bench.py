@@ -408,11 +408,11 @@ def bench_forward(args, stream, flush):
     t_fwd = _event_time(fwd, stream, args.steps, args.warmup, cold, flush)
     log(f"forward: {t_fwd * 1000:.1f} us ({'cold' if cold else 'warm'})")
     plan = abi.DlrmPlan(model, dense_in, idx, out=torch.empty((B, 1), device="cuda"),
-                        workspace=torch.empty_like(ws))
+                        workspace=torch.empty_like(ws), mode="graph")
     t_plan = _event_time(lambda: plan.run(stream), stream, args.steps, args.warmup, cold, flush)
     plan_same = bool(torch.equal(plan.out, out))
     plan.close()
-    log(f"forward as a plan (graph replay): {t_plan * 1000:.1f} us, same output: {plan_same}")
+    log(f"forward as a graph-mode plan: {t_plan * 1000:.1f} us, same output: {plan_same}")
     # each layer alone (warm: weights and activations are on-chip-sized)
     layers = []
     acts = {}
@@ -473,7 +473,7 @@ def bench_forward(args, stream, flush):
     log(f"  emb+interact {t_emb * 1000:.1f} us, {emb_bytes / (t_emb * 1e-3) / 1e9:.0f} GB/s")
     return {"workload": f"dlrm: {w.description}", "batch": B, "cache": "cold" if cold else "warm",
             "us_per_forward": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
-            "plan_us_per_forward": t_plan * 1e3, "plan_equals_eager": plan_same,
+            "graph_plan_us_per_forward": t_plan * 1e3, "plan_equals_eager": plan_same,
             "emb_interact_us": t_emb * 1e3,
             "emb_interact_algorithmic_gbps": emb_bytes / (t_emb * 1e-3) / 1e9,
             "mlp_chains": chains, "mlp_layers": layers, "mlp_us_sum": mlp_us,
@@ -484,8 +484,8 @@ def bench_forward(args, stream, flush):
 def bench_cells(args, stream):
     """The pages' small DLRMv1 cells (3 dense, D=16, L=2, 4096-row tables,
     MLPs 3-16 and (16+P)-16-1), nc x batch, warm: the whole forward per call
-    through dlrm_forward (7 launches, host validation each call) and through
-    a plan (one graph launch).  Each call is bracketed by events on the
+    through dlrm_forward (validation and packing each call, then the launch)
+    and through plans (direct: the recorded launch; graph: a graph launch).  Each call is bracketed by events on the
     stream without synchronizing in between, so a host-bound call shows its
     host time; the pages' harness is mirrored (10 warmup, 5 rounds x 20
     calls, median of round medians)."""
@@ -509,31 +509,49 @@ def bench_cells(args, stream):
             fargs = (ctypes.byref(model.struct), b, dense.data_ptr(), abi._ptr_array(idx), None,
                      abi._i64_array([i.numel() for i in idx]), out.data_ptr(), ws.data_ptr(),
                      ws.numel(), stream.cuda_stream)
-            plan = abi.DlrmPlan(model, dense, idx, out=torch.empty((b, 1), device="cuda"),
-                                workspace=torch.empty_like(ws))
-            handle, sptr = plan._handle, stream.cuda_stream
+            plans = {m: abi.DlrmPlan(model, dense, idx, out=torch.empty((b, 1), device="cuda"),
+                                     workspace=torch.empty_like(ws), mode=m)
+                     for m in ("direct", "graph")}
+            sptr = stream.cuda_stream
 
             def eager():
                 lib.dlrm_forward(*fargs)
-
-            def replay():
-                lib.dlrm_plan_run(handle, sptr)
+            fns = {"eager": eager}
+            for m, pl in plans.items():
+                fns[f"plan_{m}"] = (lambda h=pl._handle: lib.dlrm_plan_run(h, sptr))
             row = {"num_tables": nc, "batch": b}
-            for name, fn in (("eager", eager), ("plan", replay)):
+            for name, fn in fns.items():
                 row[f"{name}_us"] = _rounds_time(fn, stream) * 1e3
+                row[f"{name}_host_us"] = _host_time(fn) * 1e3
             torch.cuda.synchronize()
-            same = bool(torch.equal(plan.out, out))
-            row["plan_equals_eager"] = same
+            row["plans_equal_eager"] = all(bool(torch.equal(pl.out, out)) for pl in plans.values())
             cells.append(row)
-            log(f"cell nc={nc:2d} b={b:5d}: eager {row['eager_us']:6.1f} us, plan "
-                f"{row['plan_us']:6.1f} us (same output: {same})")
-            plan.close()
-            del model, tables, plan
+            log(f"cell nc={nc:2d} b={b:5d}: eager {row['eager_us']:6.1f} us "
+                f"(host {row['eager_host_us']:4.1f}), plan direct {row['plan_direct_us']:6.1f} us "
+                f"(host {row['plan_direct_host_us']:4.1f}), plan graph {row['plan_graph_us']:6.1f} "
+                f"us (host {row['plan_graph_host_us']:4.1f}); same output: "
+                f"{row['plans_equal_eager']}")
+            for pl in plans.values():
+                pl.close()
+            del model, tables, plans
     return {"model": "pages' cell: 3 dense, D=16, L=2, 4096-row tables, MLPs 3-16 and "
                      "(16+P)-16-1, uniform indices, warm",
             "timing": "events around each call, no sync between calls; 10 warmup, 5 rounds x 20 "
                       "calls, median of round medians",
             "cells": cells}
+
+
+def _host_time(fn, calls=200):
+    """Host time per call (ms): back-to-back calls without waiting for the
+    GPU, the final synchronization excluded."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    t = (time.perf_counter() - t0) / calls
+    torch.cuda.synchronize()
+    return t * 1e3
 
 
 def _rounds_time(fn, stream, warmup=10, rounds=5, per_round=20):

@@ -24,6 +24,7 @@ MAX_TABLES = 64
 MAX_DIM = 1024
 DTYPES = {"f32": 0, "bf16": 1}
 POOLS = {"sum": 0, "mean": 1}
+PLAN_MODES = {"direct": 0, "graph": 1}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
            "dlrm_emb_interact_pool", "linear_bias_act", "mlp_forward",
@@ -103,7 +104,7 @@ def load(path: str = LIB_PATH):
                                  ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t, _vp]
     lib.dlrm_plan_create.restype = ctypes.c_int
     lib.dlrm_plan_create.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
-                                     ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t,
+                                     ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t, _i32,
                                      ctypes.POINTER(_vp)]
     lib.dlrm_plan_update.restype = ctypes.c_int
     lib.dlrm_plan_update.argtypes = [_vp, _vp, ptrs, ptrs, ctypes.POINTER(_i64), _vp]
@@ -451,12 +452,13 @@ def dlrm_forward(model: DlrmModel, dense_in, indices, offsets=None, out=None, wo
 
 
 class DlrmPlan:
-    """A dlrm_forward recorded into a HIP graph for fixed buffers
-    (dlrm_plan_create); run() replays it (dlrm_plan_run).  The caller writes
-    each batch into the bound dense_in / indices tensors and reads `out`."""
+    """A dlrm_forward recorded once for fixed buffers (dlrm_plan_create), as
+    its packed launches (mode "direct") or as a HIP graph (mode "graph");
+    run() replays it (dlrm_plan_run).  The caller writes each batch into the
+    bound dense_in / indices tensors and reads `out`."""
 
     def __init__(self, model: DlrmModel, dense_in, indices, offsets=None, out=None,
-                 workspace=None):
+                 workspace=None, mode="direct"):
         torch = _torch()
         self._lib = load()
         self.model = model
@@ -475,7 +477,8 @@ class DlrmPlan:
         _check(self._lib.dlrm_plan_create(
             ctypes.byref(model.struct), self.batch, self.dense_in.data_ptr(), self._ip,
             self._op, self._nidx, self.out.data_ptr(), self.workspace.data_ptr(),
-            self.workspace.numel() * self.workspace.element_size(), ctypes.byref(self._handle)),
+            self.workspace.numel() * self.workspace.element_size(), PLAN_MODES[mode],
+            ctypes.byref(self._handle)),
             "dlrm_plan_create")
 
     def _bind(self, indices, offsets):

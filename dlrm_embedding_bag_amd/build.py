@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdlrm_mi355x.so")
-SOURCES = ["abi.hip", "emb_interact.hip", "linear.hip", "mlp_chain.hip"]
+SOURCES = ["abi.hip", "emb_interact.hip", "forward_small.hip", "linear.hip", "mlp_chain.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

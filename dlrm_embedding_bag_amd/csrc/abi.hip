@@ -3,9 +3,12 @@
 // argument error is reported before any work is enqueued; nothing here
 // allocates device memory or synchronizes the stream.
 #include <limits.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <functional>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "../../include/dlrm_embedding_bag.h"
@@ -163,6 +166,32 @@ int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
   return DLRM_OK;
 }
 
+// Where a forward's launches go: straight onto a stream, or into a list that
+// a plan replays later.  Each launch is a callable taking the stream.
+using Launch = std::function<hipError_t(hipStream_t)>;
+struct Emitter {
+  hipStream_t stream = nullptr;
+  std::vector<Launch> *record = nullptr;
+};
+
+template <typename F>
+int emit(const Emitter &em, F &&f) {
+  if (em.record) {
+    em.record->emplace_back(std::forward<F>(f));
+    return DLRM_OK;
+  }
+  return hip_status(f(em.stream));
+}
+
+// The one-launch forward is used whenever the model fits it, unless the
+// environment variable DLRM_FORWARD_LAYERED is set (a switch for comparing
+// the two compositions).
+bool small_forward_enabled() { return getenv("DLRM_FORWARD_LAYERED") == nullptr; }
+
+SmallLayer small_layer_of(const dlrm_layer &L) {
+  return SmallLayer{L.weight, L.bias, L.in_features, L.out_features, L.act};
+}
+
 // Checks every argument of a forward (nothing is enqueued).
 int validate_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                      const int32_t *const *indices, const int32_t *const *offsets,
@@ -187,7 +216,7 @@ int validate_forward(const dlrm_model *model, int32_t batch, const float *dense_
 int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                     const int32_t *const *indices, const int32_t *const *offsets,
                     const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
-                    hipStream_t st) {
+                    const Emitter &em) {
   ForwardLayout lay;
   int rc = plan_forward(model, batch, lay);
   if (rc) return rc;
@@ -202,6 +231,27 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return DLRM_ERR_WORKSPACE;
   const int B = batch, D = model->dim, K = model->num_tables;
+
+  // Models whose MLPs are small run the whole forward as one launch.
+  if (small_forward_enabled() && model->num_bottom <= kMaxSmallLayers &&
+      model->num_top <= kMaxSmallLayers) {
+    SmallLayer bl[kMaxSmallLayers], tl[kMaxSmallLayers];
+    for (int l = 0; l < model->num_bottom; ++l) bl[l] = small_layer_of(model->bottom[l]);
+    for (int l = 0; l < model->num_top; ++l) tl[l] = small_layer_of(model->top[l]);
+    SmallForwardParams sp{};
+    int threads = 0;
+    if (plan_forward_small(B, K, D, gc.vec, model->bottom[0].in_features, model->num_bottom, bl,
+                           model->num_top, tl, sp, threads)) {
+      sp.dense_in = dense_in;
+      sp.out = out;
+      sp.n_out = model->top[model->num_top - 1].out_features;
+      const bool csr = gc.csr, vec = gc.vec;
+      return emit(em, [=](hipStream_t s) {
+        return launch_forward_small(ts, csr, vec, sp, threads, s);
+      });
+    }
+  }
+
   char *ws = static_cast<char *>(workspace);
   float *R = reinterpret_cast<float *>(ws + lay.off_R);
   float *buf[2] = {reinterpret_cast<float *>(ws + lay.off_buf0),
@@ -213,7 +263,7 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   ChainParams cp;
   if (lay.bottom_chain &&
       pack_chain(B, model->num_bottom, model->bottom, dense_in, ldx, R, lay.ldR, cp)) {
-    rc = hip_status(launch_mlp_chain(cp, st));
+    rc = emit(em, [=](hipStream_t s) { return launch_mlp_chain(cp, s); });
     if (rc) return rc;
   } else {
   for (int l = 0; l < model->num_bottom; ++l) {
@@ -221,8 +271,10 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
     const bool last = l + 1 == model->num_bottom;
     float *y = last ? R : buf[l & 1];
     const int64_t ldy = last ? lay.ldR : lay.ld_buf;
-    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
-                                  L.act, y, ldy, st));
+    rc = emit(em, [=](hipStream_t s) {
+      return launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias, L.act, y,
+                           ldy, s);
+    });
     if (rc) return rc;
     x = y;
     ldx = ldy;
@@ -242,7 +294,7 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   ip.out_vec = 1;
   ip.emb_out = nullptr;
   ip.emb_in = nullptr;
-  rc = hip_status(launch_interact(&ts, gc, ip, threads, st));
+  rc = emit(em, [=](hipStream_t s) { return launch_interact(&ts, gc, ip, threads, s); });
   if (rc) return rc;
 
   // Top MLP on cat(dense, dots) = R.
@@ -250,14 +302,16 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   ldx = lay.ldR;
   const int32_t out_w = model->top[model->num_top - 1].out_features;
   if (lay.top_chain && pack_chain(B, model->num_top, model->top, R, lay.ldR, out, out_w, cp))
-    return hip_status(launch_mlp_chain(cp, st));
+    return emit(em, [=](hipStream_t s) { return launch_mlp_chain(cp, s); });
   for (int l = 0; l < model->num_top; ++l) {
     const dlrm_layer &L = model->top[l];
     const bool last = l + 1 == model->num_top;
     float *y = last ? out : buf[l & 1];
     const int64_t ldy = last ? L.out_features : lay.ld_buf;
-    rc = hip_status(launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
-                                  L.act, y, ldy, st));
+    rc = emit(em, [=](hipStream_t s) {
+      return launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias, L.act, y,
+                           ldy, s);
+    });
     if (rc) return rc;
     x = y;
     ldx = ldy;
@@ -273,7 +327,7 @@ int capture_forward(const dlrm_model &model, int32_t batch, const float *dense_i
   *graph = nullptr;
   if (hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed) != hipSuccess) return DLRM_ERR_HIP;
   const int rc = enqueue_forward(&model, batch, dense_in, indices, offsets, n_idx, out, workspace,
-                                 workspace_bytes, st);
+                                 workspace_bytes, Emitter{st, nullptr});
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(st, &g);
   if (rc || e != hipSuccess) {
@@ -422,7 +476,7 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
                  void *stream) {
   return enqueue_forward(model, batch, dense_in, indices, offsets, n_idx, out, workspace,
-                         workspace_bytes, (hipStream_t)stream);
+                         workspace_bytes, Emitter{(hipStream_t)stream, nullptr});
 }
 
 // ---------------------------------------------------------------------------
@@ -437,9 +491,11 @@ struct dlrm_plan {
   std::vector<int64_t> rows;
   dlrm_model model;
   int32_t batch = 0;
+  int32_t mode = DLRM_PLAN_DIRECT;
   void *workspace = nullptr;
   size_t workspace_bytes = 0;
-  hipStream_t capture = nullptr;
+  std::vector<Launch> launches;  // direct mode
+  hipStream_t capture = nullptr;  // graph mode
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
 };
@@ -447,9 +503,10 @@ struct dlrm_plan {
 int dlrm_plan_create(const dlrm_model *model, int32_t batch, const float *dense_in,
                      const int32_t *const *indices, const int32_t *const *offsets,
                      const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
-                     dlrm_plan **plan_out) {
+                     int32_t mode, dlrm_plan **plan_out) {
   if (!plan_out) return DLRM_ERR_NULL;
   *plan_out = nullptr;
+  if (mode != DLRM_PLAN_DIRECT && mode != DLRM_PLAN_GRAPH) return DLRM_ERR_SHAPE;
   int rc = validate_forward(model, batch, dense_in, indices, offsets, n_idx, out, workspace,
                             workspace_bytes);
   if (rc) return rc;
@@ -466,8 +523,19 @@ int dlrm_plan_create(const dlrm_model *model, int32_t batch, const float *dense_
   p->model.tables = p->tables.data();
   p->model.rows = p->rows.data();
   p->batch = batch;
+  p->mode = mode;
   p->workspace = workspace;
   p->workspace_bytes = workspace_bytes;
+  if (mode == DLRM_PLAN_DIRECT) {
+    rc = enqueue_forward(&p->model, batch, dense_in, indices, offsets, n_idx, out, workspace,
+                         workspace_bytes, Emitter{nullptr, &p->launches});
+    if (rc) {
+      delete p;
+      return rc;
+    }
+    *plan_out = p;
+    return DLRM_OK;
+  }
   if (hipStreamCreateWithFlags(&p->capture, hipStreamNonBlocking) != hipSuccess) {
     delete p;
     return DLRM_ERR_HIP;
@@ -491,6 +559,14 @@ int dlrm_plan_update(dlrm_plan *plan, const float *dense_in, const int32_t *cons
   int rc = validate_forward(&plan->model, plan->batch, dense_in, indices, offsets, n_idx, out,
                             plan->workspace, plan->workspace_bytes);
   if (rc) return rc;
+  if (plan->mode == DLRM_PLAN_DIRECT) {
+    std::vector<Launch> fresh;
+    rc = enqueue_forward(&plan->model, plan->batch, dense_in, indices, offsets, n_idx, out,
+                         plan->workspace, plan->workspace_bytes, Emitter{nullptr, &fresh});
+    if (rc) return rc;
+    plan->launches.swap(fresh);
+    return DLRM_OK;
+  }
   hipGraph_t g = nullptr;
   rc = capture_forward(plan->model, plan->batch, dense_in, indices, offsets, n_idx, out,
                        plan->workspace, plan->workspace_bytes, plan->capture, &g);
@@ -517,7 +593,11 @@ int dlrm_plan_update(dlrm_plan *plan, const float *dense_in, const int32_t *cons
 
 int dlrm_plan_run(dlrm_plan *plan, void *stream) {
   if (!plan) return DLRM_ERR_NULL;
-  return hip_status(hipGraphLaunch(plan->exec, (hipStream_t)stream));
+  const hipStream_t st = (hipStream_t)stream;
+  if (plan->mode == DLRM_PLAN_GRAPH) return hip_status(hipGraphLaunch(plan->exec, st));
+  for (const Launch &f : plan->launches)
+    if (f(st) != hipSuccess) return DLRM_ERR_HIP;
+  return DLRM_OK;
 }
 
 int dlrm_plan_destroy(dlrm_plan *plan) {

@@ -48,6 +48,36 @@ bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, i
 hipError_t launch_interact(const TableSet *ts, const GatherConfig &gc, const InteractParams &ip,
                            int threads, hipStream_t stream);
 
+// The whole forward in one launch (forward_small.hip) for small MLPs.
+constexpr int kMaxSmallLayers = 4;           // per MLP
+constexpr int kSmallMaxWidth = 1024;         // widest layer input or output
+constexpr int kSmallWeightFloats = 64 * 1024;  // all MLP weights together (256 KiB)
+
+struct SmallLayer {
+  const float *W;     // (N, K) dense
+  const float *bias;  // (N,) or nullptr
+  int K, N, act;
+};
+
+struct SmallForwardParams {
+  InteractParams ip;  // gather + interaction geometry (ip.out etc. unused)
+  int nb, nt;         // bottom and top layer counts
+  SmallLayer layer[2 * kMaxSmallLayers];  // bottom in [0, nb), top from kMaxSmallLayers
+  const float *dense_in;  // (B, in0)
+  int in0;
+  float *out;  // (B, n_out)
+  int n_out;
+  int ld_buf, ldR;            // LDS row strides (floats)
+  int r_off, a_off, b_off;    // LDS offsets (floats); the tile starts at 0
+};
+
+// Fills `p` (all but dense_in, out, n_out) for batch B; false if the model
+// is too large for the one-launch forward.
+bool plan_forward_small(int B, int K, int D, bool vec4, int in0, int nb, const SmallLayer *bottom,
+                        int nt, const SmallLayer *top, SmallForwardParams &p, int &threads);
+hipError_t launch_forward_small(const TableSet &ts, bool csr, bool vec4,
+                                const SmallForwardParams &p, int threads, hipStream_t stream);
+
 constexpr int kMaxChainLayers = 4;
 constexpr int kMaxChainWidth = 512;  // widest layer the MLP chain keeps in LDS
 #ifndef DLRM_CHAIN_NARROW_K

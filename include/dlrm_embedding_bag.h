@@ -300,6 +300,11 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  *   out        (B, top[last].out_features) float32
  *   workspace  device memory of at least dlrm_forward_workspace_bytes bytes,
  *              256-byte aligned; its contents are scratch
+ * Composition: a model whose MLPs hold at most 64 Ki weights in all (widths
+ * <= 1024, <= 4 layers each) runs as ONE launch with every intermediate on
+ * chip; larger models run each layer as its own tiled GEMM launch around the
+ * fused gather + interaction (7 launches for 3 + 3 layers).  Setting the
+ * environment variable DLRM_FORWARD_LAYERED forces the layered composition.
  */
 DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  const int32_t *const *indices, const int32_t *const *offsets,
@@ -316,21 +321,26 @@ DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *d
  * buffers and calls dlrm_plan_run.
  *
  * dlrm_plan_create -- validates exactly as dlrm_forward does (same argument
- *   meanings; batch >= 1), then records the forward's launches into a graph
- *   on a private stream and instantiates it.  The model's host arrays are
- *   copied into the plan; every device pointer (weights, tables, dense_in,
- *   indices, offsets, out, workspace) must stay valid while the plan lives.
- *   Allocates host memory and HIP graph objects, no device buffers.
- *   On success *plan receives the plan; on error it is set to NULL.
+ *   meanings; batch >= 1) and records the forward's launches once:
+ *     DLRM_PLAN_DIRECT  the launches with their packed kernel arguments;
+ *                       a run issues them with no validation or packing
+ *     DLRM_PLAN_GRAPH   a HIP graph (recorded on a private stream and
+ *                       instantiated); a run is one graph launch
+ *   The model's host arrays are copied into the plan; every device pointer
+ *   (weights, tables, dense_in, indices, offsets, out, workspace) must stay
+ *   valid while the plan lives.  Allocates host memory (and HIP graph
+ *   objects in graph mode), no device buffers.  An unknown mode is
+ *   DLRM_ERR_SHAPE.  On success *plan receives the plan; on error it is set
+ *   to NULL.
  *
  * dlrm_plan_update -- rebinds the per-batch buffers (dense_in, indices,
  *   offsets, n_idx, out) of a plan, same model, batch and workspace: the
- *   forward is recorded again and the executable graph updated in place
- *   (re-instantiated if the launch shapes changed).  Must not race a run of
- *   the same plan.
+ *   forward is recorded again (in graph mode the executable graph is updated
+ *   in place, or re-instantiated if the launch shapes changed).  Must not
+ *   race a run of the same plan.
  *
- * dlrm_plan_run -- enqueues one forward on `stream` (one graph launch); no
- *   host work besides the launch and no synchronization.  Runs of one plan
+ * dlrm_plan_run -- enqueues one forward on `stream` (the recorded launches,
+ *   or one graph launch); no other host work and no synchronization.  Runs of one plan
  *   share its workspace and output, so runs on different streams must be
  *   ordered by the caller.
  *
@@ -340,10 +350,15 @@ DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *d
  */
 typedef struct dlrm_plan dlrm_plan;
 
+typedef enum dlrm_plan_mode {
+  DLRM_PLAN_DIRECT = 0, /* replay the recorded launches          */
+  DLRM_PLAN_GRAPH = 1   /* replay a HIP graph of the launches    */
+} dlrm_plan_mode;
+
 DLRM_API int dlrm_plan_create(const dlrm_model *model, int32_t batch, const float *dense_in,
                               const int32_t *const *indices, const int32_t *const *offsets,
                               const int64_t *n_idx, float *out, void *workspace,
-                              size_t workspace_bytes, dlrm_plan **plan);
+                              size_t workspace_bytes, int32_t mode, dlrm_plan **plan);
 DLRM_API int dlrm_plan_update(dlrm_plan *plan, const float *dense_in,
                               const int32_t *const *indices, const int32_t *const *offsets,
                               const int64_t *n_idx, float *out);

@@ -231,17 +231,21 @@ def test_plan_argument_errors(lib):
     n = _n(K, B * 20)
     f = lib.dlrm_plan_create
     h = ctypes.c_void_p(FAKE)
-    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws, None) == 1
-    assert f(ctypes.byref(bad_dim), B, FAKE, idx, None, n, FAKE, FAKE, ws,
-             ctypes.byref(h)) == 2
-    assert h.value is None, "a failed create leaves NULL in *plan"
-    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws - 1,
-             ctypes.byref(h)) == 4
-    assert f(ctypes.byref(good), B, None, idx, None, n, FAKE, FAKE, ws, ctypes.byref(h)) == 1
-    assert f(ctypes.byref(good), B, FAKE, idx, None, _n(K, B * 20 + 1), FAKE, FAKE, ws,
-             ctypes.byref(h)) == 2
-    assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, FAKE, ws,
-             ctypes.byref(h)) == 2                                      # batch 0: no plan
+    for mode in (0, 1):
+        assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws, mode, None) == 1
+        assert f(ctypes.byref(bad_dim), B, FAKE, idx, None, n, FAKE, FAKE, ws, mode,
+                 ctypes.byref(h)) == 2
+        assert h.value is None, "a failed create leaves NULL in *plan"
+        assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws - 1, mode,
+                 ctypes.byref(h)) == 4
+        assert f(ctypes.byref(good), B, None, idx, None, n, FAKE, FAKE, ws, mode,
+                 ctypes.byref(h)) == 1
+        assert f(ctypes.byref(good), B, FAKE, idx, None, _n(K, B * 20 + 1), FAKE, FAKE, ws,
+                 mode, ctypes.byref(h)) == 2
+        assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, FAKE, ws, mode,
+                 ctypes.byref(h)) == 2                                  # batch 0: no plan
+    assert f(ctypes.byref(good), B, FAKE, idx, None, n, FAKE, FAKE, ws, 2,
+             ctypes.byref(h)) == 2                                      # unknown mode
     assert lib.dlrm_plan_run(None, None) == 1
     assert lib.dlrm_plan_update(None, FAKE, idx, None, n, FAKE) == 1
     assert lib.dlrm_plan_destroy(None) == 0

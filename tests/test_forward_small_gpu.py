@@ -1,0 +1,85 @@
+"""GPU parity of the one-launch forward: dlrm_forward runs models whose MLPs
+are small (at most 64 Ki weights, widths <= 1024, <= 4 layers per MLP) as a
+single kernel.  Compared with the oracle on the pages' cell shapes and on
+ragged ones (scalar path, CSR bags, batches that leave a workgroup partly
+empty), and with the layered composition (DLRM_FORWARD_LAYERED) within the
+float tolerance."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import gpu_available
+from gpu_helpers import assert_close, dev, host
+from dlrm_embedding_bag_amd import abi, inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+def _case(w, seed, bias_std=0.1, csr=False):
+    rng = np.random.default_rng(seed)
+    tables = [inputs.table_host(w, k, seed) * np.float32(10) for k in range(w.num_tables)]
+    bottom, top = inputs.dlrm_layers(w, seed, bias_std=bias_std)
+    dense = inputs.dense(w, seed)
+    if csr:
+        lens = rng.integers(0, 2 * w.bag + 2, size=(w.num_tables, w.batch))
+        offs = [np.concatenate([[0], np.cumsum(l)[:-1]]).astype(np.int32) for l in lens]
+        idx = [rng.integers(0, w.rows, int(l.sum())).astype(np.int32) for l in lens]
+    else:
+        offs = None
+        idx = [inputs.indices(w, k, seed) for k in range(w.num_tables)]
+    model = abi.DlrmModel([(dev(a), dev(b), act) for a, b, act in bottom],
+                          [(dev(a), dev(b), act) for a, b, act in top],
+                          [dev(t) for t in tables])
+    return tables, idx, offs, dense, bottom, top, model
+
+
+def _run(model, dense, idx, offs, layered=False):
+    if layered:
+        os.environ["DLRM_FORWARD_LAYERED"] = "1"
+    try:
+        return host(abi.dlrm_forward(model, dev(dense), [dev(i) for i in idx],
+                                     offsets=[dev(o) for o in offs] if offs else None))
+    finally:
+        os.environ.pop("DLRM_FORWARD_LAYERED", None)
+
+
+SHAPES = [  # (num_tables, batch, D, bag, bottom, top)
+    (2, 2, 16, 2, (16,), (16, 1)),          # the pages' smallest cell
+    (32, 2048, 16, 2, (16,), (16, 1)),      # the pages' largest cell
+    (8, 1025, 16, 2, (16,), (16, 1)),       # ragged last workgroup
+    (5, 37, 12, 3, (24, 12), (20, 8, 2)),   # D % 16 != 0, two outputs
+    (3, 19, 7, 4, (9, 7), (11, 1)),         # D % 4 != 0: scalar path
+    (26, 300, 64, 5, (64, 64), (64, 1)),    # D = 64, 26 tables
+    (4, 64, 32, 20, (128, 64, 32), (96, 48, 24, 1)),  # four top layers, long bags
+]
+
+
+@pytest.mark.parametrize("csr", [False, True])
+@pytest.mark.parametrize("K,B,D,L,bottom,top", SHAPES)
+def test_one_launch_forward_vs_oracle(K, B, D, L, bottom, top, csr):
+    w = inputs.Workload("small", batch=B, num_tables=K, rows=4096, dim=D, bag=L, dist="uniform",
+                        dense_in=3, bottom=bottom, top=top)
+    tables, idx, offs, dense, bl, tl, model = _case(w, seed=K + B, csr=csr)
+    want, _, _ = oracle.forward(dense, bl, tl, tables, idx, offs)
+    got = _run(model, dense, idx, offs)
+    assert got.shape == want.shape
+    assert_close(got, want, "one-launch forward")
+    layered = _run(model, dense, idx, offs, layered=True)
+    assert_close(layered, want, "layered forward")
+    assert_close(got, layered, "one launch vs layered")
+
+
+def test_one_launch_forward_is_one_kernel_in_a_plan():
+    """A plan of a small model replays the single launch; every replay
+    equals the eager call bit for bit."""
+    w = inputs.cell_workload(16, 256)
+    tables, idx, offs, dense, bl, tl, model = _case(w, seed=4)
+    d, x = dev(dense), [dev(i) for i in idx]
+    plan = abi.DlrmPlan(model, d, x)
+    eager = host(abi.dlrm_forward(model, d, x))
+    for _ in range(3):
+        assert np.array_equal(host(plan.run()), eager)
+    plan.close()

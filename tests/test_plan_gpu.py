@@ -35,14 +35,15 @@ CASES = [inputs.cell_workload(2, 2), inputs.cell_workload(32, 2048),
                          dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1))]
 
 
+@pytest.mark.parametrize("mode", ["direct", "graph"])
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
-def test_plan_replays_equal_eager_forward(w):
+def test_plan_replays_equal_eager_forward(w, mode):
     import torch
     model, tables, bottom, top = _model(w)
     dense0, idx0 = _batch(w, 0)
     dense_buf = dev(dense0)
     idx_buf = [dev(i) for i in idx0]
-    plan = abi.DlrmPlan(model, dense_buf, idx_buf)
+    plan = abi.DlrmPlan(model, dense_buf, idx_buf, mode=mode)
     # the first replay against the oracle
     got = host(plan.run())
     want, _, _ = oracle.forward(dense0, bottom, top, tables, idx0)
@@ -61,14 +62,18 @@ def test_plan_replays_equal_eager_forward(w):
     plan.close()
 
 
-def test_plan_on_a_side_stream_and_update():
+@pytest.mark.parametrize("mode", ["direct", "graph"])
+@pytest.mark.parametrize("layered", [False, True])
+def test_plan_on_a_side_stream_and_update(mode, layered, monkeypatch):
     """A plan replays on a caller stream; update() rebinds other buffers,
-    including CSR offsets (another gather kernel: the graph is rebuilt)."""
+    including CSR offsets (another gather kernel: a graph is rebuilt)."""
     import torch
+    if layered:
+        monkeypatch.setenv("DLRM_FORWARD_LAYERED", "1")
     w = inputs.cell_workload(16, 300)
     model, tables, bottom, top = _model(w, seed=3)
     dense, idx = _batch(w, 1)
-    plan = abi.DlrmPlan(model, dev(dense), [dev(i) for i in idx])
+    plan = abi.DlrmPlan(model, dev(dense), [dev(i) for i in idx], mode=mode)
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         out = plan.run(stream=side)
@@ -106,6 +111,7 @@ def test_plan_rejects_bad_arguments():
         abi.DlrmPlan(model, dev(dense), [dev(i) for i in idx][:-1] + [dev(idx[-1][:-1])])
     assert e.value.name == "DLRM_ERR_SHAPE"
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(abi.DlrmError) as e:
-        abi.DlrmPlan(model, dev(dense), [dev(i) for i in idx], workspace=small)
-    assert e.value.name == "DLRM_ERR_WORKSPACE"
+    for mode in ("direct", "graph"):
+        with pytest.raises(abi.DlrmError) as e:
+            abi.DlrmPlan(model, dev(dense), [dev(i) for i in idx], workspace=small, mode=mode)
+        assert e.value.name == "DLRM_ERR_WORKSPACE"
