@@ -69,6 +69,8 @@ struct SmallForwardParams {
   int n_out;
   int ld_buf, ldR;            // LDS row strides (floats)
   int r_off, a_off, b_off;    // LDS offsets (floats); the tile starts at 0
+  int w_lds;                  // weights and biases are staged in LDS
+  int w_off[2 * kMaxSmallLayers], bias_off[2 * kMaxSmallLayers];  // their LDS offsets
 };
 
 // Fills `p` (all but dense_in, out, n_out) for batch B; false if the model
