@@ -57,6 +57,7 @@ METRIC = ("samples/sec + µs/forward (emb-bag+interact, B=2048 nc=32); "
           "achieved HBM GB/s")
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ["dlrm_embedding_bag_amd/csrc/emb_interact.hip",
+                  "dlrm_embedding_bag_amd/csrc/gather_interact.hpp",
                   "dlrm_embedding_bag_amd/csrc/common.hpp"]
 
 
@@ -596,7 +597,8 @@ def bench_variants(args, stream, flush):
         rows.append({"workload": f"{name}: {w.description}", "us": ms * 1e3,
                      "samples_per_s": case.B / (ms * 1e-3),
                      "algorithmic_bytes_per_launch": nbytes, "algorithmic_gbps": gbs,
-                     "frac_hbm": gbs / HBM_PEAK_GBPS})
+                     "frac_hbm": gbs / HBM_PEAK_GBPS,
+                     "traffic": read_traffic(kernel_source_hash(), name)})
         log(f"variant {name:14s} {ms * 1000:7.1f} us {case.B / (ms * 1e-3) / 1e6:6.1f} M "
             f"samples/s {gbs:6.0f} GB/s")
         del case
