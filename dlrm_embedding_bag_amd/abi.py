@@ -27,7 +27,8 @@ POOLS = {"sum": 0, "mean": 1}
 PLAN_MODES = {"direct": 0, "graph": 1}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
-           "dlrm_emb_interact_pool", "linear_bias_act", "mlp_forward",
+           "dlrm_emb_interact_pool", "dlrm_emb_interact_dots", "linear_bias_act",
+           "linear_bias_act_split", "mlp_forward",
            "dlrm_forward_workspace_bytes", "dlrm_forward", "dlrm_plan_create",
            "dlrm_plan_update", "dlrm_plan_run", "dlrm_plan_destroy")
 
@@ -92,6 +93,11 @@ def load(path: str = LIB_PATH):
     lib.emb_bag_pool.argtypes = [ctypes.POINTER(Bags), _vp, _vp]
     lib.dlrm_emb_interact_pool.restype = ctypes.c_int
     lib.dlrm_emb_interact_pool.argtypes = [ctypes.POINTER(Bags), _vp, _vp, _vp, _vp]
+    lib.dlrm_emb_interact_dots.restype = ctypes.c_int
+    lib.dlrm_emb_interact_dots.argtypes = [ctypes.POINTER(Bags), _vp, _vp, _i64, _vp, _vp]
+    lib.linear_bias_act_split.restype = ctypes.c_int
+    lib.linear_bias_act_split.argtypes = [_i32, _i32, _i32, _vp, _i64, _i32, _vp, _i64, _vp, _vp,
+                                          _i32, _vp, _i64, _vp]
     lib.linear_bias_act.restype = ctypes.c_int
     lib.linear_bias_act.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _i64,
                                     _vp]
@@ -326,6 +332,74 @@ def dlrm_emb_interact_pool(tables, indices, dense, offsets=None, weights=None, p
         eo = emb_out.data_ptr()
     _check(lib.dlrm_emb_interact_pool(ctypes.byref(g.struct), dense.data_ptr(), out.data_ptr(),
                                       eo, _stream(stream)), "dlrm_emb_interact_pool")
+    return out
+
+
+def dlrm_emb_interact_dots(tables, indices, dense, offsets=None, weights=None, pool="sum",
+                           out=None, emb_out=None, stream=None):
+    """Fused gather + interaction writing only the dots: (B, F(F-1)/2) float32
+    (out may be a row-strided view with unit column stride)."""
+    torch = _torch()
+    lib = load()
+    _dev(dense, torch.float32, "dense")
+    g = _BagsArg(tables, indices, offsets, weights, pool, dense.shape[0])
+    B, D = dense.shape
+    if D != g.D:
+        raise ValueError("dense must be (B, D)")
+    P = (g.K + 1) * g.K // 2
+    if out is None:
+        out = torch.empty((B, P), dtype=torch.float32, device=dense.device)
+    if (not isinstance(out, torch.Tensor) or out.device.type != "cuda"
+            or out.dtype != torch.float32 or out.shape != (B, P) or out.stride(1) != 1):
+        raise ValueError("out must be a (B, F(F-1)/2) float32 GPU tensor with unit column stride")
+    eo = None
+    if emb_out is not None:
+        _dev(emb_out, torch.float32, "emb_out")
+        if emb_out.shape != (B, g.K, D):
+            raise ValueError("emb_out must be (B, K, D)")
+        eo = emb_out.data_ptr()
+    _check(lib.dlrm_emb_interact_dots(ctypes.byref(g.struct), dense.data_ptr(), out.data_ptr(),
+                                      out.stride(0), eo, _stream(stream)),
+           "dlrm_emb_interact_dots")
+    return out
+
+
+def _matrix(t, what):
+    torch = _torch()
+    if (not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.float32
+            or t.dim() != 2 or t.stride(1) != 1):
+        raise ValueError(f"{what} must be a 2-D float32 GPU tensor with unit column stride")
+    return t
+
+
+def linear_bias_act_split(a_lo, a_hi, w, bias=None, act="none", out=None, stream=None):
+    """act([a_lo | a_hi] @ w.T + bias) as (M, N) float32, the concat read in place."""
+    torch = _torch()
+    lib = load()
+    _matrix(a_lo, "a_lo")
+    _matrix(a_hi, "a_hi")
+    _dev(w, torch.float32, "w")
+    M, K_lo = a_lo.shape
+    K_hi = a_hi.shape[1]
+    if a_hi.shape[0] != M or w.shape[1] != K_lo + K_hi:
+        raise ValueError("a_lo (M, K_lo), a_hi (M, K_hi) and w (N, K_lo + K_hi) disagree")
+    N = w.shape[0]
+    bp = None
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+        bp = bias.data_ptr()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a_lo.device)
+    _matrix(out, "out")
+    if out.shape != (M, N):
+        raise ValueError("out must be (M, N)")
+    _check(lib.linear_bias_act_split(M, N, K_lo, a_lo.data_ptr(), a_lo.stride(0), K_hi,
+                                     a_hi.data_ptr(), a_hi.stride(0), w.data_ptr(), bp,
+                                     ACTS[act] if isinstance(act, str) else int(act),
+                                     out.data_ptr(), out.stride(0), _stream(stream)),
+           "linear_bias_act_split")
     return out
 
 

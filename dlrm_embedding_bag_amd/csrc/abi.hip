@@ -287,6 +287,7 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   int threads = 0;
   if (!plan_interact(B, K, D, gc.vec, chunk_elems(gc), ip, threads)) return DLRM_ERR_UNSUPPORTED;
   ip.copy_dense = 0;
+  ip.dot_off = D;
   ip.dense = R;
   ip.ld_dense = lay.ldR;
   ip.out = R;
@@ -391,6 +392,7 @@ int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim, const f
   if (!plan_interact(batch, num_emb, dim, gc.vec, gc.vec ? 4 : 1, ip, threads))
     return DLRM_ERR_UNSUPPORTED;
   ip.copy_dense = 1;
+  ip.dot_off = dim;
   ip.dense = dense;
   ip.ld_dense = dim;
   ip.out = out;
@@ -417,11 +419,41 @@ int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, float *out
   if (!plan_interact(batch, K, dim, gc.vec, chunk_elems(gc), ip, threads))
     return DLRM_ERR_UNSUPPORTED;
   ip.copy_dense = 1;
+  ip.dot_off = dim;
   ip.dense = dense;
   ip.ld_dense = dim;
   ip.out = out;
   ip.ld_out = dim + ip.P;
   ip.out_vec = aligned16(out) && ip.ld_out % 4 == 0;
+  ip.emb_out = emb_out;
+  ip.emb_in = nullptr;
+  return hip_status(launch_interact(&ts, gc, ip, threads, (hipStream_t)stream));
+}
+
+int dlrm_emb_interact_dots(const dlrm_bags *bags, const float *dense, float *dots,
+                           int64_t ld_dots, float *emb_out, void *stream) {
+  if (!bags) return DLRM_ERR_NULL;
+  TableSet ts;
+  GatherConfig gc;
+  int rc = pack_bags(*bags, ts, gc);
+  if (rc) return rc;
+  const int32_t batch = bags->batch, K = bags->num_tables, dim = bags->dim;
+  const int64_t F = (int64_t)K + 1;
+  if (ld_dots < F * (F - 1) / 2) return DLRM_ERR_SHAPE;
+  if (batch == 0) return DLRM_OK;  // nothing to read or write
+  if (!dense || !dots) return DLRM_ERR_NULL;
+  gc.vec = gc.vec && aligned16(dense) && (!emb_out || aligned16(emb_out));
+  InteractParams ip{};
+  int threads = 0;
+  if (!plan_interact(batch, K, dim, gc.vec, chunk_elems(gc), ip, threads))
+    return DLRM_ERR_UNSUPPORTED;
+  ip.copy_dense = 0;
+  ip.dot_off = 0;
+  ip.dense = dense;
+  ip.ld_dense = dim;
+  ip.out = dots;
+  ip.ld_out = ld_dots;
+  ip.out_vec = 0;
   ip.emb_out = emb_out;
   ip.emb_in = nullptr;
   return hip_status(launch_interact(&ts, gc, ip, threads, (hipStream_t)stream));
@@ -444,6 +476,18 @@ int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda
   if (m == 0) return DLRM_OK;  // nothing to read or write
   if (!a || !w || !c) return DLRM_ERR_NULL;
   return hip_status(launch_linear(m, n, k, a, lda, w, bias, act, c, ldc, (hipStream_t)stream));
+}
+
+int linear_bias_act_split(int32_t m, int32_t n, int32_t k_lo, const float *a_lo, int64_t lda_lo,
+                          int32_t k_hi, const float *a_hi, int64_t lda_hi, const float *w,
+                          const float *bias, int32_t act, float *c, int64_t ldc, void *stream) {
+  if (m < 0 || n < 1 || k_lo < 1 || k_hi < 1 || (int64_t)k_lo + k_hi > INT32_MAX ||
+      lda_lo < k_lo || lda_hi < k_hi || ldc < n || !valid_act(act))
+    return DLRM_ERR_SHAPE;
+  if (m == 0) return DLRM_OK;  // nothing to read or write
+  if (!a_lo || !a_hi || !w || !c) return DLRM_ERR_NULL;
+  return hip_status(launch_linear_split(m, n, k_lo, a_lo, lda_lo, k_hi, a_hi, lda_hi, w, bias,
+                                        act, c, ldc, (hipStream_t)stream));
 }
 
 int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers, const float *a,

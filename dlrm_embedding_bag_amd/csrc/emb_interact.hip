@@ -90,7 +90,7 @@ __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractPar
   __syncthreads();
 
   // Phase 2: the strict-lower-triangle dots.
-  float *out0 = ip.out + (int64_t)b0 * ip.ld_out;
+  float *out0 = ip.out + (int64_t)b0 * ip.ld_out + ip.dot_off;
   const int nvalid = min(S, B - b0);
   if constexpr (VW == 4)
     dots_blocked(X, ip, FR, out0, ip.ld_out, nvalid);

@@ -172,9 +172,9 @@ __global__ __launch_bounds__(kSmallThreads) void forward_small_kernel(TableSet t
     R[s * p.ldR + c] = X[(size_t)(s * FR) * DP + c];
   }
   if constexpr (VW == 4)
-    dots_blocked(X, ip, FR, R, p.ldR, S);
+    dots_blocked(X, ip, FR, R + D, p.ldR, S);
   else
-    dots_per_pair<VW>(X, ip, FR, R, p.ldR, S);
+    dots_per_pair<VW>(X, ip, FR, R + D, p.ldR, S);
   __syncthreads();
 
   // Top MLP; its last layer writes the output rows of the valid samples.

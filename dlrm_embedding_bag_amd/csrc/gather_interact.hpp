@@ -312,7 +312,7 @@ __device__ __forceinline__ void pool_bag(const TableSet &ts, int k, int b, int B
 enum { MODE_FUSED = 0, MODE_LOAD = 1 };
 
 
-// The dots of the S samples staged in X go to out0 + s * ld + D + p for the
+// The dots of the S samples staged in X go to out0 + s * ld + p for the
 // nvalid first samples (out0 may point to global memory or to LDS).
 
 // One quad per dot, p -> (i, j) in closed form (any D; used by the scalar path).
@@ -335,7 +335,7 @@ __device__ __forceinline__ void dots_per_pair(const float *X, const InteractPara
     float acc = 0.0f;
     for (int c = r; c < nvec; c += 4) acc = vdot_acc(xi[c], xj[c], acc);
     acc = quad_sum(acc);
-    if (r == 0 && s < nvalid) out0[(int64_t)s * ld + D + p] = acc;
+    if (r == 0 && s < nvalid) out0[(int64_t)s * ld + p] = acc;
   }
 }
 
@@ -429,7 +429,7 @@ __device__ __forceinline__ void dots_blocked(const float *X, const InteractParam
     // lane r of quad 0 holds dots (4I + x, 4J + y), y = 0..3, x = 2*(r&1) + ((r>>1)&1)
     const int i = 4 * I + 2 * (r & 1) + ((r >> 1) & 1);
     if (tl < 4 && s < nvalid && i < F) {
-      float *o = out0 + (int64_t)s * ld + D + i * (i - 1) / 2;
+      float *o = out0 + (int64_t)s * ld + i * (i - 1) / 2;
 #pragma unroll
       for (int y = 0; y < 4; ++y) {
         const int j = 4 * J + y;

@@ -18,6 +18,7 @@ struct InteractParams {
   int Q;            // quads per 4 x 4 dot block (blocked interaction)
   int lds_bytes;    // dynamic LDS per workgroup
   int copy_dense;   // write dense into out[:, 0:D]
+  int dot_off;      // column of the first dot in an out row: D, or 0 for dots only
   int out_vec;      // out rows are 16-byte aligned (vector dense copy)
   const float *dense;
   int64_t ld_dense;
@@ -115,5 +116,11 @@ hipError_t launch_mlp_chain(ChainParams p, hipStream_t stream);
 // C = act(A W^T + bias); A (M, K) stride lda, W (N, K) dense, C stride ldc.
 hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const float *W,
                          const float *bias, int act, float *C, int64_t ldc, hipStream_t stream);
+// The same with A = [A_lo | A_hi]: A_lo (M, K_lo) stride lda_lo, A_hi (M, K_hi)
+// stride lda_hi, W (N, K_lo + K_hi).
+hipError_t launch_linear_split(int M, int N, int K_lo, const float *A_lo, int64_t lda_lo,
+                               int K_hi, const float *A_hi, int64_t lda_hi, const float *W,
+                               const float *bias, int act, float *C, int64_t ldc,
+                               hipStream_t stream);
 
 }  // namespace dlrm

@@ -25,6 +25,12 @@
 //
 // Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
 // bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
+//
+// Split A ([FASTPATHS] matmul2d.rs, a_split and the *_split_a frontends: the
+// top MLP reads cat(dense, interactions) from two pointers without building
+// the concat): columns [0, k_lo) of A come from one matrix and [k_lo, K) from
+// another.  Both kernels take the A source as a struct; the unsplit
+// instantiations never look at its second half.
 #include <math.h>
 
 #include "common.hpp"
@@ -50,6 +56,16 @@ __device__ __forceinline__ float apply_act(float x, int act) {
 
 // float4 of columns k..k+3 of row `row` (already clamped into the matrix) of
 // a matrix with stride ld, for a slab known to lie inside K: no bounds tests.
+// Where A's columns live: [0, k_lo) in lo (row stride ld_lo), [k_lo, K) in
+// hi (row stride ld_hi) when split.
+struct ASrc {
+  const float *lo;
+  int64_t ld_lo;
+  const float *hi;
+  int64_t ld_hi;
+  int k_lo;
+};
+
 template <bool VEC>
 __device__ __forceinline__ float4 load_full(const float *__restrict__ base, int64_t ld, int row,
                                             int k) {
@@ -73,10 +89,47 @@ __device__ __forceinline__ float4 load_tail(const float *__restrict__ base, int6
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <int BM, int BN, int GM, int GN, bool VA, bool VW, bool VC>
-__global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
-                                                            const float *__restrict__ A,
-                                                            int64_t lda,
+// Column k (and k+1..k+3) of row `row` of A, inside K.  Split: with VEC the
+// split point is a multiple of 4, so a float4 lies in one half; without, each
+// element picks its half.
+template <bool SPLIT, bool VEC>
+__device__ __forceinline__ float4 load_a_full(const ASrc &a, int row, int k) {
+  if constexpr (!SPLIT) {
+    return load_full<VEC>(a.lo, a.ld_lo, row, k);
+  } else if constexpr (VEC) {
+    const bool lo = k < a.k_lo;
+    return load_full<true>(lo ? a.lo : a.hi, lo ? a.ld_lo : a.ld_hi, row, lo ? k : k - a.k_lo);
+  } else {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kk = k + e;
+      v[e] = kk < a.k_lo ? a.lo[(int64_t)row * a.ld_lo + kk]
+                         : a.hi[(int64_t)row * a.ld_hi + (kk - a.k_lo)];
+    }
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <bool SPLIT>
+__device__ __forceinline__ float4 load_a_tail(const ASrc &a, int row, int k, int K) {
+  if constexpr (!SPLIT) {
+    return load_tail(a.lo, a.ld_lo, row, k, K);
+  } else {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kk = min(k + e, K - 1);
+      const float x = kk < a.k_lo ? a.lo[(int64_t)row * a.ld_lo + kk]
+                                  : a.hi[(int64_t)row * a.ld_hi + (kk - a.k_lo)];
+      v[e] = k + e < K ? x : 0.0f;
+    }
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <int BM, int BN, int GM, int GN, bool VA, bool VW, bool VC, bool SPLIT>
+__global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K, const ASrc A,
                                                             const float *__restrict__ W,
                                                             const float *__restrict__ bias,
                                                             int act, float *__restrict__ C,
@@ -136,12 +189,12 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
     const int kb = sl * kBK;
     if (sl < nfull) {
 #pragma unroll
-      for (int i = 0; i < A_V4; ++i) ra[i] = load_full<VA>(A, lda, arow[i], kb + acol[i]);
+      for (int i = 0; i < A_V4; ++i) ra[i] = load_a_full<SPLIT, VA>(A, arow[i], kb + acol[i]);
 #pragma unroll
       for (int i = 0; i < W_V4; ++i) rw[i] = load_full<VW>(W, K, wrow[i], kb + wcol[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < A_V4; ++i) ra[i] = load_tail(A, lda, arow[i], kb + acol[i], K);
+      for (int i = 0; i < A_V4; ++i) ra[i] = load_a_tail<SPLIT>(A, arow[i], kb + acol[i], K);
 #pragma unroll
       for (int i = 0; i < W_V4; ++i) rw[i] = load_tail(W, K, wrow[i], kb + wcol[i], K);
     }
@@ -261,9 +314,8 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
 }
 
 // N <= 8: each wave computes 4 rows at a time, 16 lanes per row.
-template <bool VEC>
-__global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K,
-                                                   const float *__restrict__ A, int64_t lda,
+template <bool VEC, bool SPLIT>
+__global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K, const ASrc A,
                                                    const float *__restrict__ W,
                                                    const float *__restrict__ bias, int act,
                                                    float *__restrict__ C, int64_t ldc) {
@@ -274,18 +326,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K,
   // All 16 lanes of a row stay active through the DPP sums, so rows past M
   // compute on row M-1 and skip the store.
   const int mr = m < M ? m : M - 1;
-  const float *a = A + (int64_t)mr * lda;
+  const float *a = A.lo + (int64_t)mr * A.ld_lo;
+  const float *ah = SPLIT ? A.hi + (int64_t)mr * A.ld_hi - A.k_lo : nullptr;  // column k at ah[k]
   for (int n = 0; n < N; ++n) {
     const float *w = W + (int64_t)n * K;
     float acc = 0.0f;
     if (VEC) {
       for (int k = 4 * c; k < K; k += 64) {
-        const float4 x = *reinterpret_cast<const float4 *>(a + k);
+        const float *src = (SPLIT && k >= A.k_lo) ? ah : a;
+        const float4 x = *reinterpret_cast<const float4 *>(src + k);
         const float4 y = *reinterpret_cast<const float4 *>(w + k);
         acc = vdot_acc(x, y, acc);
       }
     } else {
-      for (int k = c; k < K; k += 16) acc = __builtin_fmaf(a[k], w[k], acc);
+      for (int k = c; k < K; k += 16)
+        acc = __builtin_fmaf((SPLIT && k >= A.k_lo) ? ah[k] : a[k], w[k], acc);
     }
     acc = row16_sum(acc);
     if (c == 0 && m < M) {
@@ -295,17 +350,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K,
   }
 }
 
-template <int BM, int BN, int GM, int GN>
-hipError_t launch_gemm_cfg(int M, int N, int K, const float *A, int64_t lda, const float *W,
-                           const float *bias, int act, float *C, int64_t ldc, bool va, bool vw,
-                           bool vc, hipStream_t stream) {
+template <int BM, int BN, int GM, int GN, bool SPLIT>
+hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, const float *W, const float *bias,
+                           int act, float *C, int64_t ldc, bool va, bool vw, bool vc,
+                           hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   const int xcd_chunk = (tiles % 8 == 0) ? (int)(tiles / 8) : 0;
   dim3 grid((unsigned)tiles), block(64 * GM * GN);
 #define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                       \
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, GM, GN, A_, W_, C_>), grid, block, 0, stream, M, N, \
-                     K, A, lda, W, bias, act, C, ldc, tiles_n, xcd_chunk)
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, GM, GN, A_, W_, C_, SPLIT>), grid, block, 0, stream,  \
+                     M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk)
   if (va && vw && vc)
     DLRM_GEMM_LAUNCH(true, true, true);
   else if (va && !vw && vc)
@@ -322,22 +377,21 @@ hipError_t launch_gemm_cfg(int M, int N, int K, const float *A, int64_t lda, con
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const float *W,
-                         const float *bias, int act, float *C, int64_t ldc, hipStream_t stream) {
-  const bool va = aligned16(A) && lda % 4 == 0;
+template <bool SPLIT>
+hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const float *W,
+                             const float *bias, int act, float *C, int64_t ldc,
+                             hipStream_t stream) {
   const bool vw = aligned16(W) && K % 4 == 0;
   const bool vc = aligned16(C) && ldc % 4 == 0;
   if (N <= 8) {
     const int rows_per_block = 16;
     dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(256);
     if (va && vw && K % 4 == 0)
-      hipLaunchKernelGGL((gemv_kernel<true>), grid, block, 0, stream, M, N, K, A, lda, W, bias,
+      hipLaunchKernelGGL((gemv_kernel<true, SPLIT>), grid, block, 0, stream, M, N, K, A, W, bias,
                          act, C, ldc);
     else
-      hipLaunchKernelGGL((gemv_kernel<false>), grid, block, 0, stream, M, N, K, A, lda, W, bias,
-                         act, C, ldc);
+      hipLaunchKernelGGL((gemv_kernel<false, SPLIT>), grid, block, 0, stream, M, N, K, A, W,
+                         bias, act, C, ldc);
     return hipGetLastError();
   }
   // Tile shape: the largest tile that still gives every CU a workgroup.
@@ -347,28 +401,47 @@ hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const
 #else
   constexpr int forced = 0;
 #endif
-  if (forced == 7)
-    return launch_gemm_cfg<128, 64, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                          stream);
-  if (forced == 8)
-    return launch_gemm_cfg<64, 128, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                          stream);
-  if (forced == 9)
-    return launch_gemm_cfg<128, 128, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                           stream);
-  if (forced == 10)
-    return launch_gemm_cfg<64, 64, 1, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                         stream);
+  if constexpr (forced == 7)
+    return launch_gemm_cfg<128, 64, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                 stream);
+  if constexpr (forced == 8)
+    return launch_gemm_cfg<64, 128, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                 stream);
+  if constexpr (forced == 9)
+    return launch_gemm_cfg<128, 128, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                  stream);
+  if constexpr (forced == 10)
+    return launch_gemm_cfg<64, 64, 1, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                stream);
   // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
   // for every CU, else 64 x 64, else 64 x 32 on 4 waves.
   if (forced == 1 || (forced == 0 && tiles(128, 128) >= 256))
-    return launch_gemm_cfg<128, 128, 2, 4>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                           stream);
+    return launch_gemm_cfg<128, 128, 2, 4, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                  stream);
   if (forced == 3 || (forced == 0 && tiles(64, 64) >= 256))
-    return launch_gemm_cfg<64, 64, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                         stream);
-  return launch_gemm_cfg<64, 32, 2, 2>(M, N, K, A, lda, W, bias, act, C, ldc, va, vw, vc,
-                                       stream);
+    return launch_gemm_cfg<64, 64, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                stream);
+  return launch_gemm_cfg<64, 32, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                              stream);
+}
+
+}  // namespace
+
+hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const float *W,
+                         const float *bias, int act, float *C, int64_t ldc, hipStream_t stream) {
+  const ASrc src{A, lda, nullptr, 0, K};
+  const bool va = aligned16(A) && lda % 4 == 0;
+  return launch_linear_src<false>(M, N, K, src, va, W, bias, act, C, ldc, stream);
+}
+
+hipError_t launch_linear_split(int M, int N, int K_lo, const float *A_lo, int64_t lda_lo,
+                               int K_hi, const float *A_hi, int64_t lda_hi, const float *W,
+                               const float *bias, int act, float *C, int64_t ldc,
+                               hipStream_t stream) {
+  const ASrc src{A_lo, lda_lo, A_hi, lda_hi, K_lo};
+  const bool va = aligned16(A_lo) && lda_lo % 4 == 0 && aligned16(A_hi) && lda_hi % 4 == 0 &&
+                  K_lo % 4 == 0;
+  return launch_linear_src<true>(M, N, K_lo + K_hi, src, va, W, bias, act, C, ldc, stream);
 }
 
 }  // namespace dlrm

@@ -222,6 +222,21 @@ DLRM_API int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, f
                                     float *emb_out, void *stream);
 
 /*
+ * dlrm_emb_interact_dots -- the fused gather + interaction writing only the
+ * dots, the (B, P) layout of the pages' stacked pairwise-dot kernel
+ * ([FASTPATHS] dlrm_interact.rs, PairwiseDotLowerTriStackedKernel output;
+ * the top MLP then reads the dense vector and the dots through a split A,
+ * see linear_bias_act_split):
+ *   dots[b, p] = dot(X_b[i], X_b[j]),  (i, j) = pair p,  X_b as above
+ *   bags     [host] the lookups (any dlrm_bags form)
+ *   dense    (B, D) float32, feature 0 (read, not copied)
+ *   dots     (B, P) float32 with row stride ld_dots >= P = F(F-1)/2
+ *   emb_out  NULL, or (B, K, D) float32 receiving the pooled vectors
+ */
+DLRM_API int dlrm_emb_interact_dots(const dlrm_bags *bags, const float *dense, float *dots,
+                                    int64_t ld_dots, float *emb_out, void *stream);
+
+/*
  * linear_bias_act -- fused linear layer ([FASTPATHS] matmul2d.rs, Activation
  * epilogue; linear_bias / linear_bias_relu / linear_bias_sigmoid):
  *
@@ -237,6 +252,30 @@ DLRM_API int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, f
 DLRM_API int linear_bias_act(int32_t m, int32_t n, int32_t k, const float *a,
                     int64_t lda, const float *w, const float *bias, int32_t act,
                     float *c, int64_t ldc, void *stream);
+
+/*
+ * linear_bias_act_split -- linear_bias_act whose input is the concatenation
+ * [a_lo | a_hi] of two matrices, read in place ([FASTPATHS] matmul2d.rs,
+ * a_split and the linear_bias / linear_bias_relu / linear_bias_sigmoid
+ * *_split_a frontends: the first top-MLP layer reads cat(dense, dots)):
+ *
+ *   c[m, n] = act(bias[n] + sum_{k < k_lo} a_lo[m, k] w[n, k]
+ *                         + sum_{k < k_hi} a_hi[m, k] w[n, k_lo + k])
+ *
+ *   m >= 0 (0: nothing to do), n >= 1, k_lo >= 1, k_hi >= 1
+ *   a_lo     (m, k_lo) float32 with row stride lda_lo >= k_lo
+ *   a_hi     (m, k_hi) float32 with row stride lda_hi >= k_hi
+ *   w        (n, k_lo + k_hi) float32, dense
+ *   bias     (n,) float32, or NULL
+ *   c        (m, n) float32 with row stride ldc >= n
+ * For n > 8 the k order of every sum is the one linear_bias_act uses on the
+ * concatenated matrix, so both give the same bits; for n <= 8 the order may
+ * differ (within float rounding).
+ */
+DLRM_API int linear_bias_act_split(int32_t m, int32_t n, int32_t k_lo, const float *a_lo,
+                                   int64_t lda_lo, int32_t k_hi, const float *a_hi,
+                                   int64_t lda_hi, const float *w, const float *bias, int32_t act,
+                                   float *c, int64_t ldc, void *stream);
 
 /* One MLP layer (of a dlrm_model or an mlp_forward stack). */
 typedef struct dlrm_layer {

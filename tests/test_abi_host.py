@@ -140,6 +140,27 @@ def test_emb_bag_pool_argument_errors(lib):
     assert fi(ctypes.byref(_bags(B=0, n=0)), None, None, None, None) == 0
 
 
+def test_split_and_dots_argument_errors(lib):
+    f = lib.linear_bias_act_split
+    #        m  n  klo a_lo  lda klo hi  lda   w  bias act  c  ldc stream
+    assert f(4, 0, 3, FAKE, 3, 5, FAKE, 5, FAKE, None, 0, FAKE, 2, None) == 2     # n < 1
+    assert f(4, 2, 0, FAKE, 3, 5, FAKE, 5, FAKE, None, 0, FAKE, 2, None) == 2     # k_lo < 1
+    assert f(4, 2, 3, FAKE, 3, 0, FAKE, 5, FAKE, None, 0, FAKE, 2, None) == 2     # k_hi < 1
+    assert f(4, 2, 3, FAKE, 2, 5, FAKE, 5, FAKE, None, 0, FAKE, 2, None) == 2     # lda_lo < k_lo
+    assert f(4, 2, 3, FAKE, 3, 5, FAKE, 4, FAKE, None, 0, FAKE, 2, None) == 2     # lda_hi < k_hi
+    assert f(4, 2, 3, FAKE, 3, 5, FAKE, 5, FAKE, None, 3, FAKE, 2, None) == 2     # bad act
+    assert f(4, 2, 3, None, 3, 5, FAKE, 5, FAKE, None, 0, FAKE, 2, None) == 1     # a_lo NULL
+    assert f(4, 2, 3, FAKE, 3, 5, None, 5, FAKE, None, 0, FAKE, 2, None) == 1     # a_hi NULL
+    assert f(0, 2, 3, None, 3, 5, None, 5, None, None, 0, None, 2, None) == 0     # m == 0
+    g = lib.dlrm_emb_interact_dots
+    ok = _bags(K=3)
+    assert g(None, FAKE, FAKE, 6, None, None) == 1
+    assert g(ctypes.byref(ok), FAKE, FAKE, 5, None, None) == 2          # ld_dots < P = 6
+    assert g(ctypes.byref(ok), None, FAKE, 6, None, None) == 1          # dense NULL
+    assert g(ctypes.byref(ok), FAKE, None, 6, None, None) == 1          # dots NULL
+    assert g(ctypes.byref(_bags(K=3, B=0, n=0)), None, None, 6, None, None) == 0
+
+
 def test_linear_argument_errors(lib):
     f = lib.linear_bias_act
     assert f(4, 0, 3, FAKE, 3, FAKE, None, 0, FAKE, 1, None) == 2     # n < 1
