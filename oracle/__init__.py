@@ -57,10 +57,12 @@ def load(path: str = None):
         ctypes.POINTER(_i32p), _i64p, _f32p]
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_fp8_e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_fp8_e4m3_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_emb_bag.argtypes = [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.POINTER(ctypes.c_void_p), _i64p, ctypes.POINTER(_i32p),
-        ctypes.POINTER(_i32p), ctypes.POINTER(_f32p), _i64p, ctypes.c_int32, _f32p]
+        ctypes.POINTER(_i32p), ctypes.POINTER(_f32p), _i64p, ctypes.c_int32, _f32p, _f32p]
     lib.oracle_interact.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     _f32p, _f32p, _f32p]
     lib.oracle_linear.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -175,14 +177,28 @@ def bf16_to_f32(bits, lib=None):
                     np.float32).reshape(bits.shape)
 
 
-def emb_bag(tables, indices, offsets=None, batch=None, weights=None, pool="sum",
+def fp8_e4m3_to_f64(codes, lib=None):
+    """float64 value of each uint8 FP8 E4M3 code (elementwise)."""
+    lib = lib or load()
+    codes = np.asarray(codes, np.uint8)
+    return np.array([lib.oracle_fp8_e4m3_to_f64(int(c)) for c in codes.ravel()],
+                    np.float64).reshape(codes.shape)
+
+
+_DTYPES = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.uint8): 2}
+
+
+def emb_bag(tables, indices, offsets=None, batch=None, weights=None, pool="sum", scales=None,
             lib=None):
     """Pooled (B, K, D) float32 with mean pooling, per-sample weights and
-    bfloat16 tables (tables given as uint16 bit patterns are bfloat16)."""
+    narrow table storage: uint16 tables hold bfloat16 bit patterns, uint8
+    tables FP8 E4M3 codes; scales (K,) multiplies each table's pooled value."""
     lib = lib or load()
     K = len(tables)
-    bf16 = tables[0].dtype == np.uint16
-    tables = [np.ascontiguousarray(t, np.uint16 if bf16 else np.float32) for t in tables]
+    dt = np.asarray(tables[0]).dtype
+    code = _DTYPES.get(dt, 0)
+    store = {0: np.float32, 1: np.uint16, 2: np.uint8}[code]
+    tables = [np.ascontiguousarray(t, store) for t in tables]
     indices = [_i32(i) for i in indices]
     D = tables[0].shape[1]
     if offsets is not None:
@@ -199,10 +215,12 @@ def emb_bag(tables, indices, offsets=None, batch=None, weights=None, pool="sum",
         weights = [_f32(w) if np.asarray(w).size else np.zeros(1, np.float32) for w in weights]
         w_ptrs = _ptr_array(weights, _f32p)
     out = np.empty((B, K, D), np.float32)
+    sc = _f32(scales) if scales is not None else None
     rc = lib.oracle_emb_bag(
-        K, B, D, 1 if bf16 else 0, tab_ptrs, _p(rows, _i64p), _ptr_array(idx_bufs, _i32p),
+        K, B, D, code, tab_ptrs, _p(rows, _i64p), _ptr_array(idx_bufs, _i32p),
         _ptr_array(offsets, _i32p) if offsets is not None else None, w_ptrs,
-        _p(n_idx, _i64p), POOLS[pool], _p(out, _f32p))
+        _p(n_idx, _i64p), POOLS[pool], _p(sc, _f32p) if sc is not None else None,
+        _p(out, _f32p))
     _check(rc, "emb_bag")
     return out
 

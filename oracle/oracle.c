@@ -117,6 +117,19 @@ float oracle_bf16_to_f32(uint16_t b) {
   return f;
 }
 
+double oracle_fp8_e4m3_to_f64(uint8_t c) {
+  const int sign = c >> 7;
+  const int expo = (c >> 3) & 15;
+  const int man = c & 7;
+  double v;
+  if (expo == 15 && man == 7) return NAN;
+  if (expo == 0)
+    v = ldexp((double)man, -9);             /* subnormal: (m / 8) x 2^(1 - 7) */
+  else
+    v = ldexp((double)(8 + man), expo - 10); /* (1 + m / 8) x 2^(e - 7) */
+  return sign ? -v : v;
+}
+
 /* The sum of oracle_emb_bag_sum with the two torch.nn.EmbeddingBag options
  * the pages' lowering rejects: mean pooling and per-sample weights, and with
  * bfloat16 table storage.  Every term is formed and summed in double. */
@@ -124,10 +137,12 @@ int oracle_emb_bag(int32_t K, int32_t B, int32_t D, int32_t table_dtype,
                    const void *const *tables, const int64_t *rows,
                    const int32_t *const *indices, const int32_t *const *offsets,
                    const float *const *weights, const int64_t *n_idx, int32_t pool,
-                   float *out) {
+                   const float *scales, float *out) {
   if (K < 1 || B < 1 || D < 1 || !tables || !rows || !indices || !n_idx || !out)
     return -1;
-  if (table_dtype != ORACLE_F32 && table_dtype != ORACLE_BF16) return -6;
+  if (table_dtype != ORACLE_F32 && table_dtype != ORACLE_BF16 &&
+      table_dtype != ORACLE_FP8_E4M3)
+    return -6;
   if (pool != ORACLE_POOL_SUM && pool != ORACLE_POOL_MEAN) return -6;
   if (weights && pool != ORACLE_POOL_SUM) return -6;
   for (int32_t k = 0; k < K; ++k) {
@@ -156,13 +171,18 @@ int oracle_emb_bag(int32_t K, int32_t B, int32_t D, int32_t table_dtype,
           int64_t r = idx[l];
           if (r < 0 || r >= rows[k]) return -2;
           int64_t e = r * (int64_t)D + d;
-          double v = table_dtype == ORACLE_BF16
-                         ? (double)oracle_bf16_to_f32(((const uint16_t *)tables[k])[e])
-                         : (double)((const float *)tables[k])[e];
+          double v;
+          if (table_dtype == ORACLE_BF16)
+            v = (double)oracle_bf16_to_f32(((const uint16_t *)tables[k])[e]);
+          else if (table_dtype == ORACLE_FP8_E4M3)
+            v = oracle_fp8_e4m3_to_f64(((const uint8_t *)tables[k])[e]);
+          else
+            v = (double)((const float *)tables[k])[e];
           double w = weights ? (double)weights[k][l] : 1.0;
           acc += w * v;
         }
         if (pool == ORACLE_POOL_MEAN && end > start) acc /= (double)(end - start);
+        if (scales) acc *= (double)scales[k];
         out[((int64_t)b * K + k) * D + d] = (float)acc;
       }
     }

@@ -68,11 +68,17 @@ int oracle_emb_bag_sum(int32_t K, int32_t B, int32_t D,
                        const int32_t *const *offsets, const int64_t *n_idx,
                        float *out);
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
 enum { ORACLE_POOL_SUM = 0, ORACLE_POOL_MEAN = 1 };
 
 /* bfloat16 (the upper 16 bits of an IEEE float32) to float32: exact. */
 float oracle_bf16_to_f32(uint16_t b);
+
+/* FP8 E4M3 as the OCP 8-bit floating point format defines it (the "fn"
+ * variant: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals at exponent 0, no infinities, S.1111.111 is NaN, largest finite
+ * 448) to double: exact. */
+double oracle_fp8_e4m3_to_f64(uint8_t c);
 
 /* Generalised EmbeddingBag pooling, the adjacent semantics of the pages'
  * sum-only kernel ([FASTPATHS] translator dispatch, _embedding_bag lowering:
@@ -82,13 +88,17 @@ float oracle_bf16_to_f32(uint16_t b);
  *   mean: out[b,k,:] = (sum over l in bag of row(idx[l])) / |bag|, 0 if empty
  * with w_l = weights[k][l] when weights is not NULL (sum only, as in torch),
  * else 1.  table_dtype ORACLE_BF16 means tables[k] holds uint16_t bfloat16
- * values, converted exactly to f32 before use.  Bags as in
+ * values, converted exactly to f32 before use; ORACLE_FP8_E4M3 means uint8_t
+ * FP8 E4M3 codes (oracle_fp8_e4m3_to_f64).  scales: NULL, or K per-table
+ * factors applied to the pooled value (out = scales[k] x pool(...)), which
+ * lets narrow storage hold tables of any magnitude.  Bags as in
  * oracle_emb_bag_sum.  Errors: as oracle_emb_bag_sum, and -6 for weights
  * with mean pooling or an unknown dtype or pool. */
 int oracle_emb_bag(int32_t K, int32_t B, int32_t D, int32_t table_dtype,
                    const void *const *tables, const int64_t *rows,
                    const int32_t *const *indices, const int32_t *const *offsets,
                    const float *const *weights, const int64_t *n_idx, int32_t pool,
+                   const float *scales,
                    float *out);
 
 /* Strict-lower-triangle pairwise-dot interaction ([FASTPATHS]

@@ -9,6 +9,10 @@ What pins what:
   emb-bag      numpy/torch float64 library routines (count-matrix product,
                torch embedding_bag), L=1 row copy, k identical indices == k*row,
                linearity, arange offsets == uniform stride, hand-worked CSR case
+  emb-bag fp8  the E4M3 format's fixed points (1, +-, smallest subnormal and
+               normal, 448, NaN), torch's float8_e4m3fn on all 256 codes, torch
+               float64 embedding_bag on decoded tables times per-table scales,
+               exact power-of-two scaling
   emb-bag ext  torch's bfloat16->float32 conversion on all 65536 patterns, torch
                float64 embedding_bag (mean; sum with per-sample weights; bf16
                tables), unit weights == sum, mean of copies == row, hand-worked
@@ -182,6 +186,47 @@ def pin_emb_bag_ext(lib):
     assert np.array_equal(got[:, 0], np.array(g["expected_weighted_sum"], np.float32))
 
 
+# -------------------------------------------- emb-bag: fp8 tables, scales --
+def pin_emb_bag_fp8(lib):
+    import torch
+    F = torch.nn.functional
+    # the format's own fixed points: 1.0, the smallest subnormal, the smallest
+    # normal, the largest finite value, signs, and the NaN code
+    spots = {0x38: 1.0, 0xB8: -1.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x7E: 448.0,
+             0x3C: 1.5, 0x00: 0.0, 0x07: 7 * 2.0 ** -9}
+    for c, v in spots.items():
+        assert oracle.fp8_e4m3_to_f64(np.array([c], np.uint8), lib=lib)[0] == v, hex(c)
+    assert np.isnan(oracle.fp8_e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8), lib=lib)).all()
+    # every code against torch's float8_e4m3fn
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.fp8_e4m3_to_f64(codes, lib=lib)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(mine, ref, equal_nan=True)
+    # pooled fp8 tables against torch float64 embedding_bag on the decoded values
+    rng = np.random.default_rng(31)
+    B, D, L = 6, 8, 3
+    rows = [11, 9]
+    finite = codes[(codes & 0x7F) != 0x7F]
+    tables = [rng.choice(finite, size=(r, D)).astype(np.uint8) for r in rows]
+    idx = [rng.integers(0, r, B * L).astype(np.int32) for r in rows]
+    wts = [rng.standard_normal(B * L).astype(np.float32) for _ in rows]
+    scales = np.array([0.25, 3.0], np.float32)
+    offs = torch.arange(0, B * L, L)
+    dec = [torch.from_numpy(oracle.fp8_e4m3_to_f64(t, lib=lib)) for t in tables]
+    for pool, w in (("sum", None), ("mean", None), ("sum", wts)):
+        got = oracle.emb_bag(tables, idx, batch=B, weights=w, pool=pool, scales=scales, lib=lib)
+        for k in range(2):
+            psw = torch.from_numpy(w[k].astype(np.float64)) if w is not None else None
+            want = F.embedding_bag(torch.from_numpy(idx[k].astype(np.int64)), dec[k], offs,
+                                   mode=pool, per_sample_weights=psw).numpy() * float(scales[k])
+            np.testing.assert_allclose(got[:, k], want, rtol=1e-6, atol=1e-6)
+    # a power-of-two scale multiplies the pooled value exactly
+    plain = oracle.emb_bag(tables, idx, batch=B, lib=lib)
+    scaled = oracle.emb_bag(tables, idx, batch=B, scales=np.array([0.5, 4.0], np.float32),
+                            lib=lib)
+    assert np.array_equal(scaled, plain * np.array([0.5, 4.0], np.float32)[None, :, None])
+
+
 # ------------------------------------------------------------- interaction --
 def pin_interact(lib):
     rng = np.random.default_rng(12)
@@ -318,5 +363,5 @@ def pin_forward(lib):
     assert np.array_equal(E, oracle.emb_bag_sum(tables, idx, batch=w.batch, lib=lib))
 
 
-ALL_PINS = (pin_pair_map, pin_emb_bag, pin_emb_bag_ext, pin_interact, pin_linear,
-            pin_forward)
+ALL_PINS = (pin_pair_map, pin_emb_bag, pin_emb_bag_ext, pin_emb_bag_fp8, pin_interact,
+            pin_linear, pin_forward)

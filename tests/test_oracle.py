@@ -23,6 +23,10 @@ def test_emb_bag_mean_weights_bf16(lib):
     oracle_pins.pin_emb_bag_ext(lib)
 
 
+def test_emb_bag_fp8_and_scales(lib):
+    oracle_pins.pin_emb_bag_fp8(lib)
+
+
 def test_interact(lib):
     oracle_pins.pin_interact(lib)
 

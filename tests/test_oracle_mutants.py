@@ -84,6 +84,18 @@ MUTANTS = {
     "bf16_wrong_shift": (
         "uint32_t bits = (uint32_t)b << 16;",
         "uint32_t bits = (uint32_t)b << 15;"),
+    "fp8_exponent_bias_8": (
+        "v = ldexp((double)(8 + man), expo - 10);",
+        "v = ldexp((double)(8 + man), expo - 11);"),
+    "fp8_subnormal_scale": (
+        "v = ldexp((double)man, -9);",
+        "v = ldexp((double)man, -10);"),
+    "fp8_no_nan_code": (
+        "if (expo == 15 && man == 7) return NAN;",
+        "if (expo == 16 && man == 7) return NAN;"),
+    "scale_dropped": (
+        "if (scales) acc *= (double)scales[k];",
+        "if (scales) acc *= 1.0;"),
     "pair_float_sqrt_no_fixups": (
         "  int64_t i = (int64_t)floor((1.0 + sqrt(1.0 + 8.0 * (double)p)) / 2.0);\n"
         "  while (i * (i - 1) / 2 > p) --i;\n"
