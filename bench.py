@@ -31,7 +31,7 @@ batch) per call, eager dlrm_forward against a graph-replayed plan, and
 (or HBM for the layers below the ridge point).
 
 Options: --workload {nc32,nc32-uniform,mid,tiny,large} (or one variant,
-nc32-bf16 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-variants,
+nc32-bf16 / nc32-fp8 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-variants,
 --no-cells,
 --sweep (batch x
 num_tables grid instead of the default line), --warm, --no-cpu-baseline,
@@ -88,7 +88,7 @@ def pool_bytes_per_sample(w, K, n_idx_per_sample):
     + per-sample weights + CSR offsets + dense + output."""
     F = K + 1
     P = F * (F - 1) // 2
-    row = w.dim * (2 if w.table_dtype == "bf16" else 4)
+    row = w.dim * {"f32": 4, "bf16": 2, "fp8": 1}[w.table_dtype]
     return (n_idx_per_sample * (row + 4 + (4 if w.weighted else 0))
             + (K * 4 if w.lengths != "fixed" else 0) + w.dim * 4 + (w.dim + P) * 4)
 
@@ -118,7 +118,9 @@ class PoolCase:
             idx_d = [torch.from_numpy(i).cuda() for i in idx]
             dense = torch.from_numpy(inputs.dense(w, sd)).cuda()
             out = torch.empty((self.B, w.out_width), dtype=torch.float32, device="cuda")
-            g = abi._BagsArg(self.tables, idx_d, offs, wts, w.pool, self.B)
+            sc = inputs.table_scale(w)
+            g = abi._BagsArg(self.tables, idx_d, offs, wts, w.pool, self.B,
+                             [sc] * self.K if sc else None)
             args = (ctypes.byref(g.struct), dense.data_ptr(), out.data_ptr(), None,
                     stream.cuda_stream)
             self.batches.append((g, dense, out, args))
@@ -575,14 +577,14 @@ def _rounds_time(fn, stream, warmup=10, rounds=5, per_round=20):
     return statistics.median(meds)
 
 
-VARIANTS = ("nc32-bf16", "nc32-mean", "nc32-weighted", "nc32-csr")
+VARIANTS = ("nc32-bf16", "nc32-fp8", "nc32-mean", "nc32-weighted", "nc32-csr")
 
 
 def bench_variants(args, stream, flush):
     """The fused gather + interaction of the general bag forms on the nc32
-    shape (B=2048, K=32 x 1,000,000 x D=64, Zipf(1.05)): bfloat16 tables,
-    mean pooling, per-sample weights, CSR bags of size 0..40; cold, through
-    dlrm_emb_interact_pool."""
+    shape (B=2048, K=32 x 1,000,000 x D=64, Zipf(1.05)): bfloat16 and FP8
+    E4M3 tables, mean pooling, per-sample weights, CSR bags of size 0..40;
+    cold, through dlrm_emb_interact_pool."""
     import torch
     from dlrm_embedding_bag_amd import inputs
     rows = []

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "DLRM_OK", 1: "DLRM_ERR_NULL", 2: "DLRM_ERR_SHAPE",
 ACTS = {"none": 0, "relu": 1, "sigmoid": 2}
 MAX_TABLES = 64
 MAX_DIM = 1024
-DTYPES = {"f32": 0, "bf16": 1}
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 POOLS = {"sum": 0, "mean": 1}
 PLAN_MODES = {"direct": 0, "graph": 1}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
@@ -54,7 +54,8 @@ class Bags(ctypes.Structure):
                 ("table_dtype", _i32), ("pool", _i32),
                 ("tables", ctypes.POINTER(_vp)), ("rows", ctypes.POINTER(_i64)),
                 ("indices", ctypes.POINTER(_vp)), ("offsets", ctypes.POINTER(_vp)),
-                ("n_idx", ctypes.POINTER(_i64)), ("weights", ctypes.POINTER(_vp))]
+                ("n_idx", ctypes.POINTER(_i64)), ("weights", ctypes.POINTER(_vp)),
+                ("scales", ctypes.POINTER(ctypes.c_float))]
 
 
 class Model(ctypes.Structure):
@@ -254,13 +255,14 @@ def dlrm_emb_interact(tables, indices, dense, offsets=None, out=None, emb_out=No
 class _BagsArg:
     """A dlrm_bags struct and the host arrays it points to (kept alive)."""
 
-    def __init__(self, tables, indices, offsets, weights, pool, batch):
+    def __init__(self, tables, indices, offsets, weights, pool, batch, scales=None):
         torch = _torch()
         if len(tables) == 0:
             raise ValueError("at least one table is required")
         dt = tables[0].dtype
-        if dt not in (torch.float32, torch.bfloat16):
-            raise TypeError("tables must be float32 or bfloat16")
+        codes = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
+        if dt not in codes:
+            raise TypeError("tables must be float32, bfloat16 or float8_e4m3fn")
         self.tables = [_dev(t, dt, f"tables[{k}]") for k, t in enumerate(tables)]
         self.indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
         if len(self.tables) != len(self.indices):
@@ -287,17 +289,23 @@ class _BagsArg:
                         _i64_array([i.numel() for i in self.indices]),
                         _ptr_array(self.weights) if self.weights is not None else None)
         tp, rows, ip, op, nidx, wp = self._arrays
-        self.struct = Bags(self.K, self.B, self.D, 1 if dt == torch.bfloat16 else 0,
-                           POOLS[pool], tp, rows, ip, op, nidx, wp)
+        self._scales = None
+        if scales is not None:
+            if len(scales) != self.K:
+                raise ValueError("scales must have one entry per table")
+            self._scales = (ctypes.c_float * self.K)(*[float(x) for x in scales])
+        self.struct = Bags(self.K, self.B, self.D, codes[dt], POOLS[pool], tp, rows, ip, op, nidx,
+                           wp, self._scales)
 
 
 def emb_bag_pool(tables, indices, offsets=None, weights=None, pool="sum", batch=None, out=None,
-                 stream=None):
-    """(B, K, D) float32 pooled bags of float32 or bfloat16 tables, sum or mean
-    pooling, optional per-sample weights; see include/dlrm_embedding_bag.h."""
+                 stream=None, scales=None):
+    """(B, K, D) float32 pooled bags of float32, bfloat16 or float8_e4m3fn
+    tables, sum or mean pooling, optional per-sample weights and per-table
+    scales; see include/dlrm_embedding_bag.h."""
     torch = _torch()
     lib = load()
-    g = _BagsArg(tables, indices, offsets, weights, pool, batch)
+    g = _BagsArg(tables, indices, offsets, weights, pool, batch, scales)
     if out is None:
         out = torch.empty((g.B, g.K, g.D), dtype=torch.float32, device=g.tables[0].device)
     _dev(out, torch.float32, "out")
@@ -309,12 +317,12 @@ def emb_bag_pool(tables, indices, offsets=None, weights=None, pool="sum", batch=
 
 
 def dlrm_emb_interact_pool(tables, indices, dense, offsets=None, weights=None, pool="sum",
-                           out=None, emb_out=None, stream=None):
+                           out=None, emb_out=None, stream=None, scales=None):
     """Fused gather + interaction over any dlrm_bags form: (B, D + F(F-1)/2)."""
     torch = _torch()
     lib = load()
     _dev(dense, torch.float32, "dense")
-    g = _BagsArg(tables, indices, offsets, weights, pool, dense.shape[0])
+    g = _BagsArg(tables, indices, offsets, weights, pool, dense.shape[0], scales)
     B, D = dense.shape
     if D != g.D:
         raise ValueError("dense must be (B, D)")
@@ -336,13 +344,13 @@ def dlrm_emb_interact_pool(tables, indices, dense, offsets=None, weights=None, p
 
 
 def dlrm_emb_interact_dots(tables, indices, dense, offsets=None, weights=None, pool="sum",
-                           out=None, emb_out=None, stream=None):
+                           out=None, emb_out=None, stream=None, scales=None):
     """Fused gather + interaction writing only the dots: (B, F(F-1)/2) float32
     (out may be a row-strided view with unit column stride)."""
     torch = _torch()
     lib = load()
     _dev(dense, torch.float32, "dense")
-    g = _BagsArg(tables, indices, offsets, weights, pool, dense.shape[0])
+    g = _BagsArg(tables, indices, offsets, weights, pool, dense.shape[0], scales)
     B, D = dense.shape
     if D != g.D:
         raise ValueError("dense must be (B, D)")

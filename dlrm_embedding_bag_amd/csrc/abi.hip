@@ -18,7 +18,8 @@
 using namespace dlrm;
 
 static_assert(DLRM_MAX_TABLES == kMaxTables, "table limit mismatch");
-static_assert(DLRM_F32 == kF32 && DLRM_BF16 == kBF16, "dtype codes mismatch");
+static_assert(DLRM_F32 == kF32 && DLRM_BF16 == kBF16 && DLRM_FP8_E4M3 == kFP8,
+              "dtype codes mismatch");
 
 namespace {
 
@@ -29,13 +30,17 @@ bool valid_act(int act) {
 int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Elements per 16-byte row chunk of a table type.
+int dtype_chunk(int dtype) { return dtype == kFP8 ? 16 : dtype == kBF16 ? 8 : 4; }
+
 // Validates the bag arguments shared by the gather entry points and packs
 // them into the by-value kernel argument.  gc.vec says whether the dim and
 // the tables allow the 16-byte chunk path (outputs are checked by the caller).
 int pack_bags(const dlrm_bags &g, TableSet &ts, GatherConfig &gc) {
   const int32_t K = g.num_tables, B = g.batch, D = g.dim;
   if (K < 1 || K > DLRM_MAX_TABLES || B < 0 || D < 1 || D > DLRM_MAX_DIM) return DLRM_ERR_SHAPE;
-  if (g.table_dtype != DLRM_F32 && g.table_dtype != DLRM_BF16) return DLRM_ERR_SHAPE;
+  if (g.table_dtype != DLRM_F32 && g.table_dtype != DLRM_BF16 && g.table_dtype != DLRM_FP8_E4M3)
+    return DLRM_ERR_SHAPE;
   if (g.pool != DLRM_POOL_SUM && g.pool != DLRM_POOL_MEAN) return DLRM_ERR_SHAPE;
   if (!g.tables || !g.rows || !g.indices || !g.n_idx) return DLRM_ERR_NULL;
   if (g.weights && g.pool != DLRM_POOL_SUM) return DLRM_ERR_UNSUPPORTED;
@@ -43,8 +48,9 @@ int pack_bags(const dlrm_bags &g, TableSet &ts, GatherConfig &gc) {
   gc.dtype = g.table_dtype;
   gc.csr = g.offsets != nullptr;
   gc.psw = g.weights != nullptr;
-  gc.vec = (D % (g.table_dtype == DLRM_BF16 ? 8 : 4)) == 0;
+  gc.vec = (D % dtype_chunk(g.table_dtype)) == 0;
   ts.mean = g.pool == DLRM_POOL_MEAN;
+  ts.scaled = g.scales != nullptr;
   for (int k = 0; k < K; ++k) {
     if (!g.tables[k]) return DLRM_ERR_NULL;
     if (g.rows[k] < 1 || g.n_idx[k] < 0 || g.n_idx[k] > INT32_MAX) return DLRM_ERR_SHAPE;
@@ -61,6 +67,7 @@ int pack_bags(const dlrm_bags &g, TableSet &ts, GatherConfig &gc) {
     ts.wt[k] = gc.psw ? g.weights[k] : nullptr;
     ts.bag[k] = (!gc.csr && B > 0) ? (int32_t)(g.n_idx[k] / B) : 0;
     ts.nidx[k] = (int32_t)g.n_idx[k];
+    ts.scale[k] = g.scales ? g.scales[k] : 1.0f;
     gc.vec = gc.vec && aligned16(g.tables[k]);
   }
   return DLRM_OK;
@@ -82,10 +89,11 @@ dlrm_bags f32_sum_bags(int32_t K, int32_t B, int32_t D, const float *const *tabl
   g.offsets = offsets;
   g.n_idx = n_idx;
   g.weights = nullptr;
+  g.scales = nullptr;
   return g;
 }
 
-int chunk_elems(const GatherConfig &gc) { return gc.vec ? (gc.dtype == kBF16 ? 8 : 4) : 1; }
+int chunk_elems(const GatherConfig &gc) { return gc.vec ? dtype_chunk(gc.dtype) : 1; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DLRM_OK : DLRM_ERR_HIP; }
 

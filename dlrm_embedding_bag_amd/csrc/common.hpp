@@ -14,19 +14,21 @@ constexpr int kWave = 64;
 constexpr size_t kLdsBudget = 64 * 1024;  // dynamic LDS per workgroup we allow
 
 // Table storage types (values of dlrm_dtype).
-enum { kF32 = 0, kBF16 = 1 };
+enum { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
 // Per-table device pointers and bag geometry, passed to the kernels by value
-// in the kernel-argument segment (2.5 KiB), so a call needs no host-to-device
+// in the kernel-argument segment (2.8 KiB), so a call needs no host-to-device
 // copy of a pointer table.
 struct TableSet {
-  const void *table[kMaxTables];   // float32 or bfloat16 rows, per the kernel's type
+  const void *table[kMaxTables];   // float32, bfloat16 or fp8 rows, per the kernel's type
   const int32_t *idx[kMaxTables];
   const int32_t *off[kMaxTables];  // CSR bag starts; unused in uniform mode
   const float *wt[kMaxTables];     // per-sample weights (n_idx,); used by weighted kernels
   int32_t bag[kMaxTables];         // L_k, uniform mode
   int32_t nidx[kMaxTables];        // number of indices of table k
+  float scale[kMaxTables];         // per-table factor on the pooled value
   int32_t mean;                    // divide every non-empty bag's sum by its size
+  int32_t scaled;                  // apply scale[]
 };
 
 template <int VW>

@@ -149,7 +149,12 @@ static void dispatch_flags(bool csr, bool psw, int gs, Fn &&fn) {
 template <typename Fn>
 static void dispatch_gather(const GatherConfig &gc, int D, Fn &&fn) {
   const int gs = gc.vec ? shuffle_group(D / chunk_elems(gc.dtype, true)) : 0;
-  if (gc.dtype == kBF16) {
+  if (gc.dtype == kFP8) {
+    if (gc.vec)
+      dispatch_flags<uint8_t, 4>(gc.csr, gc.psw, gs, fn);
+    else
+      dispatch_flags<uint8_t, 1>(gc.csr, gc.psw, gs, fn);
+  } else if (gc.dtype == kBF16) {
     if (gc.vec)
       dispatch_flags<uint16_t, 4>(gc.csr, gc.psw, gs, fn);
     else

@@ -53,11 +53,16 @@ namespace dlrm {
 #ifndef DLRM_GATHER_ROUND_BF16
 #define DLRM_GATHER_ROUND_BF16 12
 #endif
+#ifndef DLRM_GATHER_ROUND_FP8
+#define DLRM_GATHER_ROUND_FP8 8
+#endif
 
 constexpr int kUnroll = 8;  // generic path: loads in flight per lane
 // Shuffle path: row loads in flight per lane, by table storage type.
 template <typename TT>
-constexpr int kRound = sizeof(TT) == 2 ? DLRM_GATHER_ROUND_BF16 : DLRM_GATHER_ROUND;
+constexpr int kRound = sizeof(TT) == 1   ? DLRM_GATHER_ROUND_FP8
+                       : sizeof(TT) == 2 ? DLRM_GATHER_ROUND_BF16
+                                         : DLRM_GATHER_ROUND;
 
 __device__ __forceinline__ void store_unaligned(float *p, float4 v) {
   p[0] = v.x;
@@ -161,6 +166,54 @@ struct RowChunk<uint16_t, 1> {
   }
 };
 
+// FP8 E4M3 (the OCP "fn" encoding) codes, decoded by the hardware
+// conversion, which yields the exact value of each code: bytes 0-1 of a
+// 32-bit word with word_sel false, bytes 2-3 with true.
+template <>
+struct RowChunk<uint8_t, 4> {
+  using Raw = uint4;
+  static constexpr int EL = 16;
+  static __device__ __forceinline__ Raw zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  static __device__ __forceinline__ void add(float *a, Raw r) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      a[4 * i] += lo[0];
+      a[4 * i + 1] += lo[1];
+      a[4 * i + 2] += hi[0];
+      a[4 * i + 3] += hi[1];
+    }
+  }
+  static __device__ __forceinline__ void fma(float *a, float wt, Raw r) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+      a[4 * i] = __builtin_fmaf(wt, lo[0], a[4 * i]);
+      a[4 * i + 1] = __builtin_fmaf(wt, lo[1], a[4 * i + 1]);
+      a[4 * i + 2] = __builtin_fmaf(wt, hi[0], a[4 * i + 2]);
+      a[4 * i + 3] = __builtin_fmaf(wt, hi[1], a[4 * i + 3]);
+    }
+  }
+};
+
+template <>
+struct RowChunk<uint8_t, 1> {
+  using Raw = uint8_t;
+  static constexpr int EL = 1;
+  static __device__ __forceinline__ Raw zero() { return 0; }
+  static __device__ __forceinline__ float val(Raw r) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)r, false)[0];
+  }
+  static __device__ __forceinline__ void add(float *a, Raw r) { a[0] += val(r); }
+  static __device__ __forceinline__ void fma(float *a, float w, Raw r) {
+    a[0] = __builtin_fmaf(w, val(r), a[0]);
+  }
+};
+
 // Stores chunk c (EL floats) of a float32 row.
 template <int EL>
 __device__ __forceinline__ void store_chunk(float *row, int c, const float *a) {
@@ -169,9 +222,10 @@ __device__ __forceinline__ void store_chunk(float *row, int c, const float *a) {
   } else if constexpr (EL == 4) {
     reinterpret_cast<float4 *>(row)[c] = make_float4(a[0], a[1], a[2], a[3]);
   } else {
-    float4 *p = reinterpret_cast<float4 *>(row) + 2 * c;
-    p[0] = make_float4(a[0], a[1], a[2], a[3]);
-    p[1] = make_float4(a[4], a[5], a[6], a[7]);
+    float4 *p = reinterpret_cast<float4 *>(row) + (EL / 4) * c;
+#pragma unroll
+    for (int q = 0; q < EL / 4; ++q)
+      p[q] = make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
   }
 }
 
@@ -303,6 +357,11 @@ __device__ __forceinline__ void pool_bag(const TableSet &ts, int k, int b, int B
       const float n = (float)(be - bs);
 #pragma unroll
       for (int i = 0; i < EL; ++i) acc[i] = acc[i] / n;
+    }
+    if (ts.scaled) {
+      const float sc = ts.scale[k];
+#pragma unroll
+      for (int i = 0; i < EL; ++i) acc[i] *= sc;
     }
     store_chunk<EL>(row, c, acc);
     if (eo) store_chunk<EL>(eo, c, acc);
@@ -457,6 +516,8 @@ inline int lanes_per_row(int D, int el) {
 
 // Elements per row chunk: 4 (float32) or 8 (bfloat16) on the vector path, 1
 // on the scalar path.
-inline int chunk_elems(int dtype, bool vec) { return vec ? (dtype == kBF16 ? 8 : 4) : 1; }
+inline int chunk_elems(int dtype, bool vec) {
+  return vec ? (dtype == kFP8 ? 16 : dtype == kBF16 ? 8 : 4) : 1;
+}
 
 }  // namespace dlrm

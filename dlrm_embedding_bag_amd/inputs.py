@@ -12,7 +12,10 @@ Recipe (every stream is seeded from a base seed and a fixed stream number):
   weights of k   stream 5000 + k   per-sample weights, U[0, 1) float32
   lengths of k   stream 6000 + k   CSR bag sizes, uniform integers on [0, 2L]
 bfloat16 tables keep the high 16 bits of the float32 draw (truncation), as
-bit patterns (uint16 on the host, torch.bfloat16 on the device).
+bit patterns (uint16 on the host, torch.bfloat16 on the device).  FP8 E4M3
+tables hold the draw divided by FP8_SCALE = 2^-8, rounded to the nearest
+E4M3 value by torch's float8_e4m3fn conversion (uint8 codes on the host,
+torch.float8_e4m3fn on the device), and are pooled with that scale.
 CSR workloads draw one bag size per (sample, table), mean L, empty bags
 included; the indices of table k then number the sum of its sizes and the
 offsets are the exclusive prefix sums of the sizes.
@@ -54,7 +57,7 @@ class Workload:
     bottom: tuple = ()             # bottom MLP widths after dense_in
     top: tuple = ()                # top MLP widths after the interaction
     table_source: str = "host"     # "host" (numpy) or "device" (torch CUDA)
-    table_dtype: str = "f32"       # "f32" or "bf16" table storage
+    table_dtype: str = "f32"       # "f32", "bf16" or "fp8" (E4M3) table storage
     pool: str = "sum"              # "sum" or "mean"
     weighted: bool = False         # per-sample weights (sum only)
     lengths: str = "fixed"         # "fixed" (L per bag) or "uniform" (0..2L, CSR)
@@ -101,6 +104,10 @@ WORKLOADS = {
         "nc32-bf16", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
         dist="zipf", table_source="device", table_dtype="bf16",
         description="nc32 with bfloat16 tables (128-byte rows)"),
+    "nc32-fp8": Workload(
+        "nc32-fp8", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
+        dist="zipf", table_source="device", table_dtype="fp8",
+        description="nc32 with FP8 E4M3 tables (64-byte rows, scale 2^-8)"),
     "nc32-mean": Workload(
         "nc32-mean", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
         dist="zipf", table_source="device", pool="mean",
@@ -237,10 +244,30 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (x.view(np.uint32) >> 16).astype(np.uint16)
 
 
+FP8_SCALE = 2.0 ** -8
+
+
+def table_scale(w: Workload):
+    """Per-table scale of the workload's storage (None: no scaling)."""
+    return FP8_SCALE if w.table_dtype == "fp8" else None
+
+
+def fp8_codes(x: np.ndarray) -> np.ndarray:
+    """uint8 FP8 E4M3 codes of x / FP8_SCALE (torch's float8_e4m3fn rounding)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32) / np.float32(FP8_SCALE))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def table_host_typed(w: Workload, table: int, seed: int = 0, rows: int = None) -> np.ndarray:
-    """table_host in the workload's storage type (uint16 bit patterns for bf16)."""
+    """table_host in the workload's storage type (uint16 bit patterns for bf16,
+    uint8 codes for fp8)."""
     t = table_host(w, table, seed, rows)
-    return bf16_bits(t) if w.table_dtype == "bf16" else t
+    if w.table_dtype == "bf16":
+        return bf16_bits(t)
+    if w.table_dtype == "fp8":
+        return fp8_codes(t)
+    return t
 
 
 def table_device_typed(w: Workload, table: int, seed: int = 0, device="cuda",
@@ -248,6 +275,8 @@ def table_device_typed(w: Workload, table: int, seed: int = 0, device="cuda",
     """table_device in the workload's storage type (torch.bfloat16 for bf16)."""
     import torch
     t = table_device(w, table, seed, device, rows)
+    if w.table_dtype == "fp8":
+        return t.div_(FP8_SCALE).to(torch.float8_e4m3fn)
     if w.table_dtype != "bf16":
         return t
     return (t.view(torch.int32) >> 16).to(torch.int16).view(torch.bfloat16)

@@ -147,8 +147,10 @@ DLRM_API int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
 
 /* Storage type of embedding-table rows. */
 typedef enum dlrm_dtype {
-  DLRM_F32 = 0,  /* IEEE float32                                            */
-  DLRM_BF16 = 1  /* bfloat16: the high 16 bits of a float32, widened exactly */
+  DLRM_F32 = 0,      /* IEEE float32                                          */
+  DLRM_BF16 = 1,     /* bfloat16: the high 16 bits of a float32, widened exactly */
+  DLRM_FP8_E4M3 = 2  /* OCP FP8 E4M3 ("fn": bias 7, subnormals, no infinities,
+                        S.1111.111 NaN, max 448), one byte, decoded exactly   */
 } dlrm_dtype;
 
 /* How a bag's rows are combined (the modes of torch.nn.EmbeddingBag). */
@@ -175,6 +177,9 @@ typedef enum dlrm_pool {
  *                per_sample_weights of torch.nn.EmbeddingBag); sum pooling
  *                only (with DLRM_POOL_MEAN it is DLRM_ERR_UNSUPPORTED, as in
  *                torch)
+ *   scales       NULL, or [host] K float32 factors: table k's pooled value is
+ *                multiplied by scales[k] (what lets fp8 storage hold tables
+ *                of any magnitude: store w / scale, get scale x pool)
  *
  * Pooling ([FASTPATHS] translator dispatch, aten._embedding_bag lowering:
  * the pages' path takes sum mode only and rejects per-sample weights; the
@@ -182,10 +187,11 @@ typedef enum dlrm_pool {
  *   sum   out[b, k, :] = sum_{l in bag(b,k)} w_l * row(tables[k], indices[k][l])
  *         with w_l = weights[k][l], or 1 without weights
  *   mean  out[b, k, :] = (sum_{l in bag(b,k)} row(...)) / |bag(b,k)|, 0 if empty
- * Rows of bfloat16 tables are widened to float32 exactly; accumulation is
- * float32 in bag order.
- * The vector path needs dim % 4 == 0 (float32) or dim % 8 == 0 (bfloat16)
- * and 16-byte aligned tables and outputs; anything else takes the scalar path.
+ * Rows of bfloat16 and fp8 tables are widened to float32 exactly;
+ * accumulation is float32 in bag order, then mean and scale.
+ * The vector path needs 16-byte rows chunks (dim % 4 == 0 for float32, 8 for
+ * bfloat16, 16 for fp8) and 16-byte aligned tables and outputs; anything else
+ * takes the scalar path.
  */
 typedef struct dlrm_bags {
   int32_t num_tables;
@@ -199,6 +205,7 @@ typedef struct dlrm_bags {
   const int32_t *const *offsets;
   const int64_t *n_idx;
   const float *const *weights;
+  const float *scales;
 } dlrm_bags;
 
 /*

@@ -58,10 +58,13 @@ def sampled_subproblem(tables_dev, idx_host, bag, samples):
 
 
 def host_table(t):
-    """Host copy of a device table: float32, or uint16 bit patterns for bfloat16."""
+    """Host copy of a device table: float32, uint16 bit patterns for bfloat16,
+    uint8 codes for float8_e4m3fn."""
     import torch
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
     return host(t)
 
 

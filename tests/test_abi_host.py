@@ -117,7 +117,7 @@ def test_emb_bag_pool_argument_errors(lib):
     f = lib.emb_bag_pool
     ok = _bags()
     assert f(None, FAKE, None) == 1                                     # bags NULL
-    assert f(ctypes.byref(_bags(dtype=2)), FAKE, None) == 2             # unknown dtype
+    assert f(ctypes.byref(_bags(dtype=3)), FAKE, None) == 2             # unknown dtype
     assert f(ctypes.byref(_bags(pool=2)), FAKE, None) == 2              # unknown pool
     assert f(ctypes.byref(_bags(pool=1, weights=True)), FAKE, None) == 3  # mean + weights
     assert f(ctypes.byref(_bags(n=7)), FAKE, None) == 2                 # n_idx % B

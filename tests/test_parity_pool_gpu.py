@@ -1,9 +1,11 @@
 """GPU parity of the general EmbeddingBag forms (emb_bag_pool and
-dlrm_emb_interact_pool): bfloat16 tables, mean pooling, per-sample weights,
-CSR bags of any size, against the CPU oracle on the same seeded inputs.
+dlrm_emb_interact_pool): bfloat16 and FP8 E4M3 tables with per-table scales,
+mean pooling, per-sample weights, CSR bags of any size, against the CPU oracle
+on the same seeded inputs.
 
 Sums and weighted sums of dyadic values are exact in any order, so they are
-compared bit for bit (bfloat16 holds these dyadic values exactly); mean
+compared bit for bit (bfloat16 holds these dyadic values exactly, and the fp8
+cases draw codes whose sums stay exact); mean
 pooling divides once more and is held to |gpu - oracle| <= 1e-5 + 1e-5
 |oracle|, as are the random-valued cases.  The small cases span several
 workgroups, ragged batches and every row-chunk path (16-byte shuffle groups
@@ -25,17 +27,34 @@ def _bf16_dev(bits):
     return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
 
 
+def _fp8_dev(codes):
+    import torch
+    return torch.from_numpy(codes).cuda().view(torch.float8_e4m3fn)
+
+
+# E4M3 codes with exponent field 4..11: values 2^-3 .. 30, multiples of 2^-6.
+# With weights n/256 (|n| < 16) and up to ~60 terms every partial sum stays
+# below 2^24 units of 2^-14, so sums and weighted sums are exact in float32.
+_EXACT_FP8 = np.array([c for c in range(256) if 4 <= ((c >> 3) & 15) <= 11], np.uint8)
+
+
 def _case(B, K, rows, D, L, dtype, csr, weighted, seed, dyadic=True):
     """Host tables (float32 or uint16 bf16 bits), indices, offsets, weights."""
     rng = np.random.default_rng(seed)
     m = inputs.dyadic_max_int(D, L)
     tables, idx, offs, wts = [], [], [], []
     for k in range(K):
-        if dyadic:
-            t = inputs.dyadic(rng, (rows, D), max_int=m)
+        if dtype == "fp8":
+            if dyadic:
+                tables.append(rng.choice(_EXACT_FP8, size=(rows, D)))
+            else:   # the workloads' tables: N(0, 0.01^2) encoded at scale 2^-8
+                tables.append(inputs.fp8_codes(rng.standard_normal((rows, D)) * 0.01))
         else:
-            t = (rng.standard_normal((rows, D)) * 0.1).astype(np.float32)
-        tables.append(inputs.bf16_bits(t) if dtype == "bf16" else t)
+            if dyadic:
+                t = inputs.dyadic(rng, (rows, D), max_int=m)
+            else:
+                t = (rng.standard_normal((rows, D)) * 0.1).astype(np.float32)
+            tables.append(inputs.bf16_bits(t) if dtype == "bf16" else t)
         if csr:
             lens = rng.integers(0, 2 * L + 1, size=B)
             lens[0] = 0                       # an empty first bag
@@ -54,14 +73,21 @@ def _case(B, K, rows, D, L, dtype, csr, weighted, seed, dyadic=True):
 
 
 def _dev_tables(tables):
-    return [_bf16_dev(t) if t.dtype == np.uint16 else dev(t) for t in tables]
+    return [_bf16_dev(t) if t.dtype == np.uint16 else _fp8_dev(t) if t.dtype == np.uint8
+            else dev(t) for t in tables]
 
 
-def _gpu_pool(tables, idx, offs, wts, pool, B):
+def _scales(dtype, K):
+    """Per-table scales for fp8 tables: powers of two, so scaling is exact."""
+    return [2.0 ** (-(k % 5) - 4) for k in range(K)] if dtype == "fp8" else None
+
+
+def _gpu_pool(tables, idx, offs, wts, pool, B, scales=None):
     return host(abi.emb_bag_pool(
         _dev_tables(tables), [dev(i) for i in idx],
         offsets=[dev(o) for o in offs] if offs is not None else None,
-        weights=[dev(w) for w in wts] if wts is not None else None, pool=pool, batch=B))
+        weights=[dev(w) for w in wts] if wts is not None else None, pool=pool, batch=B,
+        scales=scales))
 
 
 POOL_SHAPES = [  # (B, K, rows, D, L)
@@ -73,11 +99,14 @@ POOL_SHAPES = [  # (B, K, rows, D, L)
     (6, 2, 20, 256, 9),       # bf16: 32 lanes; f32: a full wave
     (3, 2, 10, 1024, 3),      # bf16: 128 chunks, 64 lanes
     (4, 3, 25, 24, 2),        # bf16: 3 chunks per row
-    (5, 64, 10, 32, 1),       # maximum K
+    (5, 64, 10, 32, 1),       # maximum K; fp8: 2 chunks per row
+    (8, 3, 40, 48, 6),        # fp8: 3 chunks per row (generic vector path)
+    (6, 2, 30, 128, 4),       # fp8: 8 lanes per row
 ]
 FORMS = [  # (dtype, pool, weighted)
     ("f32", "sum", False), ("f32", "mean", False), ("f32", "sum", True),
     ("bf16", "sum", False), ("bf16", "mean", False), ("bf16", "sum", True),
+    ("fp8", "sum", False), ("fp8", "mean", False), ("fp8", "sum", True),
 ]
 
 
@@ -87,8 +116,9 @@ FORMS = [  # (dtype, pool, weighted)
 def test_pool_forms(B, K, rows, D, L, dtype, pool, weighted, csr):
     tables, idx, offs, wts = _case(B, K, rows, D, L, dtype, csr, weighted,
                                    seed=B * 31 + K + D)
-    want = oracle.emb_bag(tables, idx, offs, batch=B, weights=wts, pool=pool)
-    got = _gpu_pool(tables, idx, offs, wts, pool, B)
+    sc = _scales(dtype, K)
+    want = oracle.emb_bag(tables, idx, offs, batch=B, weights=wts, pool=pool, scales=sc)
+    got = _gpu_pool(tables, idx, offs, wts, pool, B, scales=sc)
     if pool == "sum":
         assert np.array_equal(got, want), "dyadic sums are exact in any order"
     else:
@@ -102,9 +132,10 @@ def test_pool_forms_random_values(dtype, pool, weighted):
     B, K, rows, D, L = 257, 6, 5000, 64, 20
     tables, idx, offs, wts = _case(B, K, rows, D, L, dtype, True, weighted, seed=5,
                                    dyadic=False)
-    want = oracle.emb_bag(tables, idx, offs, batch=B, weights=wts, pool=pool)
-    got = _gpu_pool(tables, idx, offs, wts, pool, B)
-    assert_close(got, want, f"{dtype} {pool} weighted={weighted}")
+    sc = [0.3 + 0.1 * k for k in range(K)]          # any per-table scale, any storage
+    want = oracle.emb_bag(tables, idx, offs, batch=B, weights=wts, pool=pool, scales=sc)
+    got = _gpu_pool(tables, idx, offs, wts, pool, B, scales=sc)
+    assert_close(got, want, f"{dtype} {pool} weighted={weighted} scaled")
 
 
 def test_f32_sum_form_is_emb_bag_sum_multi():
@@ -167,13 +198,14 @@ def test_fused_pool_forms(B, K, rows, D, L, dtype, pool, weighted):
     tables, idx, offs, wts = _case(B, K, rows, D, L, dtype, True, weighted, seed=B + 7 * K,
                                    dyadic=False)
     dense = np.random.default_rng(B).standard_normal((B, D)).astype(np.float32)
-    E = oracle.emb_bag(tables, idx, offs, weights=wts, pool=pool)
+    sc = [2.0 ** -6] * K if dtype == "fp8" else None
+    E = oracle.emb_bag(tables, idx, offs, weights=wts, pool=pool, scales=sc)
     want = oracle.interact(dense, E)
     emb_out = torch.empty((B, K, D), device="cuda")
     got = host(abi.dlrm_emb_interact_pool(
         _dev_tables(tables), [dev(i) for i in idx], dev(dense),
         offsets=[dev(o) for o in offs], weights=[dev(w) for w in wts] if wts else None,
-        pool=pool, emb_out=emb_out))
+        pool=pool, emb_out=emb_out, scales=sc))
     assert_close(got, want, f"fused {dtype} {pool}")
     assert np.array_equal(got[:, :D], dense)
     assert_close(host(emb_out), E, "pooled copy")
@@ -190,7 +222,8 @@ def _full_inputs(w):
     return tables, idx, offs, wts
 
 
-@pytest.mark.parametrize("name", ["nc32-bf16", "nc32-mean", "nc32-weighted", "nc32-csr"])
+@pytest.mark.parametrize("name", ["nc32-bf16", "nc32-fp8", "nc32-mean", "nc32-weighted",
+                                  "nc32-csr"])
 def test_full_size_variants_sampled(name):
     """The benchmark's fused launch of each variant workload on the full batch
     (B=2048, K=32 tables x 1,000,000 rows x D=64); sampled rows vs the oracle,
@@ -201,17 +234,20 @@ def test_full_size_variants_sampled(name):
     tables, idx, offs, wts = _full_inputs(w)
     dense = inputs.dense(w)
     out = torch.empty((w.batch, w.out_width), device="cuda")
+    sc = [inputs.table_scale(w)] * w.num_tables if inputs.table_scale(w) else None
     abi.dlrm_emb_interact_pool(
         tables, [dev(i) for i in idx], dev(dense),
         offsets=[dev(o) for o in offs] if offs is not None else None,
-        weights=[dev(x) for x in wts] if wts is not None else None, pool=w.pool, out=out)
+        weights=[dev(x) for x in wts] if wts is not None else None, pool=w.pool, out=out,
+        scales=sc)
     got = host(out)
     assert np.all(np.isfinite(got))
     assert np.array_equal(got[:, :w.dim], dense)
     samples = sample_rows(w.batch, 48, seed=len(name))
     st, si, so, sw = sampled_bags(tables, idx, samples, bag=w.bag, offsets_host=offs,
                                   weights_host=wts)
-    want = oracle.interact(dense[samples], oracle.emb_bag(st, si, so, weights=sw, pool=w.pool))
+    want = oracle.interact(dense[samples],
+                           oracle.emb_bag(st, si, so, weights=sw, pool=w.pool, scales=sc))
     assert_close(got[samples], want, f"{name} sampled")
     del tables, out
     torch.cuda.synchronize()
