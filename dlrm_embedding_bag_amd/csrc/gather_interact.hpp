@@ -53,6 +53,9 @@ namespace dlrm {
 #ifndef DLRM_GATHER_ROUND_BF16
 #define DLRM_GATHER_ROUND_BF16 12
 #endif
+#ifndef DLRM_IDX_PREFETCH
+#define DLRM_IDX_PREFETCH 1
+#endif
 #ifndef DLRM_GATHER_ROUND_FP8
 #define DLRM_GATHER_ROUND_FP8 8
 #endif
@@ -295,21 +298,29 @@ __device__ __forceinline__ void pool_group(const TT *__restrict__ tab,
                                            int c_lane, int c, int gbase, float *acc) {
   using RC = RowChunk<TT, 4>;
   using Raw = typename RC::Raw;
-  constexpr int R = kRound<TT>;
+  // (weighted bf16 rows over 4-lane groups keep 8 rows in flight: 12 would
+  // not fit the registers beside the prefetched indices and weights)
+  constexpr int R = (PSW && G == 4 && sizeof(TT) == 2) ? 8 : kRound<TT>;
   constexpr int T = (R + G - 1) / G;  // index registers per lane
   const Raw *col = reinterpret_cast<const Raw *>(tab) + c;
 #pragma unroll
   for (int i = 0; i < RC::EL; ++i) acc[i] = 0.f;
-  for (int l0 = s; l0 < e; l0 += R) {
+  // Indices (and weights) of the round starting at l0: lane c_lane loads
+  // positions c_lane, c_lane + G, ... of the round.
+  int mine[T];
+  float mine_w[T];
+  auto load_round = [&](int l0) {
     const int n = min(R, e - l0);
-    int mine[T];
-    float mine_w[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int l = c_lane + G * t;
       mine[t] = (l < n) ? idx[l0 + l] : 0;
       mine_w[t] = (PSW && l < n) ? wt[l0 + l] : 0.f;
     }
+  };
+  if (s < e) load_round(s);
+  for (int l0 = s; l0 < e; l0 += R) {
+    const int n = min(R, e - l0);
     Raw v[R];
     float w[R];
 #pragma unroll
@@ -329,9 +340,17 @@ __device__ __forceinline__ void pool_group(const TT *__restrict__ tab,
       v[u] = (u < n) ? col[(size_t)(uint32_t)r * (size_t)nvec] : RC::zero();
 #endif
     }
+#if DLRM_IDX_PREFETCH
+    // The next round's indices go out behind this round's rows, so their
+    // latency overlaps the rows' instead of adding to it.
+    if (l0 + R < e) load_round(l0 + R);
+#endif
 #pragma unroll
     for (int u = 0; u < R; ++u)
       if (u < n) accumulate<RC, PSW>(acc, w[u], v[u]);
+#if !DLRM_IDX_PREFETCH
+    if (l0 + R < e) load_round(l0 + R);
+#endif
   }
 }
 
