@@ -198,6 +198,7 @@ LINEAR_SHAPES = [  # (M, N, K)
     (300, 512, 13), (300, 256, 512), (300, 64, 256), (300, 512, 415), (300, 256, 512),
     (300, 1, 256), (37, 19, 13), (129, 130, 131), (64, 8, 5), (1, 1, 1), (5, 9, 3),
     (257, 128, 64), (70, 3, 40), (513, 72, 36),
+    (33, 22, 16), (40, 2, 600), (2000, 516, 16), (77, 4, 512),
 ]
 
 
