@@ -47,7 +47,7 @@ namespace dlrm {
 #define DLRM_ROW_NT 0
 #endif
 #ifndef DLRM_MIN_THREADS
-#define DLRM_MIN_THREADS 256
+#define DLRM_MIN_THREADS 128
 #endif
 
 #ifndef DLRM_GATHER_ROUND_BF16
