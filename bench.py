@@ -117,7 +117,13 @@ class PoolCase:
                     for k in range(self.K)] if w.weighted else None)
             idx_d = [torch.from_numpy(i).cuda() for i in idx]
             dense = torch.from_numpy(inputs.dense(w, sd)).cuda()
-            out = torch.empty((self.B, w.out_width), dtype=torch.float32, device="cuda")
+            # the interaction reads B dense rows of D floats
+            if tuple(dense.shape) != (self.B, w.dim):
+                raise ValueError(f"dense input {tuple(dense.shape)} is not (B, D) = "
+                                 f"{(self.B, w.dim)}")
+            F = self.K + 1
+            out = torch.empty((self.B, w.dim + F * (F - 1) // 2), dtype=torch.float32,
+                              device="cuda")
             sc = inputs.table_scale(w)
             g = abi._BagsArg(self.tables, idx_d, offs, wts, w.pool, self.B,
                              [sc] * self.K if sc else None)

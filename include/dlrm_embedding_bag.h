@@ -137,6 +137,11 @@ DLRM_API int dlrm_interact_lower_tri(int32_t batch, int32_t num_emb, int32_t dim
  * above; emb_out, if not NULL, also receives the (B, K, D) pooled tensor.
  *   dense    (B, D) float32
  *   out      (B, D + F(F-1)/2) float32, F = K + 1
+ * Long bags: when emb_out is given (16-byte aligned, D % 4 == 0) and the mean
+ * bag pools at least 4096 elements (L x D), the call runs as two launches on
+ * `stream`, the gather into emb_out and then the interaction reading it,
+ * which is faster there; out and emb_out hold the same values either way.
+ * emb_out must not overlap dense or out.
  */
 DLRM_API int dlrm_emb_interact(int32_t num_tables, int32_t batch, int32_t dim,
                       const float *const *tables, const int64_t *rows,
@@ -223,7 +228,8 @@ DLRM_API int emb_bag_pool(const dlrm_bags *bags, float *out, void *stream);
  *   bags     [host] the lookups (K = bags->num_tables, D = bags->dim)
  *   dense    (B, D) float32
  *   out      (B, D + F(F-1)/2) float32, F = K + 1
- *   emb_out  NULL, or (B, K, D) float32 receiving the pooled vectors
+ *   emb_out  NULL, or (B, K, D) float32 receiving the pooled vectors; long
+ *            bags then take two launches, as for dlrm_emb_interact
  */
 DLRM_API int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, float *out,
                                     float *emb_out, void *stream);
@@ -238,7 +244,8 @@ DLRM_API int dlrm_emb_interact_pool(const dlrm_bags *bags, const float *dense, f
  *   bags     [host] the lookups (any dlrm_bags form)
  *   dense    (B, D) float32, feature 0 (read, not copied)
  *   dots     (B, P) float32 with row stride ld_dots >= P = F(F-1)/2
- *   emb_out  NULL, or (B, K, D) float32 receiving the pooled vectors
+ *   emb_out  NULL, or (B, K, D) float32 receiving the pooled vectors; long
+ *            bags then take two launches, as for dlrm_emb_interact
  */
 DLRM_API int dlrm_emb_interact_dots(const dlrm_bags *bags, const float *dense, float *dots,
                                     int64_t ld_dots, float *emb_out, void *stream);

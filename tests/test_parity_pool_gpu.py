@@ -211,6 +211,67 @@ def test_fused_pool_forms(B, K, rows, D, L, dtype, pool, weighted):
     assert_close(host(emb_out), E, "pooled copy")
 
 
+LONG_SHAPES = [  # (B, K, rows, D, L) with L x D >= 4096 pooled elements per bag
+    (37, 5, 333, 128, 40),    # f32: 32 lanes per row; bf16 16; fp8 8
+    (9, 3, 100, 64, 70),      # 4480 elements, 64-wide rows
+    (5, 2, 50, 256, 20),      # a full wave per f32 row
+    (3, 26, 200, 128, 33),    # many tables, ragged workgroup tail
+]
+
+
+@pytest.mark.parametrize("dtype,pool,weighted", FORMS)
+@pytest.mark.parametrize("B,K,rows,D,L", LONG_SHAPES)
+def test_long_bags_two_launch_route(B, K, rows, D, L, dtype, pool, weighted):
+    """Long bags with emb_out given run as two launches (the gather into
+    emb_out, then the interaction reading it).  out must equal the one-launch
+    result (emb_out NULL) bit for bit, for both the [dense, dots] and the
+    dots-only layouts, and both must match the oracle."""
+    import torch
+    tables, idx, offs, wts = _case(B, K, rows, D, L, dtype, False, weighted, seed=B + 3 * K,
+                                   dyadic=False)
+    dense = np.random.default_rng(B + 1).standard_normal((B, D)).astype(np.float32)
+    sc = [2.0 ** -6] * K if dtype == "fp8" else None
+    td = _dev_tables(tables)
+    xd = [dev(i) for i in idx]
+    wd = [dev(w) for w in wts] if wts else None
+    dd = dev(dense)
+    E = oracle.emb_bag(tables, idx, None, batch=B, weights=wts, pool=pool, scales=sc)
+    want = oracle.interact(dense, E)
+    emb_out = torch.full((B, K, D), float("nan"), device="cuda")
+    two = host(abi.dlrm_emb_interact_pool(td, xd, dd, weights=wd, pool=pool, emb_out=emb_out,
+                                          scales=sc))
+    one = host(abi.dlrm_emb_interact_pool(td, xd, dd, weights=wd, pool=pool, scales=sc))
+    assert np.array_equal(two, one), "the two-launch route must match the fused launch"
+    assert_close(two, want, f"two-launch {dtype} {pool}")
+    assert_close(host(emb_out), E, "pooled copy")
+    emb_out.fill_(float("nan"))
+    d_two = host(abi.dlrm_emb_interact_dots(td, xd, dd, weights=wd, pool=pool, emb_out=emb_out,
+                                            scales=sc))
+    d_one = host(abi.dlrm_emb_interact_dots(td, xd, dd, weights=wd, pool=pool, scales=sc))
+    assert np.array_equal(d_two, d_one)
+    assert np.array_equal(d_two, two[:, D:])
+    assert_close(host(emb_out), E, "pooled copy (dots layout)")
+
+
+def test_long_csr_bags_two_launch_route():
+    """CSR bags (sizes 0..2L, one empty, one long) whose mean is long enough
+    for the two-launch route."""
+    import torch
+    B, K, rows, D, L = 41, 4, 300, 128, 60
+    tables, idx, offs, wts = _case(B, K, rows, D, L, "f32", True, True, seed=99, dyadic=False)
+    assert sum(i.shape[0] for i in idx) * D >= 4096 * B * K
+    dense = np.random.default_rng(3).standard_normal((B, D)).astype(np.float32)
+    args = ([dev(t) for t in tables], [dev(i) for i in idx], dev(dense))
+    kw = dict(offsets=[dev(o) for o in offs], weights=[dev(w) for w in wts])
+    emb_out = torch.empty((B, K, D), device="cuda")
+    two = host(abi.dlrm_emb_interact_pool(*args, emb_out=emb_out, **kw))
+    one = host(abi.dlrm_emb_interact_pool(*args, **kw))
+    assert np.array_equal(two, one)
+    E = oracle.emb_bag(tables, idx, offs, weights=wts)
+    assert_close(two, oracle.interact(dense, E), "two-launch csr")
+    assert_close(host(emb_out), E, "pooled copy")
+
+
 # ------------------------------------------------------------- full size --
 def _full_inputs(w):
     tables = [inputs.table_device_typed(w, k) for k in range(w.num_tables)]
