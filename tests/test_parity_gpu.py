@@ -129,6 +129,7 @@ def test_emb_bag_zero_batch_is_noop():
 INTERACT_SHAPES = [  # (B, K, D)
     (7, 1, 4), (33, 26, 64), (64, 32, 64), (19, 8, 12), (5, 3, 7), (3, 64, 128),
     (130, 2, 16), (2, 26, 128), (1, 5, 1), (9, 64, 4),
+    (13, 7, 64), (11, 9, 16), (6, 11, 32), (4, 14, 8), (40, 1, 64), (3, 2, 256),
 ]
 
 
