@@ -25,6 +25,8 @@
 //
 // Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
 // bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
+// Layers with K <= 16 (the 13 -> 512 first layer) are bound by writing C;
+// they take a VALU kernel with the weights in registers (thin_k_kernel).
 //
 // Split A ([FASTPATHS] matmul2d.rs, a_split and the *_split_a frontends: the
 // top MLP reads cat(dense, interactions) from two pointers without building
@@ -32,6 +34,8 @@
 // another.  Both kernels take the A source as a struct; the unsplit
 // instantiations never look at its second half.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -350,6 +354,78 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K, const AS
   }
 }
 
+// K <= 16 (the 13 -> 512 first bottom layer): the layer is bound by writing
+// C, M N floats against (M + N) K read, and a matrix-core tile would spend
+// its time on one partial k-slab.  Measured on MI355X at 8192 x 512 x 13:
+// 9.7 us against 11.4 us for the 128 x 128 MFMA tile.  Each wave owns 256 consecutive output
+// columns (4 per lane) of RB consecutive rows: the lane's 4 x K weights and
+// bias stay in registers, the RB rows of A are wave-uniform (scalar loads,
+// all issued before the arithmetic), and each row costs a lane 4 K FMAs and
+// one float4 store.  The k sum runs in order, then the bias is added.
+constexpr int kThinMaxK = 16;
+// Rows per wave: 8 rows of 13 k would spill the scalar registers, and so
+// would 4 with a split A (each k then picks its source row at run time).
+template <int K, bool SPLIT>
+constexpr int thin_rows() {
+  return SPLIT ? (K > 13 ? 1 : 2) : 4;
+}
+
+template <int K, bool SPLIT>
+__global__ __launch_bounds__(256) void thin_k_kernel(int M, int N, const ASrc A,
+                                                     const float *__restrict__ W,
+                                                     const float *__restrict__ bias, int act,
+                                                     float *__restrict__ C, int64_t ldc,
+                                                     int col_groups, int xcd_run) {
+  constexpr int RB = thin_rows<K, SPLIT>();
+  // XCD-aware order: workgroup i runs on XCD i % 8 and takes the i / 8-th of
+  // that XCD's contiguous run of workgroups, so each XCD writes a contiguous
+  // band of rows, the band the next layer's m-major tiles on that XCD read.
+  const int wg = (int)(blockIdx.x & 7) * xcd_run + (int)(blockIdx.x >> 3);
+  const int wave = __builtin_amdgcn_readfirstlane(wg * (int)(blockDim.x >> 6) +
+                                                  (int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int cg = wave % col_groups;
+  const int m0 = (wave / col_groups) * RB;
+  if (m0 >= M) return;
+  const int n = cg * 256 + 4 * lane;
+  const bool live = n < N;  // N % 4 == 0: a live lane owns 4 real columns
+  float w[4][K];
+  float bv[4];
+  const int nl = live ? n : 0;  // dead lanes read column 0 and store nothing
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[j][k] = W[(int64_t)(nl + j) * K + k];
+    bv[j] = bias ? bias[nl + j] : 0.0f;
+  }
+  const int rows = min(RB, M - m0);
+  float av[RB][K];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int64_t m = m0 + min(r, rows - 1);  // rows past M repeat the last one
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      av[r][k] = (SPLIT && k >= A.k_lo) ? A.hi[m * A.ld_hi + (k - A.k_lo)] : A.lo[m * A.ld_lo + k];
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    if (r >= rows) break;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(av[r][k], w[j][k], acc[j]);
+    if (live) {
+      float4 o;
+      o.x = apply_act(acc[0] + bv[0], act);
+      o.y = apply_act(acc[1] + bv[1], act);
+      o.z = apply_act(acc[2] + bv[2], act);
+      o.w = apply_act(acc[3] + bv[3], act);
+      *reinterpret_cast<float4 *>(C + (int64_t)(m0 + r) * ldc + n) = o;
+    }
+  }
+}
+
 template <int BM, int BN, int GM, int GN, bool SPLIT>
 hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, const float *W, const float *bias,
                            int act, float *C, int64_t ldc, bool va, bool vw, bool vc,
@@ -393,6 +469,38 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
       hipLaunchKernelGGL((gemv_kernel<false, SPLIT>), grid, block, 0, stream, M, N, K, A, W,
                          bias, act, C, ldc);
     return hipGetLastError();
+  }
+  if (K >= 1 && K <= kThinMaxK && N % 4 == 0 && vc) {
+    const int col_groups = (N + 255) / 256;
+    auto run = [&](auto kc) -> hipError_t {
+      constexpr int KK = decltype(kc)::value;
+      constexpr int rb = thin_rows<KK, SPLIT>();
+      const int64_t waves = (int64_t)((M + rb - 1) / rb) * col_groups;
+      const int64_t xcd_run = ((waves + 3) / 4 + 7) / 8;  // workgroups per XCD
+      if (xcd_run * 8 > INT32_MAX) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((thin_k_kernel<KK, SPLIT>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
+                         stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
+      return hipGetLastError();
+    };
+    switch (K) {
+      case 1: return run(std::integral_constant<int, 1>{});
+      case 2: return run(std::integral_constant<int, 2>{});
+      case 3: return run(std::integral_constant<int, 3>{});
+      case 4: return run(std::integral_constant<int, 4>{});
+      case 5: return run(std::integral_constant<int, 5>{});
+      case 6: return run(std::integral_constant<int, 6>{});
+      case 7: return run(std::integral_constant<int, 7>{});
+      case 8: return run(std::integral_constant<int, 8>{});
+      case 9: return run(std::integral_constant<int, 9>{});
+      case 10: return run(std::integral_constant<int, 10>{});
+      case 11: return run(std::integral_constant<int, 11>{});
+      case 12: return run(std::integral_constant<int, 12>{});
+      case 13: return run(std::integral_constant<int, 13>{});
+      case 14: return run(std::integral_constant<int, 14>{});
+      case 15: return run(std::integral_constant<int, 15>{});
+      case 16: return run(std::integral_constant<int, 16>{});
+      default: break;
+    }
   }
   // Tile shape: the largest tile that still gives every CU a workgroup.
   auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };

@@ -200,6 +200,9 @@ LINEAR_SHAPES = [  # (M, N, K)
     (300, 1, 256), (37, 19, 13), (129, 130, 131), (64, 8, 5), (1, 1, 1), (5, 9, 3),
     (257, 128, 64), (70, 3, 40), (513, 72, 36),
     (33, 22, 16), (40, 2, 600), (2000, 516, 16), (77, 4, 512),
+    # K <= 16 with N % 4 == 0 (the register-weight kernel): partial column
+    # groups, K = 1, a ragged last row batch
+    (37, 12, 13), (130, 1024, 7), (5, 260, 1), (1, 256, 16), (9, 20, 4),
 ]
 
 
@@ -240,6 +243,22 @@ def test_linear_strided_operands():
     abi.linear_bias_act(a, dev(w), dev(b), "relu", out=c)
     want = oracle.linear(host(a), w, b, "relu")
     assert_close(host(c), want, "strided")
+    assert np.all(host(cbuf)[:, N:] == -7.0), "columns beyond n must be untouched"
+
+
+def test_linear_thin_k_strided_operands():
+    """K <= 16 with lda > k (unaligned rows of A) and ldc > n."""
+    import torch
+    rng = np.random.default_rng(6)
+    M, N, K = 99, 64, 13
+    abuf = dev(rng.standard_normal((M, 17)).astype(np.float32))
+    a = abuf[:, :K]
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    b = rng.standard_normal(N).astype(np.float32)
+    cbuf = torch.full((M, 72), -7.0, device="cuda")
+    c = cbuf[:, :N]
+    abi.linear_bias_act(a, dev(w), dev(b), "sigmoid", out=c)
+    assert_close(host(c), oracle.linear(host(a), w, b, "sigmoid"), "thin strided")
     assert np.all(host(cbuf)[:, N:] == -7.0), "columns beyond n must be untouched"
 
 

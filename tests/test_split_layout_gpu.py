@@ -21,7 +21,9 @@ SPLIT_SHAPES = [  # (M, N, K_lo, K_hi)
     (130, 5, 64, 351),       # N <= 8: the matrix-vector kernel
     (9, 3, 5, 2),            # tiny, N <= 8, unaligned
     (300, 256, 128, 300),    # two full slabs then a tail
-    (50, 40, 5, 6),          # K <= 16: the small-K kernel
+    (50, 40, 5, 6),          # K <= 16: the register-weight kernel
+    (50, 40, 9, 7),          # K = 16, one row per wave
+    (21, 12, 13, 1),         # K = 14, ragged
     (60, 2, 300, 400),       # N <= 8 past the register-staged row length
 ]
 
