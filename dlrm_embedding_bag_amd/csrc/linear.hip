@@ -357,11 +357,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K, const AS
 // K <= 16 (the 13 -> 512 first bottom layer): the layer is bound by writing
 // C, M N floats against (M + N) K read, and a matrix-core tile would spend
 // its time on one partial k-slab.  Measured on MI355X at 8192 x 512 x 13:
-// 9.7 us against 11.4 us for the 128 x 128 MFMA tile.  Each wave owns 256 consecutive output
-// columns (4 per lane) of RB consecutive rows: the lane's 4 x K weights and
-// bias stay in registers, the RB rows of A are wave-uniform (scalar loads,
-// all issued before the arithmetic), and each row costs a lane 4 K FMAs and
-// one float4 store.  The k sum runs in order, then the bias is added.
+// 9.7 us against 11.4 us for the 128 x 128 MFMA tile.  Each wave owns 256
+// consecutive output columns (4 per lane) of RB consecutive rows: the lane's
+// 4 x K weights and bias stay in registers, the RB rows of A are wave-uniform
+// (scalar loads, all issued before the arithmetic), and each row costs a lane
+// 4 K FMAs and one float4 store.  The k sum runs in order, then the bias is
+// added.
 constexpr int kThinMaxK = 16;
 // Rows per wave: 8 rows of 13 k would spill the scalar registers, and so
 // would 4 with a split A (each k then picks its source row at run time).
