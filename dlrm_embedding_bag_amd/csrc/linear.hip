@@ -14,14 +14,14 @@
 // applies the activation and stores a float4.
 //
 // Tiles: BM x BN per workgroup of GM x GN waves (128 x 128 on 2 x 4 waves,
-// 64 x 64 or 64 x 32 on 2 x 2), BK = 32 staged through two LDS buffers (row
-// stride 36 floats: the 16 rows a ds_read_b128 touches start on different
-// banks): k-slabs are loaded into registers two slabs ahead and stored to the
-// other LDS buffer while the current one is multiplied, one barrier per slab.  Full
-// slabs load without bounds tests (rows past the matrix are clamped and their
-// outputs masked at the store); only the last, partial slab tests k.  Tiles
-// are assigned to XCDs in contiguous m-major runs so the workgroups that share
-// rows of A share an L2.
+// 128 x 64 on 4 x 2, 64 x 64 or 64 x 32 on 2 x 2), BK = 32 staged through
+// two LDS buffers (row stride 36 floats: the 16 rows a ds_read_b128 touches
+// start on different banks): k-slabs are loaded into registers two slabs
+// ahead and stored to the other LDS buffer while the current one is
+// multiplied, one barrier per slab.  Full slabs load without bounds tests
+// (rows past the matrix are clamped and their outputs masked at the store);
+// only the last, partial slab tests k.  Tiles are assigned to XCDs in
+// contiguous m-major runs so the workgroups that share rows of A share an L2.
 //
 // Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
 // bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
@@ -522,11 +522,22 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
   if constexpr (forced == 10)
     return launch_gemm_cfg<64, 64, 1, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                 stream);
+  if constexpr (forced == 11)
+    return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                 stream);
+  if constexpr (forced == 13)
+    return launch_gemm_cfg<128, 128, 4, 4, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                  stream);
   // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
-  // for every CU, else 64 x 64, else 64 x 32 on 4 waves.
+  // for every CU, else 128 x 64 on 8 waves of 32 x 32, else 64 x 64, else
+  // 64 x 32 on 4 waves.  (At 8192 x 256 x 512, 128 x 64 on 8 waves: 24.5 us,
+  // 64 x 64 on 4 waves: 26.6 us, the same sums bit for bit.)
   if (forced == 1 || (forced == 0 && tiles(128, 128) >= 256))
     return launch_gemm_cfg<128, 128, 2, 4, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                   stream);
+  if (forced == 0 && tiles(128, 64) >= 256)
+    return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                 stream);
   if (forced == 3 || (forced == 0 && tiles(64, 64) >= 256))
     return launch_gemm_cfg<64, 64, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                 stream);
