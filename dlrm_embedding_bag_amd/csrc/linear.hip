@@ -525,9 +525,6 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
   if constexpr (forced == 11)
     return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                  stream);
-  if constexpr (forced == 13)
-    return launch_gemm_cfg<128, 128, 4, 4, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                  stream);
   // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
   // for every CU, else 128 x 64 on 8 waves of 32 x 32, else 64 x 64, else
   // 64 x 32 on 4 waves.  (At 8192 x 256 x 512, 128 x 64 on 8 waves: 24.5 us,
