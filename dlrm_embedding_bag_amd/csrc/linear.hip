@@ -478,7 +478,7 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
       constexpr int rb = thin_rows<KK, SPLIT>();
       const int64_t waves = (int64_t)((M + rb - 1) / rb) * col_groups;
       const int64_t xcd_run = ((waves + 3) / 4 + 7) / 8;  // workgroups per XCD
-      if (xcd_run * 8 > INT32_MAX) return hipErrorInvalidValue;
+      if (xcd_run * 8 * 4 > INT32_MAX) return hipErrorInvalidValue;  // wave ids are int
       hipLaunchKernelGGL((thin_k_kernel<KK, SPLIT>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
                          stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
       return hipGetLastError();
