@@ -471,14 +471,15 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
                          bias, act, C, ldc);
     return hipGetLastError();
   }
-  if (K >= 1 && K <= kThinMaxK && N % 4 == 0 && vc) {
-    const int col_groups = (N + 255) / 256;
+  const int col_groups = (N + 255) / 256;
+  // (wave ids are int: at most M x col_groups waves, each a multiple of 8
+  // workgroups of 4)
+  if (K >= 1 && K <= kThinMaxK && N % 4 == 0 && vc && (int64_t)M * col_groups < (1LL << 30)) {
     auto run = [&](auto kc) -> hipError_t {
       constexpr int KK = decltype(kc)::value;
       constexpr int rb = thin_rows<KK, SPLIT>();
       const int64_t waves = (int64_t)((M + rb - 1) / rb) * col_groups;
       const int64_t xcd_run = ((waves + 3) / 4 + 7) / 8;  // workgroups per XCD
-      if (xcd_run * 8 * 4 > INT32_MAX) return hipErrorInvalidValue;  // wave ids are int
       hipLaunchKernelGGL((thin_k_kernel<KK, SPLIT>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
                          stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
       return hipGetLastError();
