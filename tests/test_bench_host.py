@@ -1,0 +1,49 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU refusal, the byte
+models behind the roofline line, and the counters lookup that turns the
+traffic figure off when the kernel sources change."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+from dlrm_embedding_bag_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr or "1 GPU" in r.stderr, r.stderr
+    assert r.stdout.strip() == "", "no JSON line for a refused run"
+
+
+def test_fused_bytes_per_sample_at_the_benchmark_shape():
+    # B = 2048, K = 32, D = 64, L = 20: rows 32*20*64*4 = 163840, indices
+    # 32*20*4 = 2560, dense 256, output (64 + 528)*4 = 2368 -> 169024 B.
+    assert bench.emb_interact_bytes_per_sample(32, 64, 20) == 169024
+    assert 2048 * bench.emb_interact_bytes_per_sample(32, 64, 20) == 346161152
+
+
+def test_general_form_bytes_reduce_to_the_f32_model():
+    w = inputs.WORKLOADS["nc32"]
+    assert bench.pool_bytes_per_sample(w, 32, 32 * 20) == \
+        bench.emb_interact_bytes_per_sample(32, 64, 20)
+    bf = inputs.WORKLOADS["nc32-bf16"]
+    # bf16 rows are half as wide: 640 rows x 128 B less
+    assert bench.pool_bytes_per_sample(bf, 32, 640) == 169024 - 640 * 128
+    wt = inputs.WORKLOADS["nc32-weighted"]
+    assert bench.pool_bytes_per_sample(wt, 32, 640) == 169024 + 640 * 4
+
+
+def test_traffic_is_dropped_when_the_kernel_sources_change(tmp_path, monkeypatch):
+    h = bench.kernel_source_hash()
+    p = tmp_path / "counters.json"
+    p.write_text(json.dumps({"nc32": {"kernel_source_hash": h,
+                                      "hbm_bytes_per_launch": 123.0}}))
+    monkeypatch.setattr(bench, "COUNTERS_JSON", str(p))
+    assert bench.read_traffic(h, "nc32") == 123.0
+    assert bench.read_traffic("0" * 16, "nc32") is None
+    assert bench.read_traffic(h, "nc32-bf16") is None
