@@ -755,6 +755,28 @@ def copy_rate(stream, mib=1024, reps=10):
     return 2 * (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def profile_linear(shape, stream):
+    """Ten launches of one linear layer, 8192 x N x K with A's row stride LDA
+    and ReLU, for kernel-trace and counter runs."""
+    import torch
+    from dlrm_embedding_bag_amd import abi
+    N, K, lda = shape
+    M = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, lda, device="cuda", generator=g)
+    w = torch.randn(N, K, device="cuda", generator=g) * 0.05
+    b = torch.randn(N, device="cuda", generator=g)
+    c = torch.empty(M, N, device="cuda")
+    lib = abi.load()
+    for _ in range(10):
+        rc = lib.linear_bias_act(M, N, K, a.data_ptr(), lda, w.data_ptr(), b.data_ptr(),
+                                 abi.ACTS["relu"], c.data_ptr(), N, stream.cuda_stream)
+        if rc:
+            raise RuntimeError(f"linear_bias_act: {rc}")
+    torch.cuda.synchronize()
+    log(f"profile-linear {M}x{N}x{K} (lda {lda}): 10 launches done")
+
+
 def copy_calibration(stream):
     """A plain device copy of 1 GiB, the known-size reference for the HBM
     byte counters (FETCH_SIZE should read 1 GiB, WRITE_SIZE 1 GiB)."""
@@ -789,6 +811,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="batch x num_tables sweep instead")
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--sweep-out", default="")
+    ap.add_argument("--profile-linear", type=int, nargs=3, metavar=("N", "K", "LDA"),
+                    help="only 10 launches of one 8192-row linear layer (for counter runs)")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the cold timed steps (for profiler runs)")
     args = ap.parse_args()
@@ -807,6 +831,9 @@ def main():
     stream = torch.cuda.Stream()
     if args.copy_calibration:
         copy_calibration(stream)
+        return
+    if args.profile_linear:
+        profile_linear(args.profile_linear, stream)
         return
     if args.sweep:
         import torch
