@@ -333,7 +333,8 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
 // in a few tables), then the interaction reading emb_out, beats the fused
 // kernel, whose workgroups each need rows of all K tables.  Measured on
 // MI355X at B = 16384, K = 26, D = 128, 40 Zipf(1.05) indices per bag:
-// 740 us against 796 us; at 20 indices and D = 64 the fused kernel wins.
+// 746 us against 826 us for the fused kernel writing emb_out; at 20 indices
+// and D = 64 the fused kernel wins.
 // Taken when the mean bag pools at least kTwoPassElems elements (L x D).
 constexpr int64_t kTwoPassElems = 4096;
 
