@@ -331,6 +331,11 @@ def bench_emb_interact(args, stream):
                 "compulsory_bytes_per_launch": int(
                     extra["distinct_row_fraction"] * case.B * case.K * case.L * case.D * 4),
                 "kernel_source_hash": khash}
+    if roofline["traffic"]:
+        # the measured HBM bytes over the same time: the bound that is real
+        # once repeated rows are served by the L2
+        roofline["traffic_gbps"] = roofline["traffic"] / (ms * 1e-3) / 1e9
+        roofline["traffic_frac"] = roofline["traffic_gbps"] / HBM_PEAK_GBPS
     res = {"metric": METRIC, "value": case.B / (ms * 1e-3), "unit": "samples/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "us_per_forward": ms * 1e3, "achieved_hbm_gbps": achieved,
