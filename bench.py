@@ -744,6 +744,75 @@ def bench_sweep(args, stream, flush):
             "cache": "warm" if args.warm else "cold", "cells": cells}
 
 
+def bench_sweep_forward(args, stream, flush):
+    """Batch sweep of the full DLRMv1 forward (K=26 tables x 1,000,000 rows x
+    D=64, 20 Zipf(1.05) indices per bag, MLPs 13-512-256-64 and
+    415-512-256-1): the whole forward cold, the gather + interaction alone
+    cold against the HBM roofline, and the six MLP layers alone (back to
+    back, warm) against the f32 MFMA roofline."""
+    import dataclasses
+    import torch
+    from dlrm_embedding_bag_amd import abi, inputs
+    batches = [256, 1024, 2048, 4096, 8192, 16384]
+    w = dataclasses.replace(inputs.WORKLOADS["dlrm"], batch=max(batches))
+    tables = [inputs.table_device(w, k, args.seed) for k in range(w.num_tables)]
+    idx = [torch.from_numpy(inputs.indices(w, k, args.seed)).cuda() for k in range(w.num_tables)]
+    dense_in = torch.from_numpy(inputs.dense(w, args.seed)).cuda()
+    bottom, top = inputs.dlrm_layers(w, args.seed)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    bl = [(dev(a), dev(b), act) for a, b, act in bottom]
+    tl = [(dev(a), dev(b), act) for a, b, act in top]
+    model = abi.DlrmModel(bl, tl, tables)
+    lib = abi.load()
+    K, D, L = w.num_tables, w.dim, w.bag
+    F = K + 1
+    P = F * (F - 1) // 2
+    cells = []
+    for B in batches:
+        xs = [i[: B * L] for i in idx]
+        nidx = abi._i64_array([x.numel() for x in xs])
+        ws = torch.empty(model.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, 1), device="cuda")
+        fa = (ctypes.byref(model.struct), B, dense_in.data_ptr(), abi._ptr_array(xs), None, nidx,
+              out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        t_fwd = _event_time(lambda: lib.dlrm_forward(*fa), stream, args.sweep_steps, 3, True,
+                            flush)
+        d64 = torch.zeros((B, D), device="cuda")
+        r = torch.empty((B, D + P), device="cuda")
+        ea = (K, B, D, abi._ptr_array(tables), abi._i64_array([t.shape[0] for t in tables]),
+              abi._ptr_array(xs), None, nidx, d64.data_ptr(), r.data_ptr(), None,
+              stream.cuda_stream)
+        t_emb = _event_time(lambda: lib.dlrm_emb_interact(*ea), stream, args.sweep_steps, 3,
+                            True, flush)
+        emb_bytes = B * emb_interact_bytes_per_sample(K, D, L)
+        # the six layers alone
+        mlp_t, mlp_f = 0.0, 0.0
+        x = dense_in[:B]
+        for part, layers in (("bottom", bl), ("top", tl)):
+            if part == "top":
+                x = torch.zeros((B, D + P), device="cuda")
+            for wt, b, act in layers:
+                n, k = wt.shape
+                y = torch.empty((B, n), device="cuda")
+                la = (B, n, k, x.data_ptr(), x.stride(0), wt.data_ptr(), b.data_ptr(),
+                      abi.ACTS[act], y.data_ptr(), n, stream.cuda_stream)
+                mlp_t += _back_to_back_time(lambda: lib.linear_bias_act(*la), stream, 20, 3)
+                mlp_f += 2.0 * B * n * k
+                x = y
+        tf = mlp_f / (mlp_t * 1e-3) / 1e12
+        gbs = emb_bytes / (t_emb * 1e-3) / 1e9
+        cells.append({"batch": B, "forward_us": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
+                      "emb_interact_us": t_emb * 1e3, "emb_interact_algorithmic_gbps": gbs,
+                      "emb_interact_frac_hbm": gbs / HBM_PEAK_GBPS, "mlp_us": mlp_t * 1e3,
+                      "mlp_tflops": tf, "mlp_frac_f32_mfma": tf / F32_MFMA_PEAK_TFLOPS})
+        log(f"sweep-forward B={B:5d}: forward {t_fwd * 1e3:7.1f} us "
+            f"({B / (t_fwd * 1e-3) / 1e6:5.1f} M/s), emb+interact {t_emb * 1e3:6.1f} us "
+            f"({gbs:6.0f} GB/s), MLP {mlp_t * 1e3:6.1f} us ({tf:5.1f} TFLOP/s)")
+        del ws, out, d64, r
+    return {"workload": f"dlrm: {w.description}", "cache": "cold forward and gather, warm "
+            "MLP layers", "cells": cells}
+
+
 def copy_rate(stream, mib=1024, reps=10):
     """Read + write rate of a plain 1 GiB device copy (a practical HBM figure)."""
     import torch
@@ -814,6 +883,8 @@ def main():
     ap.add_argument("--no-cells", action="store_true",
                     help="skip the pages' small-cell forward latency grid (eager vs plan)")
     ap.add_argument("--sweep", action="store_true", help="batch x num_tables sweep instead")
+    ap.add_argument("--sweep-forward", action="store_true",
+                    help="batch sweep of the full forward instead")
     ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--sweep-out", default="")
     ap.add_argument("--profile-linear", type=int, nargs=3, metavar=("N", "K", "LDA"),
@@ -839,6 +910,15 @@ def main():
         return
     if args.profile_linear:
         profile_linear(args.profile_linear, stream)
+        return
+    if args.sweep_forward:
+        import torch
+        flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+        res = bench_sweep_forward(args, stream, flush)
+        if args.sweep_out:
+            with open(args.sweep_out, "w") as f:
+                json.dump(res, f, indent=1)
+        print(json.dumps(res), flush=True)
         return
     if args.sweep:
         import torch
