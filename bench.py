@@ -16,10 +16,11 @@ skips the flush.
 Prints ONE JSON line on stdout (progress goes to stderr):
   value         samples/s = B / mean event-timed step time
   ms_per_step   mean event-timed step time
-  roofline      achieved = algorithmic bytes per launch / mean launch time,
-                against MI355X's 8 TB/s HBM peak; traffic = HBM bytes from the
-                committed rocprofv3 counter summary when it matches the
-                current kernel source, else null
+  roofline      achieved = algorithmic bytes per launch / mean kernel time
+                (events recorded by the launch itself, as rocprofv3 times the
+                kernel), against MI355X's 8 TB/s HBM peak; traffic = HBM
+                bytes from the committed rocprofv3 counter summary when it
+                matches the current kernel source, else null
   cpu_baseline  the CPU oracle timed on the host on the same workload
 
 The JSON line also carries `variants`: the same fused launch with bfloat16
@@ -225,10 +226,85 @@ def time_steps(case, steps, warmup, cold, flush_buf, stream):
     return [a.elapsed_time(b) for a, b in evs], wall
 
 
+class KernelTimer:
+    """HIP event pairs that the library's kernel launches record at the
+    kernel's own start and end (dlrm_set_kernel_timing_events), so a pair's
+    elapsed time is one kernel's execution, as rocprofv3's kernel trace
+    reports it, without the dispatch gap that events recorded around a call
+    include.  The events come from the process's HIP runtime (the one torch
+    loaded; the library links the same soname)."""
+
+    def __init__(self, n):
+        import torch
+        from dlrm_embedding_bag_amd import abi
+        torch.cuda.init()
+        self.abi = abi
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+        for _ in range(n):
+            pair = (ctypes.c_void_p(), ctypes.c_void_p())
+            for e in pair:
+                if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+            self.events.append(pair)
+
+    def arm(self, i):
+        self.abi.dlrm_set_kernel_timing_events(self.events[i][0].value, self.events[i][1].value)
+
+    def disarm(self):
+        self.abi.dlrm_set_kernel_timing_events(None, None)
+
+    def elapsed_ms(self, i):
+        a, b = self.events[i]
+        ms = ctypes.c_float()
+        if (self.hip.hipEventSynchronize(b) != 0
+                or self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0):
+            raise RuntimeError("kernel timing events were not recorded")
+        return ms.value
+
+    def close(self):
+        self.disarm()
+        for pair in self.events:
+            for e in pair:
+                self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def time_kernel(case, steps, warmup, cold, flush_buf, stream):
+    """Per-step kernel execution times (ms) of a one-launch case, from events
+    the launch itself records (KernelTimer); the same flush and batch
+    rotation as time_steps."""
+    import torch
+    timer = KernelTimer(steps)
+    try:
+        with torch.cuda.stream(stream):
+            for s in range(warmup):
+                if cold:
+                    flush_buf.max()
+                case.run(s)
+            torch.cuda.synchronize()
+            for s in range(steps):
+                if cold:
+                    flush_buf.max()
+                timer.arm(s)
+                case.run(warmup + s)
+                timer.disarm()
+            torch.cuda.synchronize()
+        return [timer.elapsed_ms(s) for s in range(steps)]
+    finally:
+        timer.close()
+
+
 # ----------------------------------------------------------- CPU baseline --
 def cpu_baseline(case, max_seconds=20.0):
-    """The CPU oracle on this workload: the full batch, tables copied to the
-    host, single-threaded C with fp64 sums (one run; more while under 2 s)."""
+    """The CPU oracle on this workload: the full batch (fewer samples if one
+    pass would exceed max_seconds), tables copied to the host, single-threaded
+    C with fp64 sums, repeated until about 10 s of CPU time; the median run."""
     import numpy as np
     import oracle
     idx, dense, out, _ = case.batches[0]
@@ -253,7 +329,7 @@ def cpu_baseline(case, max_seconds=20.0):
         E = oracle.emb_bag_sum(tables, idx_s, batch=samples)
         R = oracle.interact(dense_h[:samples], E)
         runs.append(time.perf_counter() - t0)
-        if sum(runs) > 2.0 or len(runs) >= 5:
+        if sum(runs) >= 10.0:   # about 10 s of CPU work in all
             break
     t = statistics.median(runs)
     got = out.cpu().numpy()[:samples]
@@ -295,7 +371,13 @@ def bench_emb_interact(args, stream):
     log(f"{'cold' if cold else 'warm'} step: mean {ms * 1000:.1f} us, median "
         f"{med * 1000:.1f} us over {args.steps} steps")
     nbytes = case.bytes_per_launch()
-    achieved = nbytes / (ms * 1e-3) / 1e9
+    # the roofline takes the kernel's own duration (events recorded by the
+    # launch), which is what rocprofv3's kernel trace reports for it
+    ktimes = time_kernel(case, args.steps, args.warmup, cold, flush, stream)
+    kms = statistics.mean(ktimes)
+    log(f"kernel alone: mean {kms * 1000:.1f} us, median "
+        f"{statistics.median(ktimes) * 1000:.1f} us over {args.steps} steps")
+    achieved = nbytes / (kms * 1e-3) / 1e9
     extra = {"median_ms_per_step": med, "min_ms_per_step": min(times),
              "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
              "distinct_row_fraction": case.distinct_rows_fraction()}
@@ -327,6 +409,9 @@ def bench_emb_interact(args, stream):
                 "frac": achieved / HBM_PEAK_GBPS,
                 "traffic": read_traffic(khash, w.name),
                 "kernel": "interact_kernel<4, fused> (dlrm_emb_interact)",
+                "kernel_us": kms * 1e3,
+                "timing": "kernel execution: events recorded by the launch itself "
+                          "(hipExtLaunchKernel), mean over the timed cold steps",
                 "algorithmic_bytes_per_launch": nbytes,
                 "compulsory_bytes_per_launch": int(
                     extra["distinct_row_fraction"] * case.B * case.K * case.L * case.D * 4),
@@ -334,11 +419,12 @@ def bench_emb_interact(args, stream):
     if roofline["traffic"]:
         # the measured HBM bytes over the same time: the bound that is real
         # once repeated rows are served by the L2
-        roofline["traffic_gbps"] = roofline["traffic"] / (ms * 1e-3) / 1e9
+        roofline["traffic_gbps"] = roofline["traffic"] / (kms * 1e-3) / 1e9
         roofline["traffic_frac"] = roofline["traffic_gbps"] / HBM_PEAK_GBPS
     res = {"metric": METRIC, "value": case.B / (ms * 1e-3), "unit": "samples/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "us_per_forward": ms * 1e3, "achieved_hbm_gbps": achieved,
+           "step_algorithmic_gbps": nbytes / (ms * 1e-3) / 1e9,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic (seeded N(0, 0.01^2) tables, Zipf/uniform int32 indices, "
                    "N(0,1) dense)",
@@ -420,12 +506,15 @@ def bench_variant_line(args, stream):
     flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
     times, _ = time_steps(case, args.steps, args.warmup, not args.warm, flush, stream)
     ms = statistics.mean(times)
+    kms = statistics.mean(time_kernel(case, args.steps, args.warmup, not args.warm, flush,
+                                      stream))
     nbytes = case.bytes_per_launch()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"{w.name}: mean {ms * 1000:.1f} us, {gbs:.0f} GB/s")
+    log(f"{w.name}: mean {ms * 1000:.1f} us, {gbs:.0f} GB/s; kernel alone {kms * 1000:.1f} us")
     return {"workload": f"{w.name}: {w.description}", "ms_per_step": ms,
             "samples_per_s": case.B / (ms * 1e-3), "algorithmic_gbps": gbs,
-            "frac_hbm": gbs / HBM_PEAK_GBPS, "steps": args.steps}
+            "frac_hbm": gbs / HBM_PEAK_GBPS, "kernel_us": kms * 1e3,
+            "kernel_algorithmic_gbps": nbytes / (kms * 1e-3) / 1e9, "steps": args.steps}
 
 
 def _event_time(fn, stream, steps, warmup, cold, flush):
@@ -692,12 +781,14 @@ def bench_variants(args, stream, flush):
         torch.cuda.synchronize()
         times, _ = time_steps(case, args.steps, args.warmup, not args.warm, flush, stream)
         ms = statistics.mean(times)
+        kms = statistics.mean(time_kernel(case, args.steps, 2, not args.warm, flush, stream))
         nbytes = case.bytes_per_launch()
         gbs = nbytes / (ms * 1e-3) / 1e9
         rows.append({"workload": f"{name}: {w.description}", "us": ms * 1e3,
                      "samples_per_s": case.B / (ms * 1e-3),
                      "algorithmic_bytes_per_launch": nbytes, "algorithmic_gbps": gbs,
-                     "frac_hbm": gbs / HBM_PEAK_GBPS,
+                     "frac_hbm": gbs / HBM_PEAK_GBPS, "kernel_us": kms * 1e3,
+                     "kernel_algorithmic_gbps": nbytes / (kms * 1e-3) / 1e9,
                      "traffic": read_traffic(kernel_source_hash(), name)})
         log(f"variant {name:14s} {ms * 1000:7.1f} us {case.B / (ms * 1e-3) / 1e6:6.1f} M "
             f"samples/s {gbs:6.0f} GB/s")
@@ -864,6 +955,59 @@ def copy_calibration(stream):
     log("copy calibration: 5 copies of 1 GiB done")
 
 
+def _dispatch_counter(run_dir, counter, kernel_part):
+    """Median over the dispatches of kernels whose name holds `kernel_part`
+    of one counter's per-dispatch total, from a rocprofv3 --pmc output
+    directory (its *counter_collection.csv)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and kernel_part in row["Kernel_Name"]:
+                    key = (fn, row["Dispatch_Id"])
+                    per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise ValueError(f"{counter} of a '{kernel_part}' kernel not found under {run_dir}")
+    return statistics.median(per.values()), len(per)
+
+
+def record_counters(run_root, workload, kernel_part="interact_kernel"):
+    """Scales the workload's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what
+    the same counters read for a plain 1 GiB copy and stores the HBM bytes per
+    launch in profiles/counters.json under the current kernel source hash.
+    Expects rocprofv3 -d directories pmc_<workload>_FETCH_SIZE,
+    pmc_<workload>_WRITE_SIZE, pmc_copy_FETCH_SIZE and pmc_copy_WRITE_SIZE
+    under run_root."""
+    d = lambda name: os.path.join(run_root, name)
+    fetch, nf = _dispatch_counter(d(f"pmc_{workload}_FETCH_SIZE"), "FETCH_SIZE", kernel_part)
+    write, nw = _dispatch_counter(d(f"pmc_{workload}_WRITE_SIZE"), "WRITE_SIZE", kernel_part)
+    cfetch, _ = _dispatch_counter(d("pmc_copy_FETCH_SIZE"), "FETCH_SIZE", "copyBuffer")
+    cwrite, _ = _dispatch_counter(d("pmc_copy_WRITE_SIZE"), "WRITE_SIZE", "copyBuffer")
+    copy_bytes = 1 << 30
+    fscale, wscale = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
+    entry = {"kernel_source_hash": kernel_source_hash(), "kernel_name_part": kernel_part,
+             "dispatches": [nf, nw],
+             "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
+             "copy_fetch_size_kib": cfetch, "copy_write_size_kib": cwrite,
+             "copy_bytes": copy_bytes, "fetch_scale": fscale, "write_scale": wscale,
+             "hbm_bytes_per_launch": fetch * 1024 * fscale + write * 1024 * wscale}
+    try:
+        with open(COUNTERS_JSON) as f:
+            allc = json.load(f)
+    except (OSError, ValueError):
+        allc = {}
+    allc[workload] = entry
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(allc, f, indent=1)
+        f.write("\n")
+    return entry
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -876,6 +1020,9 @@ def main():
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--record-counters", metavar="DIR", default="",
+                    help="store the workload's HBM bytes per launch from rocprofv3 --pmc "
+                         "runs under DIR in profiles/counters.json (no GPU needed)")
     ap.add_argument("--no-forward", action="store_true",
                     help="skip the full-forward section (B=8192 DLRMv1)")
     ap.add_argument("--no-variants", action="store_true",
@@ -896,6 +1043,9 @@ def main():
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.record_counters:
+        print(json.dumps(record_counters(args.record_counters, args.workload), indent=1))
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)

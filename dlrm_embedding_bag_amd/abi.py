@@ -25,7 +25,8 @@ MAX_DIM = 1024
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 POOLS = {"sum": 0, "mean": 1}
 PLAN_MODES = {"direct": 0, "graph": 1}
-EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "emb_bag_sum_multi",
+EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "dlrm_set_kernel_timing_events",
+           "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
            "dlrm_emb_interact_pool", "dlrm_emb_interact_dots", "linear_bias_act",
            "linear_bias_act_split", "mlp_forward",
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH):
     lib.dlrm_status_string.argtypes = [ctypes.c_int]
     lib.dlrm_abi_version.restype = ctypes.c_int
     lib.dlrm_abi_version.argtypes = []
+    lib.dlrm_set_kernel_timing_events.restype = ctypes.c_int
+    lib.dlrm_set_kernel_timing_events.argtypes = [_vp, _vp]
     ptrs = ctypes.POINTER(_vp)
     lib.emb_bag_sum_multi.restype = ctypes.c_int
     lib.emb_bag_sum_multi.argtypes = [_i32, _i32, _i32, ptrs, ctypes.POINTER(_i64), ptrs,
@@ -189,6 +192,12 @@ def _tables_args(tables, indices, offsets):
 
 
 # ---------------------------------------------------------------- entries --
+def dlrm_set_kernel_timing_events(start, stop):
+    """Raw hipEvent_t handles (ints) that this thread's kernel launches record
+    at their start and end, or (None, None) to stop."""
+    _check(load().dlrm_set_kernel_timing_events(start, stop), "dlrm_set_kernel_timing_events")
+
+
 def emb_bag_sum_multi(tables, indices, offsets=None, batch=None, out=None, stream=None):
     """(B, K, D) float32 pooled sums; see include/dlrm_embedding_bag.h."""
     torch = _torch()

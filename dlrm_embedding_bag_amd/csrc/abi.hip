@@ -379,9 +379,17 @@ int capture_forward(const dlrm_model &model, int32_t batch, const float *dense_i
                     const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
                     hipStream_t st, hipGraph_t *graph) {
   *graph = nullptr;
-  if (hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed) != hipSuccess) return DLRM_ERR_HIP;
+  // kernel timing events are not recorded into a graph: the captured
+  // launches are plain ones
+  const LaunchTiming timing = launch_timing();
+  launch_timing() = LaunchTiming{};
+  if (hipStreamBeginCapture(st, hipStreamCaptureModeRelaxed) != hipSuccess) {
+    launch_timing() = timing;
+    return DLRM_ERR_HIP;
+  }
   const int rc = enqueue_forward(&model, batch, dense_in, indices, offsets, n_idx, out, workspace,
                                  workspace_bytes, Emitter{st, nullptr});
+  launch_timing() = timing;
   hipGraph_t g = nullptr;
   const hipError_t e = hipStreamEndCapture(st, &g);
   if (rc || e != hipSuccess) {
@@ -393,6 +401,11 @@ int capture_forward(const dlrm_model &model, int32_t batch, const float *dense_i
 }
 
 }  // namespace
+
+LaunchTiming &dlrm::launch_timing() {
+  static thread_local LaunchTiming timing;
+  return timing;
+}
 
 extern "C" {
 
@@ -409,6 +422,12 @@ const char *dlrm_status_string(int status) {
 }
 
 int dlrm_abi_version(void) { return DLRM_ABI_VERSION; }
+
+int dlrm_set_kernel_timing_events(void *start, void *stop) {
+  if ((start == nullptr) != (stop == nullptr)) return DLRM_ERR_NULL;
+  launch_timing() = LaunchTiming{(hipEvent_t)start, (hipEvent_t)stop};
+  return DLRM_OK;
+}
 
 int emb_bag_pool(const dlrm_bags *bags, float *out, void *stream) {
   if (!bags) return DLRM_ERR_NULL;

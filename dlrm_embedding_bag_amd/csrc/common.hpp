@@ -4,8 +4,11 @@
 // 8 XCDs, HBM3E.  Nothing here is part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 namespace dlrm {
 
@@ -108,6 +111,30 @@ __device__ __forceinline__ void pair_from_index(uint32_t p, int &i, int &j) {
   r += ((r + 1) * (r + 1) <= q) ? 1 : 0;
   i = (int)((r + 1) >> 1);
   j = (int)(p - (uint32_t)i * (uint32_t)(i - 1) / 2u);
+}
+
+// Events that the calling thread's kernel launches record at the kernel's own
+// start and end (both null when timing is off); set through
+// dlrm_set_kernel_timing_events, stored per thread in abi.hip.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchTiming &launch_timing();
+
+// Every kernel of the library is launched here.  With timing on, the launch
+// goes through hipExtLaunchKernel, whose events take the dispatch's own begin
+// and end timestamps, so their elapsed time is the kernel's execution alone;
+// argument conversion to the kernel's parameter types is the same either way.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                          hipStream_t stream, Args &&...args) {
+  const LaunchTiming &t = launch_timing();
+  if (t.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, stream, t.start, t.stop, 0u,
+                          std::forward<Args>(args)...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, std::forward<Args>(args)...);
 }
 
 __host__ __device__ inline bool aligned16(const void *p) {

@@ -216,9 +216,9 @@ hipError_t launch_emb_bag(const TableSet &ts, const GatherConfig &gc, int B, int
   dim3 grid((unsigned)(per_xcd * kXcds)), block(threads);
   dispatch_gather(gc, D, [&](auto tt, auto vw, auto csr, auto gs, auto psw) {
     using TT = typename decltype(tt)::type;
-    hipLaunchKernelGGL((emb_bag_kernel<TT, decltype(vw)::value, decltype(gs)::value,
-                                       decltype(csr)::value, decltype(psw)::value>),
-                       grid, block, 0, stream, ts, B, K, D, G, per_xcd, out);
+    launch_kernel((emb_bag_kernel<TT, decltype(vw)::value, decltype(gs)::value,
+                                  decltype(csr)::value, decltype(psw)::value>),
+                  grid, block, 0, stream, ts, B, K, D, G, per_xcd, out);
   });
   return hipGetLastError();
 }
@@ -273,19 +273,19 @@ hipError_t launch_interact(const TableSet *ts, const GatherConfig &gc, const Int
   if (ts) {
     dispatch_gather(gc, ip.D, [&](auto tt, auto vw, auto csr, auto gs, auto psw) {
       using TT = typename decltype(tt)::type;
-      hipLaunchKernelGGL((interact_kernel<TT, decltype(vw)::value, MODE_FUSED,
-                                          decltype(csr)::value, decltype(gs)::value,
-                                          decltype(psw)::value>),
-                         grid, block, lds, stream, *ts, ip);
+      launch_kernel((interact_kernel<TT, decltype(vw)::value, MODE_FUSED,
+                                     decltype(csr)::value, decltype(gs)::value,
+                                     decltype(psw)::value>),
+                    grid, block, lds, stream, *ts, ip);
     });
   } else {
     TableSet empty{};
     if (gc.vec)
-      hipLaunchKernelGGL((interact_kernel<float, 4, MODE_LOAD, false, 0, false>), grid, block,
-                         lds, stream, empty, ip);
+      launch_kernel((interact_kernel<float, 4, MODE_LOAD, false, 0, false>), grid, block,
+                    lds, stream, empty, ip);
     else
-      hipLaunchKernelGGL((interact_kernel<float, 1, MODE_LOAD, false, 0, false>), grid, block,
-                         lds, stream, empty, ip);
+      launch_kernel((interact_kernel<float, 1, MODE_LOAD, false, 0, false>), grid, block,
+                    lds, stream, empty, ip);
   }
   return hipGetLastError();
 }

@@ -297,11 +297,11 @@ hipError_t launch_forward_small(const TableSet &ts, bool csr, bool vec4,
     constexpr int VW = decltype(vw)::value, GSV = decltype(gsv)::value;
     constexpr bool ST = decltype(staged)::value;
     if (csr)
-      hipLaunchKernelGGL((forward_small_kernel<VW, true, GSV, ST>), grid, block, lds, stream, ts,
-                         p);
+      launch_kernel((forward_small_kernel<VW, true, GSV, ST>), grid, block, lds, stream, ts,
+                    p);
     else
-      hipLaunchKernelGGL((forward_small_kernel<VW, false, GSV, ST>), grid, block, lds, stream, ts,
-                         p);
+      launch_kernel((forward_small_kernel<VW, false, GSV, ST>), grid, block, lds, stream, ts,
+                    p);
   };
   auto with_stage = [&](auto vw, auto gsv) {
     if (p.w_lds)

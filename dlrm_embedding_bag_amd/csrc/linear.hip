@@ -436,8 +436,8 @@ hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, const float *W, c
   const int xcd_chunk = (tiles % 8 == 0) ? (int)(tiles / 8) : 0;
   dim3 grid((unsigned)tiles), block(64 * GM * GN);
 #define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                       \
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, GM, GN, A_, W_, C_, SPLIT>), grid, block, 0, stream,  \
-                     M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk)
+  launch_kernel((gemm_kernel<BM, BN, GM, GN, A_, W_, C_, SPLIT>), grid, block, 0, stream,  \
+                M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk)
   if (va && vw && vc)
     DLRM_GEMM_LAUNCH(true, true, true);
   else if (va && !vw && vc)
@@ -464,11 +464,11 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
     const int rows_per_block = 16;
     dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(256);
     if (va && vw && K % 4 == 0)
-      hipLaunchKernelGGL((gemv_kernel<true, SPLIT>), grid, block, 0, stream, M, N, K, A, W, bias,
-                         act, C, ldc);
+      launch_kernel((gemv_kernel<true, SPLIT>), grid, block, 0, stream, M, N, K, A, W, bias,
+                    act, C, ldc);
     else
-      hipLaunchKernelGGL((gemv_kernel<false, SPLIT>), grid, block, 0, stream, M, N, K, A, W,
-                         bias, act, C, ldc);
+      launch_kernel((gemv_kernel<false, SPLIT>), grid, block, 0, stream, M, N, K, A, W,
+                    bias, act, C, ldc);
     return hipGetLastError();
   }
   const int col_groups = (N + 255) / 256;
@@ -480,8 +480,8 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
       constexpr int rb = thin_rows<KK, SPLIT>();
       const int64_t waves = (int64_t)((M + rb - 1) / rb) * col_groups;
       const int64_t xcd_run = ((waves + 3) / 4 + 7) / 8;  // workgroups per XCD
-      hipLaunchKernelGGL((thin_k_kernel<KK, SPLIT>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
-                         stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
+      launch_kernel((thin_k_kernel<KK, SPLIT>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
+                    stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
       return hipGetLastError();
     };
     switch (K) {

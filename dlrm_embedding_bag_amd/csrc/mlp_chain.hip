@@ -310,7 +310,7 @@ hipError_t launch_mlp_chain(ChainParams p, hipStream_t stream) {
       (int)(sizeof(float) * ((size_t)kBM * (kMaxChainWidth + 4) + 2 * kBM * kSlabStride)));
   if (attr != hipSuccess) return attr;
   dim3 grid((unsigned)((p.M + kBM - 1) / kBM)), block(kThreads);
-  hipLaunchKernelGGL(mlp_chain_kernel, grid, block, lds, stream, p);
+  launch_kernel(mlp_chain_kernel, grid, block, lds, stream, p);
   return hipGetLastError();
 }
 

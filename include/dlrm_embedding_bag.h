@@ -76,6 +76,28 @@ DLRM_API int dlrm_abi_version(void);
 #define DLRM_ABI_VERSION 1
 
 /*
+ * dlrm_set_kernel_timing_events -- kernel-exact timing for benchmarks.
+ * (Measurement support, not a step of the method: the pages time whole
+ * forwards with CUDA events, RESULTS.md of [FASTPATHS]; this times one
+ * kernel without the dispatch gap that events recorded around a call
+ * include.)
+ *
+ *   start, stop  hipEvent_t handles created by the caller (default flags),
+ *                or both NULL to switch timing off (the initial state).
+ *
+ * While set, every kernel that this library launches from the calling
+ * thread is dispatched with hipExtLaunchKernel and records `start` at the
+ * kernel's beginning and `stop` at its end, so after a call that launches
+ * one kernel, hipEventElapsedTime(start, stop) is that kernel's execution
+ * time; after a call that launches several, it is the last one's.  The
+ * setting is per thread; the events stay owned by the caller, who must
+ * switch timing off before destroying them.  Graph-mode plans capture
+ * plain launches whatever the setting.  Returns DLRM_ERR_NULL when exactly
+ * one of the two is NULL (nothing changes), else DLRM_OK.
+ */
+DLRM_API int dlrm_set_kernel_timing_events(void *start, void *stop);
+
+/*
  * emb_bag_sum_multi -- K EmbeddingBag(sum) lookups in one launch
  * ([FASTPATHS] embedding_bag.rs, module doc "Semantics" and
  * MultiTableEmbeddingBagSumKernel doc; translator dispatch,

@@ -43,6 +43,13 @@ def test_status_strings_and_version(lib):
     assert lib.dlrm_status_string(99) == b"unknown dlrm_status"
 
 
+def test_kernel_timing_events_need_both_or_neither(lib):
+    f = lib.dlrm_set_kernel_timing_events
+    assert f(FAKE, None) == 1                                         # DLRM_ERR_NULL
+    assert f(None, FAKE) == 1
+    assert f(None, None) == 0                                         # off
+
+
 def _tables(K, rows=10):
     t = (ctypes.c_void_p * K)(*[FAKE] * K)
     r = (ctypes.c_int64 * K)(*[rows] * K)

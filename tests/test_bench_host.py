@@ -47,3 +47,35 @@ def test_traffic_is_dropped_when_the_kernel_sources_change(tmp_path, monkeypatch
     assert bench.read_traffic(h, "nc32") == 123.0
     assert bench.read_traffic("0" * 16, "nc32") is None
     assert bench.read_traffic(h, "nc32-bf16") is None
+
+
+def _pmc_dir(root, name, counter, rows):
+    """A rocprofv3 --pmc output directory holding one counter_collection.csv
+    with (dispatch id, kernel name, per-dimension value) rows."""
+    d = os.path.join(root, name, "host", "1")
+    os.makedirs(d)
+    with open(os.path.join(d, "p_counter_collection.csv"), "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n')
+        for disp, kern, val in rows:
+            f.write(f'"{disp}","{kern}","{counter}","{val}"\n')
+
+
+def test_record_counters_scales_by_the_copy(tmp_path, monkeypatch):
+    root = str(tmp_path)
+    k = "void dlrm::interact_kernel<float, 4, 0, false, 16, false>(...)"
+    # per-dispatch totals are summed over rows of one dispatch; the median
+    # over dispatches is taken (100 KiB fetched, 10 KiB written per launch)
+    _pmc_dir(root, "pmc_w_FETCH_SIZE", "FETCH_SIZE",
+             [(1, k, 60), (1, k, 40), (2, k, 100), (3, k, 500), (4, "other", 7)])
+    _pmc_dir(root, "pmc_w_WRITE_SIZE", "WRITE_SIZE", [(1, k, 10), (2, k, 10)])
+    # the 1 GiB copy reads back half its size on FETCH_SIZE, all on WRITE_SIZE
+    _pmc_dir(root, "pmc_copy_FETCH_SIZE", "FETCH_SIZE", [(9, "__amd_rocclr_copyBuffer", 524288)])
+    _pmc_dir(root, "pmc_copy_WRITE_SIZE", "WRITE_SIZE", [(9, "__amd_rocclr_copyBuffer", 1048576)])
+    out = tmp_path / "counters.json"
+    monkeypatch.setattr(bench, "COUNTERS_JSON", str(out))
+    e = bench.record_counters(root, "w")
+    assert e["fetch_size_kib_per_dispatch"] == 100 and e["write_size_kib_per_dispatch"] == 10
+    assert e["fetch_scale"] == 2.0 and e["write_scale"] == 1.0
+    assert e["hbm_bytes_per_launch"] == 100 * 1024 * 2 + 10 * 1024
+    assert e["kernel_source_hash"] == bench.kernel_source_hash()
+    assert bench.read_traffic(bench.kernel_source_hash(), "w") == e["hbm_bytes_per_launch"]
