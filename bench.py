@@ -404,6 +404,8 @@ def bench_emb_interact(args, stream):
     if not args.profile_run:
         res_rows = bench_rows(case, args, stream, flush, cold)
         extra["rows"] = res_rows
+    if not args.profile_run and w.name == "nc32":
+        extra["uniform"] = bench_uniform(case, args, stream, flush, cold)
     khash = kernel_source_hash()
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS,
@@ -416,6 +418,7 @@ def bench_emb_interact(args, stream):
                 "compulsory_bytes_per_launch": int(
                     extra["distinct_row_fraction"] * case.B * case.K * case.L * case.D * 4),
                 "kernel_source_hash": khash}
+    roofline["compulsory_gbps"] = roofline["compulsory_bytes_per_launch"] / (kms * 1e-3) / 1e9
     if roofline["traffic"]:
         # the measured HBM bytes over the same time: the bound that is real
         # once repeated rows are served by the L2
@@ -435,6 +438,7 @@ def bench_emb_interact(args, stream):
            "roofline": roofline, "extra": extra}
     if not args.profile_run:
         extra["copy_gbps"] = copy_rate(stream)
+        log(f"practical HBM: a 1 GiB device copy moves {extra['copy_gbps']:.0f} GB/s")
     if not args.no_cpu_baseline and not args.profile_run:
         res["cpu_baseline"] = cpu_baseline(case)
         log(f"cpu baseline: {res['cpu_baseline']['value']:.0f} samples/s")
@@ -918,6 +922,28 @@ def copy_rate(stream, mib=1024, reps=10):
         e1.record(stream)
     torch.cuda.synchronize()
     return 2 * (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def bench_uniform(case, args, stream, flush, cold):
+    """The benchmark launch with uniform indices (nc32-uniform: the same
+    tables, every gathered row a distinct draw, so L2 reuse is negligible and
+    the algorithmic bytes are what HBM must deliver)."""
+    from dlrm_embedding_bag_amd import inputs
+    w = inputs.WORKLOADS["nc32-uniform"]
+    ucase = EmbInteractCase(w, args.batches, args.seed, stream, tables=case.tables)
+    times, _ = time_steps(ucase, args.steps, args.warmup, cold, flush, stream)
+    kms = statistics.mean(time_kernel(ucase, args.steps, args.warmup, cold, flush, stream))
+    ms = statistics.mean(times)
+    nbytes = ucase.bytes_per_launch()
+    res = {"workload": f"{w.name}: {w.description}", "us": ms * 1e3, "kernel_us": kms * 1e3,
+           "samples_per_s": ucase.B / (ms * 1e-3), "algorithmic_bytes_per_launch": nbytes,
+           "distinct_row_fraction": ucase.distinct_rows_fraction(),
+           "kernel_algorithmic_gbps": nbytes / (kms * 1e-3) / 1e9,
+           "kernel_frac_hbm": nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    log(f"uniform indices: {ms * 1000:.1f} us per step, kernel {kms * 1000:.1f} us, "
+        f"{res['kernel_algorithmic_gbps']:.0f} GB/s")
+    del ucase
+    return res
 
 
 def profile_linear(shape, stream):

@@ -228,9 +228,17 @@ hipError_t launch_emb_bag(const TableSet &ts, const GatherConfig &gc, int B, int
 // shape, cold): 45.7 us at up to 512 threads per workgroup, 42.6 at 256,
 // 41.2 at 128, 48.3 at 64; CSR bags of 0..40 rows 55.7 -> 48.4 us, since a
 // group's several bags even out their sizes.  Small workgroups let many
-// resident workgroups interleave their gather and dot phases on a CU.
+// resident workgroups interleave their gather and dot phases on a CU.  A
+// grid that leaves the chip idle takes larger ones (below): measured cold at
+// K = 32, D = 64, 20 Zipf indices per bag, B = 2: 20.4 -> 10.7 us, B = 256:
+// 21.8 -> 12.8, B = 1024: 28.6 -> 25.4 (K = 26: 19.5 -> 10.2, 20.2 -> 11.7,
+// 26.4 -> 22.9), B >= 2048 unchanged; fill thresholds of 2048 and 8192
+// waves were each slower somewhere.
 #ifndef DLRM_MAX_THREADS
 #define DLRM_MAX_THREADS 128
+#endif
+#ifndef DLRM_WAVE_FILL
+#define DLRM_WAVE_FILL 4096
 #endif
 
 bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, int &threads) {
@@ -251,9 +259,16 @@ bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, i
          S < B)
     S *= 2;
   ip.S = S;
-  int want = S * lanes_per_sample;
-  if (want > DLRM_MAX_THREADS) want = DLRM_MAX_THREADS;
-  threads = ((want + kWave - 1) / kWave) * kWave;
+  // Workgroup size: DLRM_MAX_THREADS when the grid fills the chip, so that
+  // many resident workgroups interleave their gather and dot phases; when it
+  // does not (fewer than DLRM_WAVE_FILL waves at the next size up), doubled
+  // up to all of a sample's lane groups at once, so that its bags are pooled
+  // side by side instead of in turn by a few groups.
+  const int want = S * lanes_per_sample;
+  const int64_t nwg = (B + S - 1) / S;
+  int cap = DLRM_MAX_THREADS;
+  while (cap < want && 2 * cap <= 1024 && nwg * (2 * cap / kWave) <= DLRM_WAVE_FILL) cap *= 2;
+  threads = ((min(want, cap) + kWave - 1) / kWave) * kWave;
   if (threads < DLRM_MIN_THREADS) threads = DLRM_MIN_THREADS;
   ip.lds_bytes = (int)(S * per_sample);
   // Quads per 4 x 4 block team: the most that still covers every block of the
