@@ -22,6 +22,9 @@
 // (rows past the matrix are clamped and their outputs masked at the store);
 // only the last, partial slab tests k.  Tiles are assigned to XCDs in
 // contiguous m-major runs so the workgroups that share rows of A share an L2.
+// The 64-row tiles, chosen when larger ones would leave CUs idle, run on two
+// wave groups that split each slab's k and add their partial tiles through
+// LDS in group order (measured at M = 256: 512 -> 256 10.5 -> 9.2 us).
 //
 // Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
 // bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
@@ -48,6 +51,9 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 #ifndef DLRM_GEMM_BK
 #define DLRM_GEMM_BK 32
+#endif
+#ifndef DLRM_GEMM_KSPLIT
+#define DLRM_GEMM_KSPLIT 2
 #endif
 constexpr int kBK = DLRM_GEMM_BK;   // k per LDS slab
 constexpr int kLdsStride = kBK + 4;
@@ -132,21 +138,29 @@ __device__ __forceinline__ float4 load_a_tail(const ASrc &a, int row, int k, int
   }
 }
 
-template <int BM, int BN, int GM, int GN, bool VA, bool VW, bool VC, bool SPLIT>
-__global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K, const ASrc A,
-                                                            const float *__restrict__ W,
-                                                            const float *__restrict__ bias,
-                                                            int act, float *__restrict__ C,
-                                                            int64_t ldc, int tiles_n,
-                                                            int xcd_chunk) {
-  constexpr int NT = 64 * GM * GN;         // threads
-  constexpr int WM = BM / GM, WN = BN / GN;  // wave tile (GM x GN waves)
+template <int BM, int BN, int GM, int GN, int KS, bool VA, bool VW, bool VC, bool SPLIT>
+__global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, int K,
+                                                                 const ASrc A,
+                                                                 const float *__restrict__ W,
+                                                                 const float *__restrict__ bias,
+                                                                 int act, float *__restrict__ C,
+                                                                 int64_t ldc, int tiles_n,
+                                                                 int xcd_chunk) {
+  // KS wave groups split k: a staged slab holds KS x kBK columns and group g
+  // multiplies columns [g kBK, (g + 1) kBK) of it; the groups' partial tiles
+  // are added in group order through LDS at the end.
+  constexpr int NT = 64 * GM * GN * KS;    // threads
+  constexpr int SK = kBK * KS;             // k per staged slab
+  constexpr int STR = SK + 4;              // LDS row stride (4 mod 32 banks, as kLdsStride)
+  constexpr int WM = BM / GM, WN = BN / GN;  // wave tile (GM x GN waves per group)
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int A_V4 = BM * kBK / 4 / NT;  // float4 loads per thread per slab
-  constexpr int W_V4 = BN * kBK / 4 / NT;
+  constexpr int A_V4 = BM * SK / 4 / NT;   // float4 loads per thread per slab
+  constexpr int W_V4 = BN * SK / 4 / NT;
   static_assert(A_V4 >= 1 && W_V4 >= 1 && TM >= 1 && TN >= 1, "tile too small");
-  static_assert(A_V4 * NT * 4 == BM * kBK && W_V4 * NT * 4 == BN * kBK, "tile split");
-  constexpr int A_ELEMS = BM * kLdsStride, W_ELEMS = BN * kLdsStride;
+  static_assert(A_V4 * NT * 4 == BM * SK && W_V4 * NT * 4 == BN * SK, "tile split");
+  constexpr int A_ELEMS = BM * STR, W_ELEMS = BN * STR;
+  static_assert(KS == 1 || (KS - 1) * GM * GN * TM * TN * 4 * 64 <= 2 * (A_ELEMS + W_ELEMS),
+                "the partial tiles of groups 1.. must fit the slab buffers");
 
   // Two LDS buffers: slab s+1 is stored while slab s is multiplied.
   __shared__ float lds[2 * (A_ELEMS + W_ELEMS)];
@@ -162,7 +176,9 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / GN, wn = wave - (wave / GN) * GN;
+  const int kg = wave / (GM * GN);       // k group
+  const int wg = wave - kg * (GM * GN);  // wave within the group
+  const int wm = wg / GN, wn = wg - (wg / GN) * GN;
   const int l16 = lane & 15, lq = lane >> 4;
 
   // Rows each thread stages; rows past the matrix are clamped to its last row
@@ -171,14 +187,14 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
 #pragma unroll
   for (int i = 0; i < A_V4; ++i) {
     const int v = tid + NT * i;
-    arow[i] = min(m0 + v / (kBK / 4), M - 1);
-    acol[i] = 4 * (v % (kBK / 4));
+    arow[i] = min(m0 + v / (SK / 4), M - 1);
+    acol[i] = 4 * (v % (SK / 4));
   }
 #pragma unroll
   for (int i = 0; i < W_V4; ++i) {
     const int v = tid + NT * i;
-    wrow[i] = min(n0 + v / (kBK / 4), N - 1);
-    wcol[i] = 4 * (v % (kBK / 4));
+    wrow[i] = min(n0 + v / (SK / 4), N - 1);
+    wcol[i] = 4 * (v % (SK / 4));
   }
 
   floatx4 acc[TM][TN];
@@ -187,10 +203,10 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nfull = K / kBK;                   // slabs inside K
-  const int nslab = (K + kBK - 1) / kBK;
+  const int nfull = K / SK;                    // slabs inside K
+  const int nslab = (K + SK - 1) / SK;
   auto fetch = [&](int sl, float4 (&ra)[A_V4], float4 (&rw)[W_V4]) {
-    const int kb = sl * kBK;
+    const int kb = sl * SK;
     if (sl < nfull) {
 #pragma unroll
       for (int i = 0; i < A_V4; ++i) ra[i] = load_a_full<SPLIT, VA>(A, arow[i], kb + acol[i]);
@@ -209,25 +225,26 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
 #pragma unroll
     for (int i = 0; i < A_V4; ++i) {
       const int v = tid + NT * i;
-      *reinterpret_cast<float4 *>(&As[(v / (kBK / 4)) * kLdsStride + acol[i]]) = ra[i];
+      *reinterpret_cast<float4 *>(&As[(v / (SK / 4)) * STR + acol[i]]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < W_V4; ++i) {
       const int v = tid + NT * i;
-      *reinterpret_cast<float4 *>(&Ws[(v / (kBK / 4)) * kLdsStride + wcol[i]]) = rw[i];
+      *reinterpret_cast<float4 *>(&Ws[(v / (SK / 4)) * STR + wcol[i]]) = rw[i];
     }
   };
-  // Fragments of one k-quad block (16 k) of the current slab.
+  // Fragments of one k-quad block (16 k) of the group's part of the slab.
+  const int kgo = kg * kBK;
   auto frags = [&](const float *As, const float *Ws, int kq, float4 (&af)[TM],
                    float4 (&wf)[TN]) {
 #pragma unroll
     for (int a = 0; a < TM; ++a)
       af[a] = *reinterpret_cast<const float4 *>(
-          &As[(wm * WM + a * 16 + l16) * kLdsStride + kq + 4 * lq]);
+          &As[(wm * WM + a * 16 + l16) * STR + kgo + kq + 4 * lq]);
 #pragma unroll
     for (int b = 0; b < TN; ++b)
       wf[b] = *reinterpret_cast<const float4 *>(
-          &Ws[(wn * WN + b * 16 + l16) * kLdsStride + kq + 4 * lq]);
+          &Ws[(wn * WN + b * 16 + l16) * STR + kgo + kq + 4 * lq]);
   };
   // 4 MFMA steps over the 4 k of each lane's float4, component-major so
   // consecutive MFMAs never share an accumulator.
@@ -289,6 +306,34 @@ __global__ __launch_bounds__(64 * GM * GN) void gemm_kernel(int M, int N, int K,
     compute(1);
     if (sl + 2 < nslab) stash(0, ra0, rw0);
     __syncthreads();
+  }
+
+  if constexpr (KS > 1) {
+    // Groups 1.. park their partial tiles in the (now idle) slab buffers;
+    // group 0 adds them in group order and stores.  The loop ended on a
+    // barrier, so every wave is done reading the buffers.
+    constexpr int PER = TM * TN * 4;  // floats per lane of one wave's tile
+    if (kg > 0) {
+      float *red = lds + ((size_t)((kg - 1) * GM * GN + wg) * PER) * 64 + lane;
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[((a * TN + b) * 4 + v) * 64] = acc[a][b][v];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int g = 1; g < KS; ++g) {
+      const float *red = lds + ((size_t)((g - 1) * GM * GN + wg) * PER) * 64 + lane;
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[a][b][v] += red[((a * TN + b) * 4 + v) * 64];
+    }
   }
 
   // Epilogue: lane holds C[m][n .. n+3] for m = .. + l16, n = .. + 4*lq.
@@ -427,16 +472,16 @@ __global__ __launch_bounds__(256) void thin_k_kernel(int M, int N, const ASrc A,
   }
 }
 
-template <int BM, int BN, int GM, int GN, bool SPLIT>
+template <int BM, int BN, int GM, int GN, bool SPLIT, int KS = 1>
 hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, const float *W, const float *bias,
                            int act, float *C, int64_t ldc, bool va, bool vw, bool vc,
                            hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   const int xcd_chunk = (tiles % 8 == 0) ? (int)(tiles / 8) : 0;
-  dim3 grid((unsigned)tiles), block(64 * GM * GN);
-#define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                       \
-  launch_kernel((gemm_kernel<BM, BN, GM, GN, A_, W_, C_, SPLIT>), grid, block, 0, stream,  \
+  dim3 grid((unsigned)tiles), block(64 * GM * GN * KS);
+#define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                          \
+  launch_kernel((gemm_kernel<BM, BN, GM, GN, KS, A_, W_, C_, SPLIT>), grid, block, 0, stream, \
                 M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk)
   if (va && vw && vc)
     DLRM_GEMM_LAUNCH(true, true, true);
@@ -536,9 +581,21 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
   if (forced == 0 && tiles(128, 64) >= 256)
     return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                  stream);
-  if (forced == 3 || (forced == 0 && tiles(64, 64) >= 256))
+  // The 64-row tiles leave one wave per SIMD: with K of at least two staged
+  // slabs, KS wave groups split each tile's k (KS times the waves, 1/KS of
+  // the MFMA chain and of the slab round trips).
+  constexpr int KS = DLRM_GEMM_KSPLIT;
+  const bool ksplit = KS > 1 && K >= 2 * kBK * KS;
+  if (forced == 3 || (forced == 0 && tiles(64, 64) >= 256)) {
+    if (ksplit)
+      return launch_gemm_cfg<64, 64, 2, 2, SPLIT, KS>(M, N, K, A, W, bias, act, C, ldc, va, vw,
+                                                      vc, stream);
     return launch_gemm_cfg<64, 64, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                 stream);
+  }
+  if (ksplit)
+    return launch_gemm_cfg<64, 32, 2, 2, SPLIT, KS>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
+                                                    stream);
   return launch_gemm_cfg<64, 32, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                               stream);
 }

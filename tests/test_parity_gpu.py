@@ -200,6 +200,9 @@ LINEAR_SHAPES = [  # (M, N, K)
     (300, 1, 256), (37, 19, 13), (129, 130, 131), (64, 8, 5), (1, 1, 1), (5, 9, 3),
     (257, 128, 64), (70, 3, 40), (513, 72, 36),
     (33, 22, 16), (40, 2, 600), (2000, 516, 16), (77, 4, 512),
+    # 64-row tiles with two wave groups splitting k (K >= 128): 64 x 64 and
+    # 64 x 32 tiles, ragged M, N and K, K = 128 exactly (two half slabs)
+    (2048, 512, 415), (2048, 256, 512), (2100, 520, 200), (600, 96, 128), (300, 70, 127),
     # K <= 16 with N % 4 == 0 (the register-weight kernel): partial column
     # groups, K = 1, a ragged last row batch
     (37, 12, 13), (130, 1024, 7), (5, 260, 1), (1, 256, 16), (9, 20, 4),

@@ -21,6 +21,7 @@ SPLIT_SHAPES = [  # (M, N, K_lo, K_hi)
     (130, 5, 64, 351),       # N <= 8: the matrix-vector kernel
     (9, 3, 5, 2),            # tiny, N <= 8, unaligned
     (300, 256, 128, 300),    # two full slabs then a tail
+    (2048, 512, 64, 351),    # 64 x 64 tiles with k split over two wave groups
     (50, 40, 5, 6),          # K <= 16: the register-weight kernel
     (50, 40, 9, 7),          # K = 16, one row per wave
     (21, 12, 13, 1),         # K = 14, ragged
