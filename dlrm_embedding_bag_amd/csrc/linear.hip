@@ -15,8 +15,8 @@
 //
 // Tiles: BM x BN per workgroup of GM x GN waves (128 x 128 on 2 x 4 waves,
 // 128 x 64 on 4 x 2, 64 x 64 or 64 x 32 on 2 x 2), BK = 32 staged through
-// two LDS buffers (row stride 36 floats: the 16 rows a ds_read_b128 touches
-// start on different banks): k-slabs are loaded into registers two slabs
+// two LDS buffers (row stride BK + 4 floats: the 16 rows a ds_read_b128
+// touches start on different banks): k-slabs are loaded into registers two slabs
 // ahead and stored to the other LDS buffer while the current one is
 // multiplied, one barrier per slab.  Full slabs load without bounds tests
 // (rows past the matrix are clamped and their outputs masked at the store);
@@ -56,7 +56,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 #define DLRM_GEMM_KSPLIT 2
 #endif
 constexpr int kBK = DLRM_GEMM_BK;   // k per LDS slab
-constexpr int kLdsStride = kBK + 4;
 
 __device__ __forceinline__ float apply_act(float x, int act) {
   if (act == 1) return x > 0.0f ? x : 0.0f;
@@ -151,7 +150,8 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
   // are added in group order through LDS at the end.
   constexpr int NT = 64 * GM * GN * KS;    // threads
   constexpr int SK = kBK * KS;             // k per staged slab
-  constexpr int STR = SK + 4;              // LDS row stride (4 mod 32 banks, as kLdsStride)
+  constexpr int STR = SK + 4;              // LDS row stride: 4 mod 32 banks, so the 16 rows
+                                           // a ds_read_b128 touches start on different banks
   constexpr int WM = BM / GM, WN = BN / GN;  // wave tile (GM x GN waves per group)
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int A_V4 = BM * SK / 4 / NT;   // float4 loads per thread per slab
