@@ -66,3 +66,30 @@ def test_graph_plan_created_with_timing_on():
         plan.close()
     finally:
         timer.close()
+
+
+def test_direct_plan_replay_records_the_last_kernel():
+    import torch
+    w = inputs.Workload("timing-plan", batch=512, num_tables=8, rows=2000, dim=64, bag=10,
+                        dist="zipf", dense_in=13, bottom=(128, 64), top=(64, 1))
+    tables = [inputs.table_host(w, k) for k in range(w.num_tables)]
+    bottom, top = inputs.dlrm_layers(w, bias_std=0.1)
+    model = abi.DlrmModel([(dev(a), dev(b), act) for a, b, act in bottom],
+                          [(dev(a), dev(b), act) for a, b, act in top],
+                          [dev(t) for t in tables])
+    dense = dev(inputs.dense(w))
+    idx = [dev(inputs.indices(w, k)) for k in range(w.num_tables)]
+    eager = host(abi.dlrm_forward(model, dense, idx))
+    out = torch.empty(eager.shape, dtype=torch.float32, device="cuda")
+    plan = abi.DlrmPlan(model, dense, idx, out=out, mode="direct")
+    timer = _timer(1)
+    try:
+        timer.arm(0)
+        plan.run()
+        timer.disarm()
+        torch.cuda.synchronize()
+        assert 0.0 < timer.elapsed_ms(0) < 100.0
+        assert np.array_equal(host(out), eager)
+    finally:
+        timer.close()
+        plan.close()
