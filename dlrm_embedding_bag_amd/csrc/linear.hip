@@ -415,13 +415,15 @@ template <int K, bool SPLIT>
 constexpr int thin_rows() {
   return SPLIT ? (K > 13 ? 1 : 2) : 4;
 }
-
-template <int K, bool SPLIT>
+template <int K, bool SPLIT, int NB>
 __global__ __launch_bounds__(256) void thin_k_kernel(int M, int N, const ASrc A,
                                                      const float *__restrict__ W,
                                                      const float *__restrict__ bias, int act,
                                                      float *__restrict__ C, int64_t ldc,
                                                      int col_groups, int xcd_run) {
+  // A wave computes NB batches of RB rows with the same weights in registers
+  // (a compile-time count, so the next batch's row loads can be issued
+  // early).
   constexpr int RB = thin_rows<K, SPLIT>();
   // XCD-aware order: workgroup i runs on XCD i % 8 and takes the i / 8-th of
   // that XCD's contiguous run of workgroups, so each XCD writes a contiguous
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(256) void thin_k_kernel(int M, int N, const ASrc A,
                                                   (int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int cg = wave % col_groups;
-  const int m0 = (wave / col_groups) * RB;
-  if (m0 >= M) return;
+  const int mw = (wave / col_groups) * RB * NB;
+  if (mw >= M) return;
   const int n = cg * 256 + 4 * lane;
   const bool live = n < N;  // N % 4 == 0: a live lane owns 4 real columns
   float w[4][K];
@@ -444,30 +446,36 @@ __global__ __launch_bounds__(256) void thin_k_kernel(int M, int N, const ASrc A,
     for (int k = 0; k < K; ++k) w[j][k] = W[(int64_t)(nl + j) * K + k];
     bv[j] = bias ? bias[nl + j] : 0.0f;
   }
-  const int rows = min(RB, M - m0);
-  float av[RB][K];
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int64_t m = m0 + min(r, rows - 1);  // rows past M repeat the last one
+  for (int bt = 0; bt < NB; ++bt) {
+    const int m0 = mw + bt * RB;
+    if (m0 >= M) break;
+    const int rows = min(RB, M - m0);
+    float av[RB][K];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      av[r][k] = (SPLIT && k >= A.k_lo) ? A.hi[m * A.ld_hi + (k - A.k_lo)] : A.lo[m * A.ld_lo + k];
-  }
+    for (int r = 0; r < RB; ++r) {
+      const int64_t m = m0 + min(r, rows - 1);  // rows past M repeat the last one
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    if (r >= rows) break;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k = 0; k < K; ++k)
+        av[r][k] = (SPLIT && k >= A.k_lo) ? A.hi[m * A.ld_hi + (k - A.k_lo)]
+                                          : A.lo[m * A.ld_lo + k];
+    }
 #pragma unroll
-    for (int k = 0; k < K; ++k)
+    for (int r = 0; r < RB; ++r) {
+      if (r >= rows) break;
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(av[r][k], w[j][k], acc[j]);
-    if (live) {
-      float4 o;
-      o.x = apply_act(acc[0] + bv[0], act);
-      o.y = apply_act(acc[1] + bv[1], act);
-      o.z = apply_act(acc[2] + bv[2], act);
-      o.w = apply_act(acc[3] + bv[3], act);
-      *reinterpret_cast<float4 *>(C + (int64_t)(m0 + r) * ldc + n) = o;
+      for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_fmaf(av[r][k], w[j][k], acc[j]);
+      if (live) {
+        float4 o;
+        o.x = apply_act(acc[0] + bv[0], act);
+        o.y = apply_act(acc[1] + bv[1], act);
+        o.z = apply_act(acc[2] + bv[2], act);
+        o.w = apply_act(acc[3] + bv[3], act);
+        *reinterpret_cast<float4 *>(C + (int64_t)(m0 + r) * ldc + n) = o;
+      }
     }
   }
 }
@@ -523,10 +531,20 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
     auto run = [&](auto kc) -> hipError_t {
       constexpr int KK = decltype(kc)::value;
       constexpr int rb = thin_rows<KK, SPLIT>();
-      const int64_t waves = (int64_t)((M + rb - 1) / rb) * col_groups;
+      // Two row batches per wave halve the weight loads but also the waves:
+      // taken while 2048 waves remain (measured at 13 -> 512: M = 8192
+      // 10.0 -> 9.3 us, M = 16384 15.3 -> 12.7; at M = 2048 5.4 -> 6.3, so
+      // one batch there; four batches were slower everywhere).
+      const int64_t waves2 = (int64_t)((M + 2 * rb - 1) / (2 * rb)) * col_groups;
+      const int batches = waves2 >= 2048 ? 2 : 1;
+      const int64_t waves = (int64_t)((M + batches * rb - 1) / (batches * rb)) * col_groups;
       const int64_t xcd_run = ((waves + 3) / 4 + 7) / 8;  // workgroups per XCD
-      launch_kernel((thin_k_kernel<KK, SPLIT>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
-                    stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
+      if (batches == 2)
+        launch_kernel((thin_k_kernel<KK, SPLIT, 2>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
+                      stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
+      else
+        launch_kernel((thin_k_kernel<KK, SPLIT, 1>), dim3((unsigned)(xcd_run * 8)), dim3(256), 0,
+                      stream, M, N, A, W, bias, act, C, ldc, col_groups, (int)xcd_run);
       return hipGetLastError();
     };
     switch (K) {

@@ -206,6 +206,8 @@ LINEAR_SHAPES = [  # (M, N, K)
     # K <= 16 with N % 4 == 0 (the register-weight kernel): partial column
     # groups, K = 1, a ragged last row batch
     (37, 12, 13), (130, 1024, 7), (5, 260, 1), (1, 256, 16), (9, 20, 4),
+    # two row batches per wave (enough rows for 2048 waves), ragged last batch
+    (8192, 512, 13), (8195, 260, 5),
 ]
 
 

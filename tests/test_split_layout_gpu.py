@@ -22,6 +22,7 @@ SPLIT_SHAPES = [  # (M, N, K_lo, K_hi)
     (9, 3, 5, 2),            # tiny, N <= 8, unaligned
     (300, 256, 128, 300),    # two full slabs then a tail
     (2048, 512, 64, 351),    # 64 x 64 tiles with k split over two wave groups
+    (16402, 64, 8, 5),       # K <= 16 split: two row batches per wave, ragged
     (50, 40, 5, 6),          # K <= 16: the register-weight kernel
     (50, 40, 9, 7),          # K = 16, one row per wave
     (21, 12, 13, 1),         # K = 14, ragged
