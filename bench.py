@@ -31,7 +31,7 @@ batch) per call, eager dlrm_forward against a graph-replayed plan, and
 (dlrm_forward), with each MLP layer timed alone against the f32 MFMA peak
 (or HBM for the layers below the ridge point).
 
-Options: --workload {nc32,nc32-uniform,mid,tiny,large} (or one variant,
+Options: --workload {nc32,nc32-uniform,mid,tiny,large,large-uniform} (or one variant,
 nc32-bf16 / nc32-fp8 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-variants,
 --no-cells,
 --sweep (batch x

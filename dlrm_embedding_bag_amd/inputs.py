@@ -100,6 +100,10 @@ WORKLOADS = {
         dist="zipf", table_source="device",
         description="B=16384, K=26 tables x 4,000,000 rows x D=128 (~53 GB), "
                     "40 indices/bag Zipf(1.05)"),
+    "large-uniform": Workload(
+        "large-uniform", batch=16384, num_tables=26, rows=4_000_000, dim=128, bag=40,
+        dist="uniform", table_source="device",
+        description="large with uniform indices (no hot rows)"),
     "nc32-bf16": Workload(
         "nc32-bf16", batch=2048, num_tables=32, rows=1_000_000, dim=64, bag=20,
         dist="zipf", table_source="device", table_dtype="bf16",
