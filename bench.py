@@ -413,6 +413,9 @@ def bench_emb_interact(args, stream):
         extra["rows"] = res_rows
     if not args.profile_run and w.name == "nc32":
         extra["uniform"] = bench_uniform(case, args, stream, flush, cold)
+    if not args.profile_run:
+        extra["host_inclusive_us"] = host_inclusive_time(case, args.steps, cold, flush,
+                                                         stream) * 1e3
     khash = kernel_source_hash()
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS,
@@ -444,6 +447,7 @@ def bench_emb_interact(args, stream):
                       "index_batches": args.batches},
            "roofline": roofline, "extra": extra}
     if not args.profile_run:
+        extra["device"] = device_info()
         extra["copy_gbps"] = copy_rate(stream)
         log(f"practical HBM: a 1 GiB device copy moves {extra['copy_gbps']:.0f} GB/s")
     if not args.no_cpu_baseline and not args.profile_run:
@@ -929,6 +933,37 @@ def copy_rate(stream, mib=1024, reps=10):
         e1.record(stream)
     torch.cuda.synchronize()
     return 2 * (mib << 20) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def host_inclusive_time(case, steps, cold, flush_buf, stream):
+    """Median wall time (ms) of one call plus the stream synchronization that
+    waits for it: what a caller that needs the result on return sees."""
+    import torch
+    times = []
+    with torch.cuda.stream(stream):
+        for s in range(steps):
+            if cold:
+                flush_buf.max()
+            stream.synchronize()
+            t0 = time.perf_counter()
+            case.run(s)
+            stream.synchronize()
+            times.append(time.perf_counter() - t0)
+    return statistics.median(times) * 1e3
+
+
+def device_info():
+    """The platform figures the rooflines assume, as the runtime reports them."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory, "warp_size": getattr(p, "warp_size", None)}
+    for key in ("L2_cache_size", "shared_memory_per_block", "shared_memory_per_multiprocessor",
+                "max_threads_per_multi_processor", "regs_per_multiprocessor"):
+        if hasattr(p, key):
+            info[key] = getattr(p, key)
+    return info
 
 
 def bench_uniform(case, args, stream, flush, cold):
