@@ -239,7 +239,15 @@ class KernelTimer:
         from dlrm_embedding_bag_amd import abi
         torch.cuda.init()
         self.abi = abi
-        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip = None
+        for name in ("libamdhip64.so.7", "libamdhip64.so"):
+            try:
+                self.hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if self.hip is None:
+            raise RuntimeError("the HIP runtime library is not loadable")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
