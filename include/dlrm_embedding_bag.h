@@ -86,10 +86,12 @@ DLRM_API int dlrm_abi_version(void);
  *                or both NULL to switch timing off (the initial state).
  *
  * While set, every kernel that this library launches from the calling
- * thread is dispatched with hipExtLaunchKernel and records `start` at the
- * kernel's beginning and `stop` at its end, so after a call that launches
- * one kernel, hipEventElapsedTime(start, stop) is that kernel's execution
- * time; after a call that launches several, it is the last one's.  The
+ * thread is dispatched with hipExtLaunchKernel, which records `start` and
+ * `stop` with that dispatch, so after a call that launches one kernel,
+ * hipEventElapsedTime(start, stop) times that kernel without the gap that
+ * events recorded around the call include (measured within a few percent
+ * of a profiler's dispatch time); after a call that launches several, it
+ * times the last one.  The
  * setting is per thread; the events stay owned by the caller, who must
  * switch timing off before destroying them.  Graph-mode plans capture
  * plain launches whatever the setting.  Returns DLRM_ERR_NULL when exactly
