@@ -76,7 +76,7 @@ DLRM_API int dlrm_abi_version(void);
 #define DLRM_ABI_VERSION 1
 
 /*
- * dlrm_set_kernel_timing_events -- kernel-exact timing for benchmarks.
+ * dlrm_set_kernel_timing_events -- per-kernel timing for benchmarks.
  * (Measurement support, not a step of the method: the pages time whole
  * forwards with CUDA events, RESULTS.md of [FASTPATHS]; this times one
  * kernel without the dispatch gap that events recorded around a call
@@ -91,11 +91,11 @@ DLRM_API int dlrm_abi_version(void);
  * hipEventElapsedTime(start, stop) times that kernel without the gap that
  * events recorded around the call include (measured within a few percent
  * of a profiler's dispatch time); after a call that launches several, it
- * times the last one.  The
- * setting is per thread; the events stay owned by the caller, who must
- * switch timing off before destroying them.  Graph-mode plans capture
- * plain launches whatever the setting.  Returns DLRM_ERR_NULL when exactly
- * one of the two is NULL (nothing changes), else DLRM_OK.
+ * times the last one.  The setting is per thread; the events stay owned by
+ * the caller, who must switch timing off before destroying them.  Graph-mode
+ * plans capture plain launches whatever the setting; a caller capturing its
+ * own stream must switch timing off first.  Returns DLRM_ERR_NULL when
+ * exactly one of the two is NULL (nothing changes), else DLRM_OK.
  */
 DLRM_API int dlrm_set_kernel_timing_events(void *start, void *stop);
 
