@@ -79,7 +79,11 @@ __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractPar
     }
   }
 
-  // Phase 1b: pooled rows -> features 1..K.
+  // Phase 1b: pooled rows -> features 1..K.  The gather runs at raised wave
+  // priority, so a CU issues the row loads of waves still gathering ahead of
+  // other waves' dot arithmetic and its L1 miss queue stays full (measured:
+  // nc32 41.5 -> 41.1 us, B = 512 17.4 -> 16.9; no change in load mode).
+  if constexpr (MODE == MODE_FUSED) __builtin_amdgcn_s_setprio(1);
   const int G = ip.G;
   const int groups = nthreads / G;
   const int g = threadIdx.x / G;
@@ -127,7 +131,8 @@ __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractPar
   }
   __syncthreads();
 
-  // Phase 2: the strict-lower-triangle dots.
+  // Phase 2: the strict-lower-triangle dots, at normal priority.
+  if constexpr (MODE == MODE_FUSED) __builtin_amdgcn_s_setprio(0);
   float *out0 = ip.out + (int64_t)b0 * ip.ld_out + ip.dot_off;
   const int nvalid = min(S, B - b0);
   if constexpr (VW == 4)
