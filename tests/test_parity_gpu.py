@@ -338,3 +338,22 @@ def test_forward_small(B, K, D, L):
     offs = [dev(inputs.offsets(w)) for _ in range(K)]
     got2 = host(abi.dlrm_forward(model, dev(dense), [dev(i) for i in idx], offsets=offs))
     assert np.array_equal(got, got2)
+
+
+@pytest.mark.parametrize("B", [40, 700, 1100])
+def test_emb_interact_workgroup_sizes_bit_exact(B):
+    """K = 32, D = 64: the fused launch takes 512-thread workgroups at B = 40,
+    256 at B = 700 and 128 at B = 1100 (workgroups grow while the grid leaves
+    CUs idle); dyadic inputs make every summation order exact, so each size
+    must give the oracle's bits, and the standalone gather + interaction the
+    same."""
+    w = W(batch=B, num_tables=32, rows=300, dim=64, bag=20, dist="zipf")
+    tables, idx, dense = make_uniform_case(w, seed=B, dyadic=True)
+    E = oracle.emb_bag_sum(tables, idx, batch=B)
+    want = oracle.interact(dense, E)
+    td = [dev(t) for t in tables]
+    xd = [dev(i) for i in idx]
+    got = host(abi.dlrm_emb_interact(td, xd, dev(dense)))
+    assert np.array_equal(got, want)
+    unfused = host(abi.dlrm_interact_lower_tri(dev(dense), abi.emb_bag_sum_multi(td, xd, batch=B)))
+    assert np.array_equal(unfused, want)
