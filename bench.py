@@ -23,8 +23,13 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                 matches the current kernel source, else null
   cpu_baseline  the CPU oracle timed on the host on the same workload
 
+`extra` carries the warm step, the stacked-table layout, the gather and the
+interaction as separate calls (`rows`), the same launch with uniform indices
+(`uniform`, no hot rows), the host-inclusive call time, a plain device
+copy's rate and the device properties the rooflines assume.
+
 The JSON line also carries `variants`: the same fused launch with bfloat16
-tables, mean pooling, per-sample weights and CSR bags of size 0..40
+tables, FP8 tables, mean pooling, per-sample weights and CSR bags of size 0..40
 (dlrm_emb_interact_pool), `cells`: the pages' small DLRMv1 cells (nc x
 batch) per call, eager dlrm_forward against a graph-replayed plan, and
 `forward`: the full DLRMv1 forward at B=8192
