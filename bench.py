@@ -16,11 +16,18 @@ skips the flush.
 Prints ONE JSON line on stdout (progress goes to stderr):
   value         samples/s = B / mean event-timed step time
   ms_per_step   mean event-timed step time
-  roofline      achieved = algorithmic bytes per launch / mean kernel time
-                (events recorded by the launch itself, as rocprofv3 times the
-                kernel), against MI355X's 8 TB/s HBM peak; traffic = HBM
-                bytes from the committed rocprofv3 counter summary when it
-                matches the current kernel source, else null
+  roofline      the fused kernel against MI355X's 8 TB/s HBM peak, with its
+                own duration (events recorded by the launch itself, as
+                rocprofv3 times the kernel).  `achieved` counts bytes that the
+                memory side served: the copy-calibrated rocprofv3 FETCH_SIZE +
+                WRITE_SIZE of profiles/counters.json when they were taken on
+                the current kernel sources (`traffic`), else the compulsory
+                bytes (each distinct row once + indices + dense + output);
+                `byte_model` says which.  The logical bytes (every gathered
+                row counted each time: the survey's algorithmic bytes) give
+                `logical_gbps`, an L2-assisted rate that is not an HBM rate.
+                `practical_peak_gbps` is the library's streaming-read kernel
+                over 4 GiB.
   cpu_baseline  the CPU oracle timed on the host on the same workload
 
 `extra` carries the warm step, the stacked-table layout, the gather and the
@@ -200,10 +207,20 @@ class EmbInteractCase:
     def bytes_per_launch(self):
         return self.B * emb_interact_bytes_per_sample(self.K, self.D, self.L)
 
-    def distinct_rows_fraction(self, nb=0):
-        idx = self.batches[nb][0]
-        n = sum(int(i.unique().numel()) for i in idx)
-        return n / (self.B * self.K * self.L)
+    def distinct_rows_fraction(self):
+        """Distinct (table, row) pairs per gathered row, averaged over the
+        rotating index batches."""
+        fr = []
+        for idx, *_ in self.batches:
+            n = sum(int(i.unique().numel()) for i in idx)
+            fr.append(n / (self.B * self.K * self.L))
+        return statistics.mean(fr)
+
+    def compulsory_bytes_per_launch(self, distinct_fraction):
+        """What HBM must deliver at least with cold caches: every distinct row
+        once, plus the indices, the dense input and the output."""
+        rows = distinct_fraction * self.B * self.K * self.L * self.D * 4
+        return int(rows + self.B * (self.K * self.L * 4 + self.D * 4 + (self.D + self.P) * 4))
 
 
 def time_steps(case, steps, warmup, cold, flush_buf, stream):
@@ -361,7 +378,66 @@ def cpu_baseline(case, max_seconds=20.0):
             "max_abs_diff_vs_gpu": err}
 
 
+def forward_cpu_baseline(w, tables_dev, idx_host, dense_host, bottom, top, out_gpu,
+                         max_seconds=20.0, seed=0):
+    """The CPU oracle's whole DLRMv1 forward (oracle.forward: fp64 sums,
+    single-threaded C, pinned to one core) on a bounded prefix of the same
+    batch.  The sample's tables are cut down to the rows its bags touch
+    (indices renumbered), which leaves every pooled sum unchanged and keeps
+    host memory small; repeated until ~10 s of CPU work, median run; also the
+    largest difference from the GPU forward on those samples."""
+    import numpy as np
+    import torch
+    import oracle
+    B, L = w.batch, w.bag
+
+    def cut(samples):
+        subs, sidx = [], []
+        for t, idx in zip(tables_dev, idx_host):
+            bags = idx[:samples * L]
+            rows = np.unique(bags)
+            subs.append(t.index_select(0, torch.from_numpy(rows.astype(np.int64)).to(t.device))
+                        .cpu().numpy())
+            sidx.append(np.searchsorted(rows, bags).astype(np.int32))
+        return subs, sidx
+
+    probe = 64
+    subs, sidx = cut(probe)
+    t0 = time.perf_counter()
+    oracle.forward(dense_host[:probe], bottom, top, subs, sidx)
+    per = (time.perf_counter() - t0) / probe
+    samples = min(B, max(probe, int(max_seconds / per)))
+    subs, sidx = cut(samples)
+    prev = os.sched_getaffinity(0)
+    core = min(prev)
+    os.sched_setaffinity(0, {core})
+    runs = []
+    try:
+        while True:
+            t0 = time.perf_counter()
+            want, _, _ = oracle.forward(dense_host[:samples], bottom, top, subs, sidx)
+            runs.append(time.perf_counter() - t0)
+            if sum(runs) >= 10.0:
+                break
+    finally:
+        os.sched_setaffinity(0, prev)
+    t = statistics.median(runs)
+    got = out_gpu[:samples]
+    err = float(np.abs(got - want).max())
+    ok = bool(np.all(np.abs(got - want) <= 1e-5 + 1e-5 * np.abs(want)))
+    log(f"forward cpu baseline: {samples / t:.0f} samples/s on one core ({samples} samples), "
+        f"max abs diff vs GPU {err:.2e}")
+    return {"value": samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+            "sample": f"the first {samples} of {B} samples of the same forward batch (tables cut "
+                      f"to the rows their bags touch), single-threaded C oracle (fp64 sums) "
+                      f"pinned to core {core} of {len(prev)} available, median of {len(runs)} "
+                      f"run(s) of {t:.3f} s",
+            "max_abs_diff_vs_gpu": err, "within_tolerance": ok}
+
+
 def read_traffic(kernel_hash, workload):
+    """The committed counter record of `workload` (profiles/counters.json)
+    if it was taken on the current kernel sources, else None."""
     try:
         with open(COUNTERS_JSON) as f:
             c = json.load(f)
@@ -370,7 +446,75 @@ def read_traffic(kernel_hash, workload):
     entry = c.get(workload)
     if not entry or entry.get("kernel_source_hash") != kernel_hash:
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry
+
+
+def hbm_roofline(logical_bytes, compulsory_bytes, kernel_ms, counters, practical):
+    """The HBM roofline of one launch.  `achieved` holds bytes that HBM's side
+    of the chip actually served: the copy-calibrated FETCH_SIZE + WRITE_SIZE
+    of the committed counter run on the current kernel (L2-miss traffic; it
+    also counts Infinity Cache hits, so it bounds DRAM traffic from above),
+    else the compulsory bytes (every distinct row once + indices + dense +
+    output, a lower bound with cold caches).  Either way frac <= 1 holds for a
+    physical transfer.  The logical (algorithmic) bytes, which count repeated
+    rows every time, are reported beside it as logical_gbps: repeated rows
+    come from L2, so that rate is not an HBM rate."""
+    t = kernel_ms * 1e-3
+    measured = counters.get("hbm_bytes_per_launch") if counters else None
+    if measured:
+        hbm, model = measured, ("memory-side bytes per launch measured by rocprofv3 "
+                                "(FETCH_SIZE + WRITE_SIZE, scaled by a known-size read and "
+                                "copy; L2 misses, Infinity Cache hits included)")
+    else:
+        hbm, model = compulsory_bytes, ("compulsory bytes per launch (distinct rows once + "
+                                        "indices + dense + output; no counter run matches "
+                                        "the current kernel)")
+    r = {"bound": "hbm", "achieved": hbm / t / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": hbm / t / 1e9 / HBM_PEAK_GBPS, "traffic": measured,
+         "byte_model": model, "bytes_per_launch": hbm,
+         "logical_bytes_per_launch": logical_bytes,
+         "logical_gbps": logical_bytes / t / 1e9,
+         "compulsory_bytes_per_launch": compulsory_bytes,
+         "compulsory_gbps": compulsory_bytes / t / 1e9,
+         "compulsory_frac": compulsory_bytes / t / 1e9 / HBM_PEAK_GBPS}
+    if counters and counters.get("dram_bytes_per_launch"):
+        r["dram_counter_bytes_per_launch"] = counters["dram_bytes_per_launch"]
+        r["dram_counter_gbps"] = counters["dram_bytes_per_launch"] / t / 1e9
+    if practical:
+        r["practical_peak_gbps"] = practical["gbps"]
+        r["frac_of_practical_peak"] = r["achieved"] / practical["gbps"]
+        r["practical_peak"] = practical
+    return r
+
+
+def practical_read_peak(stream, gib=4, reps=10):
+    """Read rate of the library's streaming-read kernel (dlrm_stream_read)
+    over a buffer far larger than the Infinity Cache: kernel time from
+    launch-recorded events, median of `reps` launches."""
+    import torch
+    from dlrm_embedding_bag_amd import abi
+    buf = torch.zeros(gib << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, device="cuda")
+    nbytes = buf.numel() * 4
+    timer = KernelTimer(reps)
+    try:
+        with torch.cuda.stream(stream):
+            abi.dlrm_stream_read(buf, sink, stream=stream)
+            for i in range(reps):
+                timer.arm(i)
+                abi.dlrm_stream_read(buf, sink, stream=stream)
+                timer.disarm()
+        torch.cuda.synchronize()
+        ms = statistics.median(timer.elapsed_ms(i) for i in range(reps))
+    finally:
+        timer.close()
+    del buf
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"practical peak: the streaming-read kernel reads {gib} GiB at {gbps:.0f} GB/s "
+        f"({gbps / HBM_PEAK_GBPS:.3f} of 8 TB/s)")
+    return {"gbps": gbps, "bytes": nbytes, "kernel_ms": ms, "frac_of_spec": gbps / HBM_PEAK_GBPS,
+            "kernel": "dlrm_stream_read (stream_read_kernel): 16-byte loads, 8 in flight per "
+                      "lane, 2048 workgroups of 256 lanes, median of 10 launches"}
 
 
 # ------------------------------------------------------------------ main --
@@ -397,7 +541,7 @@ def bench_emb_interact(args, stream):
     kms = statistics.mean(ktimes)
     log(f"kernel alone: mean {kms * 1000:.1f} us, median "
         f"{statistics.median(ktimes) * 1000:.1f} us over {args.steps} steps")
-    achieved = nbytes / (kms * 1e-3) / 1e9
+    practical = practical_read_peak(stream) if not args.profile_run else None
     extra = {"median_ms_per_step": med, "min_ms_per_step": min(times),
              "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
              "distinct_row_fraction": case.distinct_rows_fraction()}
@@ -406,7 +550,7 @@ def bench_emb_interact(args, stream):
         wms = statistics.mean(wt)
         extra["warm_ms_per_step"] = wms
         extra["warm_samples_per_s"] = case.B / (wms * 1e-3)
-        extra["warm_algorithmic_gbps"] = nbytes / (wms * 1e-3) / 1e9
+        extra["warm_logical_gbps"] = nbytes / (wms * 1e-3) / 1e9
         log(f"warm step: mean {wms * 1000:.1f} us")
     # the same batch with the K tables carved out of one allocation (stacked
     # layout): table k = base + row_offsets[k] * D, nothing else changes
@@ -425,32 +569,24 @@ def bench_emb_interact(args, stream):
         res_rows = bench_rows(case, args, stream, flush, cold)
         extra["rows"] = res_rows
     if not args.profile_run and w.name == "nc32":
-        extra["uniform"] = bench_uniform(case, args, stream, flush, cold)
+        extra["uniform"] = bench_uniform(case, args, stream, flush, cold, practical)
     if not args.profile_run:
         extra["host_inclusive_us"] = host_inclusive_time(case, args.steps, cold, flush,
                                                          stream) * 1e3
     khash = kernel_source_hash()
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS,
-                "traffic": read_traffic(khash, w.name),
-                "kernel": "interact_kernel<4, fused> (dlrm_emb_interact)",
-                "kernel_us": kms * 1e3,
-                "timing": "kernel execution: events recorded by the launch itself "
-                          "(hipExtLaunchKernel), mean over the timed cold steps",
-                "algorithmic_bytes_per_launch": nbytes,
-                "compulsory_bytes_per_launch": int(
-                    extra["distinct_row_fraction"] * case.B * case.K * case.L * case.D * 4),
-                "kernel_source_hash": khash}
-    roofline["compulsory_gbps"] = roofline["compulsory_bytes_per_launch"] / (kms * 1e-3) / 1e9
-    if roofline["traffic"]:
-        # the measured HBM bytes over the same time: the bound that is real
-        # once repeated rows are served by the L2
-        roofline["traffic_gbps"] = roofline["traffic"] / (kms * 1e-3) / 1e9
-        roofline["traffic_frac"] = roofline["traffic_gbps"] / HBM_PEAK_GBPS
+    roofline = hbm_roofline(nbytes, case.compulsory_bytes_per_launch(
+        extra["distinct_row_fraction"]), kms, read_traffic(khash, w.name), practical)
+    roofline.update({"kernel": "interact_kernel (fused gather + interaction, dlrm_emb_interact)",
+                     "kernel_us": kms * 1e3,
+                     "timing": "kernel execution: events recorded by the launch itself "
+                               "(hipExtLaunchKernel), mean over the timed cold steps",
+                     "kernel_source_hash": khash})
+    log(f"roofline: {roofline['achieved']:.0f} GB/s of {roofline['byte_model']} "
+        f"(frac {roofline['frac']:.3f} of 8 TB/s); logical {roofline['logical_gbps']:.0f} GB/s")
     res = {"metric": METRIC, "value": case.B / (ms * 1e-3), "unit": "samples/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-           "us_per_forward": ms * 1e3, "achieved_hbm_gbps": achieved,
-           "step_algorithmic_gbps": nbytes / (ms * 1e-3) / 1e9,
+           "us_per_forward": ms * 1e3, "achieved_hbm_gbps": roofline["achieved"],
+           "step_logical_gbps": nbytes / (ms * 1e-3) / 1e9,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
            "data": "synthetic (seeded N(0, 0.01^2) tables, Zipf/uniform int32 indices, "
                    "N(0,1) dense)",
@@ -462,7 +598,7 @@ def bench_emb_interact(args, stream):
     if not args.profile_run:
         extra["device"] = device_info()
         extra["copy_gbps"] = copy_rate(stream)
-        log(f"practical HBM: a 1 GiB device copy moves {extra['copy_gbps']:.0f} GB/s")
+        log(f"a 1 GiB device copy moves {extra['copy_gbps']:.0f} GB/s (read + write)")
     if not args.no_cpu_baseline and not args.profile_run:
         res["cpu_baseline"] = cpu_baseline(case)
         log(f"cpu baseline: {res['cpu_baseline']['value']:.0f} samples/s")
@@ -505,20 +641,28 @@ def bench_rows(case, args, stream, flush, cold):
     t_i = _event_time(interact, stream, args.steps, args.warmup, cold, flush)
     t_u = _event_time(lambda: (gather(), interact()), stream, args.steps, args.warmup, cold,
                       flush)
+    # the gather's logical bytes count every repeated row; its compulsory
+    # bytes count each distinct row once (plus indices and the output)
     g_bytes = B * K * L * (D + 1) * 4 + B * K * D * 4
+    distinct = sum(int(i.unique().numel()) for i in idx)
+    g_comp = distinct * D * 4 + B * K * L * 4 + B * K * D * 4
+    # the interaction reads each pooled vector and dense row once: no reuse
     i_bytes = B * K * D * 4 + B * D * 4 + B * (D + P) * 4
     rows = {"cache": "cold" if cold else "warm",
-            "emb_bag_sum_multi": {"us": t_g * 1e3, "algorithmic_bytes": g_bytes,
-                                  "gbps": g_bytes / (t_g * 1e-3) / 1e9,
-                                  "frac": g_bytes / (t_g * 1e-3) / 1e9 / HBM_PEAK_GBPS},
-            "dlrm_interact_lower_tri": {"us": t_i * 1e3, "algorithmic_bytes": i_bytes,
+            "emb_bag_sum_multi": {"us": t_g * 1e3, "logical_bytes": g_bytes,
+                                  "logical_gbps": g_bytes / (t_g * 1e-3) / 1e9,
+                                  "compulsory_bytes": g_comp,
+                                  "compulsory_gbps": g_comp / (t_g * 1e-3) / 1e9,
+                                  "compulsory_frac": g_comp / (t_g * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+            "dlrm_interact_lower_tri": {"us": t_i * 1e3, "bytes": i_bytes,
                                         "gbps": i_bytes / (t_i * 1e-3) / 1e9,
                                         "frac": i_bytes / (t_i * 1e-3) / 1e9 / HBM_PEAK_GBPS},
             "unfused_pair_us": t_u * 1e3,
             "unfused_equals_fused": same}
-    log(f"rows: gather alone {t_g * 1e3:.1f} us ({rows['emb_bag_sum_multi']['gbps']:.0f} GB/s), "
-        f"interaction alone {t_i * 1e3:.1f} us ({rows['dlrm_interact_lower_tri']['gbps']:.0f} "
-        f"GB/s), both {t_u * 1e3:.1f} us; equal to fused: {same}")
+    log(f"rows: gather alone {t_g * 1e3:.1f} us ({rows['emb_bag_sum_multi']['logical_gbps']:.0f} "
+        f"GB/s logical), interaction alone {t_i * 1e3:.1f} us "
+        f"({rows['dlrm_interact_lower_tri']['gbps']:.0f} GB/s), both {t_u * 1e3:.1f} us; "
+        f"equal to fused: {same}")
     del emb, out2
     return rows
 
@@ -540,9 +684,9 @@ def bench_variant_line(args, stream):
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"{w.name}: mean {ms * 1000:.1f} us, {gbs:.0f} GB/s; kernel alone {kms * 1000:.1f} us")
     return {"workload": f"{w.name}: {w.description}", "ms_per_step": ms,
-            "samples_per_s": case.B / (ms * 1e-3), "algorithmic_gbps": gbs,
-            "frac_hbm": gbs / HBM_PEAK_GBPS, "kernel_us": kms * 1e3,
-            "kernel_algorithmic_gbps": nbytes / (kms * 1e-3) / 1e9, "steps": args.steps}
+            "samples_per_s": case.B / (ms * 1e-3), "logical_gbps": gbs,
+            "kernel_us": kms * 1e3,
+            "kernel_logical_gbps": nbytes / (kms * 1e-3) / 1e9, "steps": args.steps}
 
 
 def _event_time(fn, stream, steps, warmup, cold, flush):
@@ -621,6 +765,15 @@ def bench_forward(args, stream, flush):
     cold = not args.warm
     t_fwd = _event_time(fwd, stream, args.steps, args.warmup, cold, flush)
     log(f"forward: {t_fwd * 1000:.1f} us ({'cold' if cold else 'warm'})")
+    cpu = None
+    if not args.no_cpu_baseline:
+        with torch.cuda.stream(stream):
+            fwd()
+        torch.cuda.synchronize()
+        cpu = forward_cpu_baseline(w, tables, [inputs.indices(w, k, args.seed)
+                                               for k in range(w.num_tables)],
+                                   inputs.dense(w, args.seed), bottom, top,
+                                   out.cpu().numpy())
     plan = abi.DlrmPlan(model, dense_in, idx, out=torch.empty((B, 1), device="cuda"),
                         workspace=torch.empty_like(ws), mode="graph")
     t_plan = _event_time(lambda: plan.run(stream), stream, args.steps, args.warmup, cold, flush)
@@ -682,18 +835,23 @@ def bench_forward(args, stream, flush):
     torch.cuda.synchronize()
     t_emb = _event_time(lambda: ecase.run(0), stream, args.steps, args.warmup, cold, flush)
     emb_bytes = ecase.bytes_per_launch()
+    emb_comp = ecase.compulsory_bytes_per_launch(ecase.distinct_rows_fraction())
     mlp_us = sum(l["us"] for l in layers)
     mlp_flops = sum(2.0 * B * l["k"] * l["n"] for l in layers)
     for l in layers:
         log(f"  {l['layer']:28s} {l['us']:7.1f} us {l['tflops']:6.1f} TFLOP/s "
             f"{l['gbps']:6.0f} GB/s ({l['bound']}, frac {l['frac']:.2f}; "
             f"{l['us_isolated']:.1f} us as one isolated launch)")
-    log(f"  emb+interact {t_emb * 1000:.1f} us, {emb_bytes / (t_emb * 1e-3) / 1e9:.0f} GB/s")
+    log(f"  emb+interact {t_emb * 1000:.1f} us, {emb_bytes / (t_emb * 1e-3) / 1e9:.0f} GB/s "
+        f"logical, {emb_comp / (t_emb * 1e-3) / 1e9:.0f} GB/s of compulsory bytes")
     return {"workload": f"dlrm: {w.description}", "batch": B, "cache": "cold" if cold else "warm",
             "us_per_forward": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
+            "cpu_baseline": cpu,
             "graph_plan_us_per_forward": t_plan * 1e3, "plan_equals_eager": plan_same,
             "emb_interact_us": t_emb * 1e3,
-            "emb_interact_algorithmic_gbps": emb_bytes / (t_emb * 1e-3) / 1e9,
+            "emb_interact_logical_gbps": emb_bytes / (t_emb * 1e-3) / 1e9,
+            "emb_interact_compulsory_gbps": emb_comp / (t_emb * 1e-3) / 1e9,
+            "emb_interact_compulsory_frac": emb_comp / (t_emb * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "mlp_chains": chains, "mlp_layers": layers, "mlp_us_sum": mlp_us,
             "mlp_tflops": mlp_flops / (mlp_us * 1e-6) / 1e12,
             "mlp_frac_of_f32_mfma_peak": mlp_flops / (mlp_us * 1e-6) / 1e12 / F32_MFMA_PEAK_TFLOPS}
@@ -812,12 +970,17 @@ def bench_variants(args, stream, flush):
         kms = statistics.mean(time_kernel(case, args.steps, 2, not args.warm, flush, stream))
         nbytes = case.bytes_per_launch()
         gbs = nbytes / (ms * 1e-3) / 1e9
-        rows.append({"workload": f"{name}: {w.description}", "us": ms * 1e3,
-                     "samples_per_s": case.B / (ms * 1e-3),
-                     "algorithmic_bytes_per_launch": nbytes, "algorithmic_gbps": gbs,
-                     "frac_hbm": gbs / HBM_PEAK_GBPS, "kernel_us": kms * 1e3,
-                     "kernel_algorithmic_gbps": nbytes / (kms * 1e-3) / 1e9,
-                     "traffic": read_traffic(kernel_source_hash(), name)})
+        counters = read_traffic(kernel_source_hash(), name)
+        row = {"workload": f"{name}: {w.description}", "us": ms * 1e3,
+               "samples_per_s": case.B / (ms * 1e-3),
+               "logical_bytes_per_launch": nbytes, "logical_gbps": gbs,
+               "kernel_us": kms * 1e3,
+               "kernel_logical_gbps": nbytes / (kms * 1e-3) / 1e9,
+               "traffic": counters.get("hbm_bytes_per_launch") if counters else None}
+        if row["traffic"]:
+            row["traffic_gbps"] = row["traffic"] / (kms * 1e-3) / 1e9
+            row["traffic_frac"] = row["traffic_gbps"] / HBM_PEAK_GBPS
+        rows.append(row)
         log(f"variant {name:14s} {ms * 1000:7.1f} us {case.B / (ms * 1e-3) / 1e6:6.1f} M "
             f"samples/s {gbs:6.0f} GB/s")
         del case
@@ -854,11 +1017,16 @@ def bench_sweep(args, stream, flush):
             t = _event_time(lambda: lib.dlrm_emb_interact(*a), stream, args.sweep_steps, 3,
                             not args.warm, flush)
             nbytes = B * emb_interact_bytes_per_sample(K, w.dim, w.bag)
+            distinct = sum(int(x.unique().numel()) for x in xs)
+            comp = distinct * w.dim * 4 + nbytes - B * K * w.bag * w.dim * 4
             gbs = nbytes / (t * 1e-3) / 1e9
+            cgbs = comp / (t * 1e-3) / 1e9
             cells.append({"batch": B, "num_tables": K, "us": t * 1e3,
-                          "samples_per_s": B / (t * 1e-3), "algorithmic_gbps": gbs,
-                          "frac_hbm": gbs / HBM_PEAK_GBPS})
-            log(f"sweep K={K:2d} B={B:5d}: {t * 1000:8.1f} us {gbs:7.0f} GB/s")
+                          "samples_per_s": B / (t * 1e-3), "logical_gbps": gbs,
+                          "distinct_row_fraction": distinct / (B * K * w.bag),
+                          "compulsory_gbps": cgbs, "compulsory_frac": cgbs / HBM_PEAK_GBPS})
+            log(f"sweep K={K:2d} B={B:5d}: {t * 1000:8.1f} us {gbs:7.0f} GB/s logical, "
+                f"{cgbs:6.0f} GB/s compulsory")
     return {"dim": w.dim, "rows": w.rows, "bag": w.bag, "index_dist": "zipf(1.05)",
             "cache": "warm" if args.warm else "cold", "cells": cells}
 
@@ -904,6 +1072,8 @@ def bench_sweep_forward(args, stream, flush):
         t_emb = _event_time(lambda: lib.dlrm_emb_interact(*ea), stream, args.sweep_steps, 3,
                             True, flush)
         emb_bytes = B * emb_interact_bytes_per_sample(K, D, L)
+        emb_comp = (sum(int(x.unique().numel()) for x in xs) * D * 4 + emb_bytes
+                    - B * K * L * D * 4)
         # the six layers alone
         mlp_t, mlp_f = 0.0, 0.0
         x = dense_in[:B]
@@ -920,9 +1090,12 @@ def bench_sweep_forward(args, stream, flush):
                 x = y
         tf = mlp_f / (mlp_t * 1e-3) / 1e12
         gbs = emb_bytes / (t_emb * 1e-3) / 1e9
+        cgbs = emb_comp / (t_emb * 1e-3) / 1e9
         cells.append({"batch": B, "forward_us": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
-                      "emb_interact_us": t_emb * 1e3, "emb_interact_algorithmic_gbps": gbs,
-                      "emb_interact_frac_hbm": gbs / HBM_PEAK_GBPS, "mlp_us": mlp_t * 1e3,
+                      "emb_interact_us": t_emb * 1e3, "emb_interact_logical_gbps": gbs,
+                      "emb_interact_compulsory_gbps": cgbs,
+                      "emb_interact_compulsory_frac": cgbs / HBM_PEAK_GBPS,
+                      "mlp_us": mlp_t * 1e3,
                       "mlp_tflops": tf, "mlp_frac_f32_mfma": tf / F32_MFMA_PEAK_TFLOPS})
         log(f"sweep-forward B={B:5d}: forward {t_fwd * 1e3:7.1f} us "
             f"({B / (t_fwd * 1e-3) / 1e6:5.1f} M/s), emb+interact {t_emb * 1e3:6.1f} us "
@@ -979,7 +1152,7 @@ def device_info():
     return info
 
 
-def bench_uniform(case, args, stream, flush, cold):
+def bench_uniform(case, args, stream, flush, cold, practical=None):
     """The benchmark launch with uniform indices (nc32-uniform: the same
     tables, every gathered row a distinct draw, so L2 reuse is negligible and
     the algorithmic bytes are what HBM must deliver)."""
@@ -990,13 +1163,19 @@ def bench_uniform(case, args, stream, flush, cold):
     kms = statistics.mean(time_kernel(ucase, args.steps, args.warmup, cold, flush, stream))
     ms = statistics.mean(times)
     nbytes = ucase.bytes_per_launch()
+    dfrac = ucase.distinct_rows_fraction()
+    comp = ucase.compulsory_bytes_per_launch(dfrac)
     res = {"workload": f"{w.name}: {w.description}", "us": ms * 1e3, "kernel_us": kms * 1e3,
-           "samples_per_s": ucase.B / (ms * 1e-3), "algorithmic_bytes_per_launch": nbytes,
-           "distinct_row_fraction": ucase.distinct_rows_fraction(),
-           "kernel_algorithmic_gbps": nbytes / (kms * 1e-3) / 1e9,
-           "kernel_frac_hbm": nbytes / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+           "samples_per_s": ucase.B / (ms * 1e-3), "logical_bytes_per_launch": nbytes,
+           "distinct_row_fraction": dfrac, "compulsory_bytes_per_launch": comp,
+           "kernel_logical_gbps": nbytes / (kms * 1e-3) / 1e9,
+           "kernel_compulsory_gbps": comp / (kms * 1e-3) / 1e9,
+           "compulsory_frac_of_spec": comp / (kms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    if practical:
+        res["compulsory_frac_of_practical_peak"] = (comp / (kms * 1e-3) / 1e9) / practical["gbps"]
     log(f"uniform indices: {ms * 1000:.1f} us per step, kernel {kms * 1000:.1f} us, "
-        f"{res['kernel_algorithmic_gbps']:.0f} GB/s")
+        f"{res['kernel_compulsory_gbps']:.0f} GB/s of distinct bytes "
+        f"({res['compulsory_frac_of_spec']:.3f} of 8 TB/s)")
     del ucase
     return res
 
@@ -1057,26 +1236,62 @@ def _dispatch_counter(run_dir, counter, kernel_part):
     return statistics.median(per.values()), len(per)
 
 
+DRAM_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+READ_PROBE_BYTES = 1 << 30
+
+
+def read_probe(stream, reps=5):
+    """Five streaming reads of a 1 GiB buffer (dlrm_stream_read), the
+    known-size read that calibrates the FETCH_SIZE counter."""
+    import torch
+    from dlrm_embedding_bag_amd import abi
+    buf = torch.zeros(READ_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            abi.dlrm_stream_read(buf, sink, stream=stream)
+    torch.cuda.synchronize()
+    log(f"read probe: {reps} reads of 1 GiB done")
+
+
 def record_counters(run_root, workload, kernel_part="interact_kernel"):
-    """Scales the workload's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what
-    the same counters read for a plain 1 GiB copy and stores the HBM bytes per
-    launch in profiles/counters.json under the current kernel source hash.
-    Expects rocprofv3 -d directories pmc_<workload>_FETCH_SIZE,
-    pmc_<workload>_WRITE_SIZE, pmc_copy_FETCH_SIZE and pmc_copy_WRITE_SIZE
-    under run_root."""
+    """Memory-side bytes per launch of the workload's kernel from rocprofv3
+    --pmc runs, stored in profiles/counters.json under the current kernel
+    source hash.  Expects these rocprofv3 -d directories under run_root:
+
+      pmc_<workload>_FETCH_SIZE, pmc_<workload>_WRITE_SIZE   the workload
+      pmc_read_FETCH_SIZE    bench.py --read-probe (1 GiB read per dispatch)
+      pmc_copy_WRITE_SIZE    bench.py --copy-calibration (1 GiB copy)
+      pmc_<workload>_DRAM, pmc_read_DRAM   (optional) TCC_EA0_RDREQ_DRAM_32B_sum
+                             and TCC_EA0_WRREQ_WRITE_DRAM_32B_sum, counted in
+                             32-byte units, so they need no calibration
+
+    FETCH_SIZE (KiB per dispatch) is scaled by what it reads for the known
+    1 GiB streaming read, WRITE_SIZE by what it reads for the 1 GiB copy."""
     d = lambda name: os.path.join(run_root, name)
     fetch, nf = _dispatch_counter(d(f"pmc_{workload}_FETCH_SIZE"), "FETCH_SIZE", kernel_part)
     write, nw = _dispatch_counter(d(f"pmc_{workload}_WRITE_SIZE"), "WRITE_SIZE", kernel_part)
-    cfetch, _ = _dispatch_counter(d("pmc_copy_FETCH_SIZE"), "FETCH_SIZE", "copyBuffer")
+    rfetch, _ = _dispatch_counter(d("pmc_read_FETCH_SIZE"), "FETCH_SIZE", "stream_read_kernel")
     cwrite, _ = _dispatch_counter(d("pmc_copy_WRITE_SIZE"), "WRITE_SIZE", "copyBuffer")
-    copy_bytes = 1 << 30
-    fscale, wscale = copy_bytes / (cfetch * 1024), copy_bytes / (cwrite * 1024)
+    fscale = READ_PROBE_BYTES / (rfetch * 1024)
+    wscale = READ_PROBE_BYTES / (cwrite * 1024)
     entry = {"kernel_source_hash": kernel_source_hash(), "kernel_name_part": kernel_part,
              "dispatches": [nf, nw],
              "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
-             "copy_fetch_size_kib": cfetch, "copy_write_size_kib": cwrite,
-             "copy_bytes": copy_bytes, "fetch_scale": fscale, "write_scale": wscale,
-             "hbm_bytes_per_launch": fetch * 1024 * fscale + write * 1024 * wscale}
+             "read_probe_fetch_size_kib": rfetch, "copy_write_size_kib": cwrite,
+             "calibration_bytes": READ_PROBE_BYTES, "fetch_scale": fscale, "write_scale": wscale,
+             "hbm_bytes_per_launch": fetch * 1024 * fscale + write * 1024 * wscale,
+             "hbm_read_bytes_per_launch": fetch * 1024 * fscale,
+             "hbm_write_bytes_per_launch": write * 1024 * wscale}
+    if os.path.isdir(d(f"pmc_{workload}_DRAM")):
+        rd, _ = _dispatch_counter(d(f"pmc_{workload}_DRAM"), DRAM_COUNTERS[0], kernel_part)
+        wr, _ = _dispatch_counter(d(f"pmc_{workload}_DRAM"), DRAM_COUNTERS[1], kernel_part)
+        entry["dram_read_bytes_per_launch"] = rd * 32
+        entry["dram_write_bytes_per_launch"] = wr * 32
+        entry["dram_bytes_per_launch"] = (rd + wr) * 32
+    if os.path.isdir(d("pmc_read_DRAM")):
+        prd, _ = _dispatch_counter(d("pmc_read_DRAM"), DRAM_COUNTERS[0], "stream_read_kernel")
+        entry["read_probe_dram_read_bytes"] = prd * 32
     try:
         with open(COUNTERS_JSON) as f:
             allc = json.load(f)
@@ -1100,7 +1315,10 @@ def main():
     ap.add_argument("--warm", action="store_true", help="do not flush caches between steps")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only five 1 GiB device copies (the WRITE_SIZE calibration)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only five 1 GiB streaming reads (the FETCH_SIZE calibration)")
     ap.add_argument("--record-counters", metavar="DIR", default="",
                     help="store the workload's HBM bytes per launch from rocprofv3 --pmc "
                          "runs under DIR in profiles/counters.json (no GPU needed)")
@@ -1138,6 +1356,9 @@ def main():
     stream = torch.cuda.Stream()
     if args.copy_calibration:
         copy_calibration(stream)
+        return
+    if args.read_probe:
+        read_probe(stream)
         return
     if args.profile_linear:
         profile_linear(args.profile_linear, stream)

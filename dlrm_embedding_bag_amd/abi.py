@@ -25,8 +25,9 @@ MAX_DIM = 1024
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 POOLS = {"sum": 0, "mean": 1}
 PLAN_MODES = {"direct": 0, "graph": 1}
+FORWARD_OPTIONS = {"layered": 1, "unfused_head": 2}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "dlrm_set_kernel_timing_events",
-           "emb_bag_sum_multi",
+           "dlrm_stream_read", "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
            "dlrm_emb_interact_pool", "dlrm_emb_interact_dots", "linear_bias_act",
            "linear_bias_act_split", "mlp_forward",
@@ -63,7 +64,8 @@ class Model(ctypes.Structure):
     _fields_ = [("num_bottom", _i32), ("bottom", ctypes.POINTER(Layer)),
                 ("num_top", _i32), ("top", ctypes.POINTER(Layer)),
                 ("num_tables", _i32), ("dim", _i32),
-                ("tables", ctypes.POINTER(_vp)), ("rows", ctypes.POINTER(_i64))]
+                ("tables", ctypes.POINTER(_vp)), ("rows", ctypes.POINTER(_i64)),
+                ("options", ctypes.c_uint32)]
 
 
 _LIB = None
@@ -84,6 +86,8 @@ def load(path: str = LIB_PATH):
     lib.dlrm_abi_version.argtypes = []
     lib.dlrm_set_kernel_timing_events.restype = ctypes.c_int
     lib.dlrm_set_kernel_timing_events.argtypes = [_vp, _vp]
+    lib.dlrm_stream_read.restype = ctypes.c_int
+    lib.dlrm_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
     ptrs = ctypes.POINTER(_vp)
     lib.emb_bag_sum_multi.restype = ctypes.c_int
     lib.emb_bag_sum_multi.argtypes = [_i32, _i32, _i32, ptrs, ctypes.POINTER(_i64), ptrs,
@@ -147,6 +151,26 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _stream_obj(stream):
+    """A torch stream object for `stream` (None: the current stream; an int:
+    an external hipStream_t handle)."""
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def _empty(shape, device, stream, dtype=None):
+    """An uninitialised float32 (or `dtype`) tensor allocated on the stream the
+    call will run on, so that the caching allocator orders its reuse after
+    the call's kernels."""
+    torch = _torch()
+    with torch.cuda.stream(_stream_obj(stream)):
+        return torch.empty(shape, dtype=dtype or torch.float32, device=device)
+
+
 def _dev(t, dtype, what):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
@@ -198,6 +222,17 @@ def dlrm_set_kernel_timing_events(start, stop):
     _check(load().dlrm_set_kernel_timing_events(start, stop), "dlrm_set_kernel_timing_events")
 
 
+def dlrm_stream_read(buf, sink, stream=None):
+    """One streaming read of the device tensor `buf` (measurement support);
+    `sink` is a float32 device tensor of at least one element."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _dev(sink, torch.float32, "sink")
+    _check(load().dlrm_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                   sink.data_ptr(), _stream(stream)), "dlrm_stream_read")
+
+
 def emb_bag_sum_multi(tables, indices, offsets=None, batch=None, out=None, stream=None):
     """(B, K, D) float32 pooled sums; see include/dlrm_embedding_bag.h."""
     torch = _torch()
@@ -209,7 +244,7 @@ def emb_bag_sum_multi(tables, indices, offsets=None, batch=None, out=None, strea
     if B is None:
         raise ValueError("batch is required with uniform-stride (offsets=None) bags")
     if out is None:
-        out = torch.empty((B, K, D), dtype=torch.float32, device=tables[0].device)
+        out = _empty((B, K, D), tables[0].device, stream)
     _dev(out, torch.float32, "out")
     _check(lib.emb_bag_sum_multi(K, B, D, tp, rows, ip, op, nidx, out.data_ptr(),
                                  _stream(stream)), "emb_bag_sum_multi")
@@ -225,7 +260,7 @@ def dlrm_interact_lower_tri(dense, emb, out=None, stream=None):
     B, N, D = emb.shape
     P = (N + 1) * N // 2
     if out is None:
-        out = torch.empty((B, D + P), dtype=torch.float32, device=emb.device)
+        out = _empty((B, D + P), emb.device, stream)
     _dev(out, torch.float32, "out")
     if dense.shape != (B, D) or out.shape != (B, D + P):
         raise ValueError("dense must be (B, D) and out (B, D + F(F-1)/2)")
@@ -246,7 +281,7 @@ def dlrm_emb_interact(tables, indices, dense, offsets=None, out=None, emb_out=No
     B, D = dense.shape
     P = (K + 1) * K // 2
     if out is None:
-        out = torch.empty((B, D + P), dtype=torch.float32, device=dense.device)
+        out = _empty((B, D + P), dense.device, stream)
     _dev(out, torch.float32, "out")
     if out.shape != (B, D + P):
         raise ValueError("out must be (B, D + F(F-1)/2)")
@@ -316,7 +351,7 @@ def emb_bag_pool(tables, indices, offsets=None, weights=None, pool="sum", batch=
     lib = load()
     g = _BagsArg(tables, indices, offsets, weights, pool, batch, scales)
     if out is None:
-        out = torch.empty((g.B, g.K, g.D), dtype=torch.float32, device=g.tables[0].device)
+        out = _empty((g.B, g.K, g.D), g.tables[0].device, stream)
     _dev(out, torch.float32, "out")
     if out.shape != (g.B, g.K, g.D):
         raise ValueError("out must be (B, K, D)")
@@ -337,7 +372,7 @@ def dlrm_emb_interact_pool(tables, indices, dense, offsets=None, weights=None, p
         raise ValueError("dense must be (B, D)")
     P = (g.K + 1) * g.K // 2
     if out is None:
-        out = torch.empty((B, D + P), dtype=torch.float32, device=dense.device)
+        out = _empty((B, D + P), dense.device, stream)
     _dev(out, torch.float32, "out")
     if out.shape != (B, D + P):
         raise ValueError("out must be (B, D + F(F-1)/2)")
@@ -365,7 +400,7 @@ def dlrm_emb_interact_dots(tables, indices, dense, offsets=None, weights=None, p
         raise ValueError("dense must be (B, D)")
     P = (g.K + 1) * g.K // 2
     if out is None:
-        out = torch.empty((B, P), dtype=torch.float32, device=dense.device)
+        out = _empty((B, P), dense.device, stream)
     if (not isinstance(out, torch.Tensor) or out.device.type != "cuda"
             or out.dtype != torch.float32 or out.shape != (B, P) or out.stride(1) != 1):
         raise ValueError("out must be a (B, F(F-1)/2) float32 GPU tensor with unit column stride")
@@ -408,7 +443,7 @@ def linear_bias_act_split(a_lo, a_hi, w, bias=None, act="none", out=None, stream
             raise ValueError("bias must have N elements")
         bp = bias.data_ptr()
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a_lo.device)
+        out = _empty((M, N), a_lo.device, stream)
     _matrix(out, "out")
     if out.shape != (M, N):
         raise ValueError("out must be (M, N)")
@@ -440,7 +475,7 @@ def linear_bias_act(a, w, bias=None, act="none", out=None, stream=None):
             raise ValueError("bias must have N elements")
         bp = bias.data_ptr()
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+        out = _empty((M, N), a.device, stream)
     if out.dim() != 2 or out.stride(1) != 1 or out.shape != (M, N):
         raise ValueError("out must be (M, N) with unit column stride")
     _check(lib.linear_bias_act(M, N, Kd, a.data_ptr(), a.stride(0), w.data_ptr(), bp,
@@ -479,7 +514,7 @@ def mlp_forward(a, layers, out=None, stream=None):
     M = a.shape[0]
     N = layers[-1][0].shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+        out = _empty((M, N), a.device, stream)
     if out.dim() != 2 or out.stride(1) != 1 or out.shape != (M, N):
         raise ValueError("out must be (M, N) with unit column stride")
     _check(lib.mlp_forward(M, len(layers), arr, a.data_ptr(), a.stride(0), out.data_ptr(),
@@ -487,14 +522,30 @@ def mlp_forward(a, layers, out=None, stream=None):
     return out
 
 
+def forward_options(options=()):
+    """The dlrm_model.options bits of an iterable of FORWARD_OPTIONS names
+    (or an int, passed through)."""
+    if isinstance(options, int):
+        return options
+    bits = 0
+    for name in options:
+        if name not in FORWARD_OPTIONS:
+            raise ValueError(f"unknown forward option {name!r} (known: {sorted(FORWARD_OPTIONS)})")
+        bits |= FORWARD_OPTIONS[name]
+    return bits
+
+
 class DlrmModel:
     """Host description of a DLRMv1 model over caller-owned device tensors.
 
     bottom / top: lists of (weight (out, in), bias (out,) or None, act) with
-    GPU float32 tensors; tables: list of (rows_k, D) GPU float32 tensors.
+    GPU float32 tensors; tables: list of (rows_k, D) GPU float32 tensors;
+    options: names from FORWARD_OPTIONS ("layered": never the one-launch
+    small-model kernel; "unfused_head": the last top layer as its own
+    launch), or the raw bits.
     """
 
-    def __init__(self, bottom, top, tables):
+    def __init__(self, bottom, top, tables, options=()):
         torch = _torch()
         self._keep = []
         self.tables = [_dev(t, torch.float32, f"tables[{k}]") for k, t in enumerate(tables)]
@@ -505,8 +556,9 @@ class DlrmModel:
         self._tables = _ptr_array(self.tables)
         self._rows = _i64_array([t.shape[0] for t in self.tables])
         self.out_features = top[-1][0].shape[0]
+        self.options = forward_options(options)
         self.struct = Model(len(bottom), self._bottom, len(top), self._top,
-                            len(self.tables), self.dim, self._tables, self._rows)
+                            len(self.tables), self.dim, self._tables, self._rows, self.options)
 
     def workspace_bytes(self, batch: int) -> int:
         return dlrm_forward_workspace_bytes(self, batch)
@@ -526,18 +578,22 @@ def dlrm_forward(model: DlrmModel, dense_in, indices, offsets=None, out=None, wo
     indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
     if offsets is not None:
         offsets = [_dev(o, torch.int32, f"offsets[{k}]") for k, o in enumerate(offsets)]
-    if out is None:
-        out = torch.empty((B, model.out_features), dtype=torch.float32, device=dense_in.device)
-    _dev(out, torch.float32, "out")
     need = model.workspace_bytes(B)
+    # Temporaries are allocated on the stream the forward runs on, so the
+    # caching allocator does not hand their blocks to other work before the
+    # forward's kernels are done with them.
+    s = _stream_obj(stream)
+    if out is None:
+        out = _empty((B, model.out_features), dense_in.device, s)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dense_in.device)
+        workspace = _empty(max(need, 1), dense_in.device, s, torch.uint8)
+    _dev(out, torch.float32, "out")
     ws = workspace.data_ptr()
     _check(lib.dlrm_forward(ctypes.byref(model.struct), B, dense_in.data_ptr(),
                             _ptr_array(indices),
                             _ptr_array(offsets) if offsets is not None else None,
                             _i64_array([i.numel() for i in indices]), out.data_ptr(), ws,
-                            workspace.numel() * workspace.element_size(), _stream(stream)),
+                            workspace.numel() * workspace.element_size(), s.cuda_stream),
            "dlrm_forward")
     return out
 
@@ -582,18 +638,26 @@ class DlrmPlan:
         self._op = _ptr_array(self.offsets) if self.offsets is not None else None
         self._nidx = _i64_array([i.numel() for i in self.indices])
 
-    def update(self, dense_in=None, indices=None, offsets=None, out=None):
-        """Rebind the per-batch buffers (dlrm_plan_update)."""
+    _KEEP = object()
+
+    def update(self, dense_in=None, indices=None, offsets=_KEEP, out=None):
+        """Rebind the per-batch buffers (dlrm_plan_update).  An argument left
+        out keeps its current binding; offsets=None explicitly switches the
+        plan to uniform-stride bags, and a list of tensors to CSR bags."""
         torch = _torch()
-        if dense_in is not None:
-            self.dense_in = _dev(dense_in, torch.float32, "dense_in")
-        if out is not None:
-            self.out = _dev(out, torch.float32, "out")
-        if indices is not None:
-            self._bind(indices, offsets)
-        _check(self._lib.dlrm_plan_update(self._handle, self.dense_in.data_ptr(), self._ip,
-                                          self._op, self._nidx, self.out.data_ptr()),
-               "dlrm_plan_update")
+        dense = self.dense_in if dense_in is None else _dev(dense_in, torch.float32, "dense_in")
+        o = self.out if out is None else _dev(out, torch.float32, "out")
+        new_idx = self.indices if indices is None else indices
+        new_off = self.offsets if offsets is DlrmPlan._KEEP else offsets
+        saved = (self.indices, self.offsets, self._ip, self._op, self._nidx)
+        self._bind(new_idx, new_off)
+        rc = self._lib.dlrm_plan_update(self._handle, dense.data_ptr(), self._ip, self._op,
+                                        self._nidx, o.data_ptr())
+        if rc != DLRM_OK:
+            (self.indices, self.offsets, self._ip, self._op, self._nidx) = saved
+            _check(rc, "dlrm_plan_update")
+        self.dense_in = dense
+        self.out = o
 
     def run(self, stream=None):
         _check(self._lib.dlrm_plan_run(self._handle, _stream(stream)), "dlrm_plan_run")

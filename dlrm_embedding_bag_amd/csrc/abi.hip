@@ -3,7 +3,6 @@
 // argument error is reported before any work is enqueued; nothing here
 // allocates device memory or synchronizes the stream.
 #include <limits.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <functional>
@@ -122,8 +121,9 @@ bool pack_chain(int32_t m, int32_t n, const dlrm_layer *layers, const float *a, 
 struct ForwardLayout {
   int64_t P = 0, ldR = 0, ld_buf = 0;
   size_t off_R = 0, off_buf0 = 0, off_buf1 = 0, total = 0;
-  bool bottom_chain = false, top_chain = false;  // MLPs run as one fused chain launch
 };
+
+constexpr uint32_t kForwardOptions = DLRM_FORWARD_LAYERED | DLRM_FORWARD_UNFUSED_HEAD;
 
 // Checks the model's shapes and computes the workspace layout for batch B.
 int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
@@ -131,6 +131,7 @@ int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
   if (m->num_bottom < 1 || m->num_top < 1 || m->num_tables < 1 ||
       m->num_tables > DLRM_MAX_TABLES || m->dim < 1 || m->dim > DLRM_MAX_DIM || B < 0)
     return DLRM_ERR_SHAPE;
+  if ((m->options & ~kForwardOptions) != 0) return DLRM_ERR_SHAPE;
   if (!m->bottom || !m->top || !m->tables || !m->rows) return DLRM_ERR_NULL;
   const int64_t F = (int64_t)m->num_tables + 1;
   lay.P = F * (F - 1) / 2;
@@ -152,25 +153,15 @@ int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
     if (l + 1 < m->num_top) widest = widest > L.out_features ? widest : L.out_features;
   }
   if (m->top[0].in_features != m->dim + lay.P) return DLRM_ERR_SHAPE;
-  // An MLP runs as one fused chain launch when the chain kernel takes its
-  // widths and its first layer is at most kChainNarrowK wide.  The threshold is
-  // 0 (never): measured inside the full forward on MI355X, the 13-512-256-64
-  // chain made the forward 8-11 us slower than three tiled GEMM launches, and
-  // the 415-wide top MLP is faster as tiled GEMMs in any case.
-  ChainParams probe;
-  const float *fake = reinterpret_cast<const float *>(uintptr_t(256));
-  lay.bottom_chain = m->bottom[0].in_features <= kChainNarrowK &&
-                     pack_chain(B, m->num_bottom, m->bottom, fake, m->bottom[0].in_features,
-                                const_cast<float *>(fake), 4, probe);
-  lay.top_chain = m->top[0].in_features <= kChainNarrowK &&
-                  pack_chain(B, m->num_top, m->top, fake, 4, const_cast<float *>(fake), 4, probe);
+  // The MLPs run layer by layer (measured inside the full forward on MI355X,
+  // the one-launch MLP chain of mlp_forward made the forward 8-11 us slower
+  // than three tiled GEMM launches for 13-512-256-64, and the 415-wide top
+  // MLP is faster as tiled GEMMs in any case).
   lay.ld_buf = round4(widest);
   lay.off_R = 0;
   lay.off_buf0 = round256((size_t)B * (size_t)lay.ldR * sizeof(float));
   lay.off_buf1 = lay.off_buf0 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
-  lay.total = (lay.bottom_chain && lay.top_chain)
-                  ? lay.off_buf0
-                  : lay.off_buf1 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
+  lay.total = lay.off_buf1 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
   return DLRM_OK;
 }
 
@@ -190,11 +181,6 @@ int emit(const Emitter &em, F &&f) {
   }
   return hip_status(f(em.stream));
 }
-
-// The one-launch forward is used whenever the model fits it, unless the
-// environment variable DLRM_FORWARD_LAYERED is set (a switch for comparing
-// the two compositions).
-bool small_forward_enabled() { return getenv("DLRM_FORWARD_LAYERED") == nullptr; }
 
 SmallLayer small_layer_of(const dlrm_layer &L) {
   return SmallLayer{L.weight, L.bias, L.in_features, L.out_features, L.act};
@@ -240,8 +226,9 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
     return DLRM_ERR_WORKSPACE;
   const int B = batch, D = model->dim, K = model->num_tables;
 
-  // Models whose MLPs are small run the whole forward as one launch.
-  if (small_forward_enabled() && model->num_bottom <= kMaxSmallLayers &&
+  // Models whose MLPs are small run the whole forward as one launch, unless
+  // the model asks for the layered composition.
+  if (!(model->options & DLRM_FORWARD_LAYERED) && model->num_bottom <= kMaxSmallLayers &&
       model->num_top <= kMaxSmallLayers) {
     SmallLayer bl[kMaxSmallLayers], tl[kMaxSmallLayers];
     for (int l = 0; l < model->num_bottom; ++l) bl[l] = small_layer_of(model->bottom[l]);
@@ -268,12 +255,6 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
   const float *x = dense_in;
   int64_t ldx = model->bottom[0].in_features;
-  ChainParams cp;
-  if (lay.bottom_chain &&
-      pack_chain(B, model->num_bottom, model->bottom, dense_in, ldx, R, lay.ldR, cp)) {
-    rc = emit(em, [=](hipStream_t s) { return launch_mlp_chain(cp, s); });
-    if (rc) return rc;
-  } else {
   for (int l = 0; l < model->num_bottom; ++l) {
     const dlrm_layer &L = model->bottom[l];
     const bool last = l + 1 == model->num_bottom;
@@ -286,7 +267,6 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
     if (rc) return rc;
     x = y;
     ldx = ldy;
-  }
   }
 
   // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
@@ -309,9 +289,6 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   // Top MLP on cat(dense, dots) = R.
   x = R;
   ldx = lay.ldR;
-  const int32_t out_w = model->top[model->num_top - 1].out_features;
-  if (lay.top_chain && pack_chain(B, model->num_top, model->top, R, lay.ldR, out, out_w, cp))
-    return emit(em, [=](hipStream_t s) { return launch_mlp_chain(cp, s); });
   for (int l = 0; l < model->num_top; ++l) {
     const dlrm_layer &L = model->top[l];
     const bool last = l + 1 == model->num_top;

@@ -239,12 +239,8 @@ hipError_t launch_emb_bag(const TableSet &ts, const GatherConfig &gc, int B, int
 // 21.8 -> 12.8, B = 1024: 28.6 -> 25.4 (K = 26: 19.5 -> 10.2, 20.2 -> 11.7,
 // 26.4 -> 22.9), B >= 2048 unchanged; fill thresholds of 2048 and 8192
 // waves were each slower somewhere.
-#ifndef DLRM_MAX_THREADS
-#define DLRM_MAX_THREADS 128
-#endif
-#ifndef DLRM_WAVE_FILL
-#define DLRM_WAVE_FILL 4096
-#endif
+constexpr int kMaxThreadsFull = 128;  // workgroup size while the grid fills the chip
+constexpr int64_t kWaveFill = 4096;    // waves that count as a full chip (16 per CU)
 
 bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, int &threads) {
   const int F = K + 1;
@@ -259,22 +255,22 @@ bool plan_interact(int B, int K, int D, bool vec4, int el, InteractParams &ip, i
   if (per_sample > kLdsBudget) return false;
   const int lanes_per_sample = K * ip.G;
   int S = 1;
-  while (S * lanes_per_sample < DLRM_MIN_THREADS &&
+  while (S * lanes_per_sample < kMinThreads &&
          (size_t)(2 * S) * per_sample <= kLdsBudget / 2 &&
          S < B)
     S *= 2;
   ip.S = S;
-  // Workgroup size: DLRM_MAX_THREADS when the grid fills the chip, so that
+  // Workgroup size: kMaxThreadsFull when the grid fills the chip, so that
   // many resident workgroups interleave their gather and dot phases; when it
-  // does not (fewer than DLRM_WAVE_FILL waves at the next size up), doubled
+  // does not (fewer than kWaveFill waves at the next size up), doubled
   // up to all of a sample's lane groups at once, so that its bags are pooled
   // side by side instead of in turn by a few groups.
   const int want = S * lanes_per_sample;
   const int64_t nwg = (B + S - 1) / S;
-  int cap = DLRM_MAX_THREADS;
-  while (cap < want && 2 * cap <= 1024 && nwg * (2 * cap / kWave) <= DLRM_WAVE_FILL) cap *= 2;
+  int cap = kMaxThreadsFull;
+  while (cap < want && 2 * cap <= 1024 && nwg * (2 * cap / kWave) <= kWaveFill) cap *= 2;
   threads = ((min(want, cap) + kWave - 1) / kWave) * kWave;
-  if (threads < DLRM_MIN_THREADS) threads = DLRM_MIN_THREADS;
+  if (threads < kMinThreads) threads = kMinThreads;
   ip.lds_bytes = (int)(S * per_sample);
   // Quads per 4 x 4 block team: the most that still covers every block of the
   // workgroup in one pass, so the interaction phase runs on as many waves as

@@ -83,10 +83,6 @@ hipError_t launch_forward_small(const TableSet &ts, bool csr, bool vec4,
 
 constexpr int kMaxChainLayers = 4;
 constexpr int kMaxChainWidth = 512;  // widest layer the MLP chain keeps in LDS
-#ifndef DLRM_CHAIN_NARROW_K
-#define DLRM_CHAIN_NARROW_K 0
-#endif
-constexpr int kChainNarrowK = DLRM_CHAIN_NARROW_K;  // dlrm_forward chains an MLP whose first K <= this
 
 // One layer of an MLP chain: out = act(in W^T + bias), W (N, K) dense.
 struct ChainLayer {

@@ -49,21 +49,8 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-#ifndef DLRM_GEMM_BK
-#define DLRM_GEMM_BK 32
-#endif
-// Scheduling hint for the k loop: LLVM's instruction-group-level-parallelism
-// strategy 1 interleaves the MFMAs with the LDS fragment reads of the next
-// k-quad.  Same instructions, same results; measured per launch at
-// 8192 x 512 x 415: 41.1 -> 38.8 us, 8192 x 256 x 512: 25.7 -> 23.8,
-// 16384 x 512 x 512: 83.8 -> 79.9 (strategies 0 and 2 gained less).
-#ifndef DLRM_GEMM_IGLP
-#define DLRM_GEMM_IGLP 1
-#endif
-#ifndef DLRM_GEMM_KSPLIT
-#define DLRM_GEMM_KSPLIT 2
-#endif
-constexpr int kBK = DLRM_GEMM_BK;   // k per LDS slab
+constexpr int kBK = 32;      // k per LDS slab
+constexpr int kKSplit = 2;   // wave groups splitting k in the 64-row tiles
 
 __device__ __forceinline__ float apply_act(float x, int act) {
   if (act == 1) return x > 0.0f ? x : 0.0f;
@@ -292,9 +279,12 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
       if (kq + 32 < kBK) frags(As, Ws, kq + 32, af0, wf0);
       mfmas(af1, wf1);
     }
-#if DLRM_GEMM_IGLP >= 0
-    __builtin_amdgcn_iglp_opt(DLRM_GEMM_IGLP);
-#endif
+    // Scheduling hint: LLVM's instruction-group-level-parallelism strategy 1
+    // interleaves the MFMAs with the LDS fragment reads of the next k-quad.
+    // Same instructions, same results; measured per launch at 8192 x 512 x
+    // 415: 41.1 -> 38.8 us, 8192 x 256 x 512: 25.7 -> 23.8, 16384 x 512 x
+    // 512: 83.8 -> 79.9 (strategies 0 and 2 gained less).
+    __builtin_amdgcn_iglp_opt(1);
   };
 
   // Slab s is loaded into register set s & 1 two slabs ahead of its use and
@@ -580,42 +570,22 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
   }
   // Tile shape: the largest tile that still gives every CU a workgroup.
   auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-#ifdef DLRM_GEMM_TILE
-  constexpr int forced = DLRM_GEMM_TILE;
-#else
-  constexpr int forced = 0;
-#endif
-  if constexpr (forced == 7)
-    return launch_gemm_cfg<128, 64, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                 stream);
-  if constexpr (forced == 8)
-    return launch_gemm_cfg<64, 128, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                 stream);
-  if constexpr (forced == 9)
-    return launch_gemm_cfg<128, 128, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                  stream);
-  if constexpr (forced == 10)
-    return launch_gemm_cfg<64, 64, 1, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                stream);
-  if constexpr (forced == 11)
-    return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                 stream);
   // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
   // for every CU, else 128 x 64 on 8 waves of 32 x 32, else 64 x 64, else
   // 64 x 32 on 4 waves.  (At 8192 x 256 x 512, 128 x 64 on 8 waves: 24.5 us,
   // 64 x 64 on 4 waves: 26.6 us, the same sums bit for bit.)
-  if (forced == 1 || (forced == 0 && tiles(128, 128) >= 256))
+  if (tiles(128, 128) >= 256)
     return launch_gemm_cfg<128, 128, 2, 4, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                   stream);
-  if (forced == 0 && tiles(128, 64) >= 256)
+  if (tiles(128, 64) >= 256)
     return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
                                                  stream);
   // The 64-row tiles leave one wave per SIMD: with K of at least two staged
   // slabs, KS wave groups split each tile's k (KS times the waves, 1/KS of
   // the MFMA chain and of the slab round trips).
-  constexpr int KS = DLRM_GEMM_KSPLIT;
+  constexpr int KS = kKSplit;
   const bool ksplit = KS > 1 && K >= 2 * kBK * KS;
-  if (forced == 3 || (forced == 0 && tiles(64, 64) >= 256)) {
+  if (tiles(64, 64) >= 256) {
     if (ksplit)
       return launch_gemm_cfg<64, 64, 2, 2, SPLIT, KS>(M, N, K, A, W, bias, act, C, ldc, va, vw,
                                                       vc, stream);

@@ -9,17 +9,17 @@
 // Each workgroup carries BM = 32 rows through every layer.  The hidden
 // activations of those rows stay in LDS (at most 32 x 512 floats), so no
 // intermediate layer touches HBM and the whole stack pays one prologue and one
-// epilogue.  With 4 waves (the default; DLRM_CHAIN_WM = 2 gives 8), wave w
+// epilogue.  With 4 waves (kWM = 2 would give 8), wave w
 // owns output columns [(w%4) N/4, (w%4 + 1) N/4) of every row: a 32 x N/4 tile
 // of v_mfma_f32_16x16x4f32 accumulators (TN = N/64 blocks of 16 columns).
 //
 // Where it pays: weights are read by every workgroup straight from L2, 16
 // rows of 64 B per wave-load, so a wide first layer (415 -> 512) is paced by
 // the vector memory path and runs slower than the tiled GEMM of linear.hip
-// (top MLP 415-512-256-1: ~97 us against ~79 us as three launches at 8192
-// rows).  With a narrow first layer (13 -> 512) the chain alone is faster
-// than three launches (45 against 52 us), but inside the full forward, where
-// launches run back to back, the three launches win; so dlrm_forward does not
+// (top MLP 415-512-256-1 at 8192 rows: 136 us, against 64 us for the three
+// layers as tiled launches).  With a narrow first layer (13 -> 512) the
+// chain took 47 us against 40 us for three launches, and inside the full
+// forward the three launches win as well; so dlrm_forward does not
 // use it and mlp_forward, its own entry point, runs it for any supported
 // stack.  Its A fragments (activation rows) come from LDS; its weight
 // fragments come straight from global memory (every workgroup reads each
@@ -43,11 +43,8 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-#ifndef DLRM_CHAIN_WM
-#define DLRM_CHAIN_WM 1
-#endif
 constexpr int kBM = 32;                 // rows per workgroup
-constexpr int kWM = DLRM_CHAIN_WM;      // waves along the rows (1 or 2)
+constexpr int kWM = 1;                  // waves along the rows (1 or 2)
 constexpr int kTM = 2 / kWM;            // 16-row MFMA blocks per wave
 constexpr int kThreads = 256 * kWM;     // 4 column quarters x kWM row groups
 constexpr int kSlab = 32;               // k per staged slab of the input

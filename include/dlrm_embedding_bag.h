@@ -10,10 +10,14 @@
  * Conventions shared by every call
  *  - Pointers are DEVICE pointers unless marked [host].  [host] arrays are
  *    read during the call only and may be freed as soon as it returns.
- *  - The caller owns every buffer.  The library allocates nothing, keeps no
- *    pointer after a call returns and has no global mutable state, so calls
- *    are re-entrant ([FASTPATHS] runtime.rs: non-owning views over caller
- *    memory).
+ *  - The caller owns every buffer.  The compute calls allocate no device
+ *    memory and keep no pointer after they return ([FASTPATHS] runtime.rs:
+ *    non-owning views over caller memory); dlrm_plan_create allocates host
+ *    memory for the plan it returns.  The library holds one piece of mutable
+ *    state: the calling thread's kernel-timing events
+ *    (dlrm_set_kernel_timing_events, measurement support, off unless a
+ *    thread sets it).  Apart from it, calls on different streams or threads
+ *    are independent and re-entrant.
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *    Every call only enqueues work on `stream` and never synchronizes
  *    ([FASTPATHS] runtime.rs: execute() stays capturable, no trailing sync).
@@ -73,7 +77,7 @@ DLRM_API const char *dlrm_status_string(int status);
 
 /* ABI version of this header (bumped on any incompatible change). */
 DLRM_API int dlrm_abi_version(void);
-#define DLRM_ABI_VERSION 1
+#define DLRM_ABI_VERSION 2
 
 /*
  * dlrm_set_kernel_timing_events -- per-kernel timing for benchmarks.
@@ -91,13 +95,33 @@ DLRM_API int dlrm_abi_version(void);
  * hipEventElapsedTime(start, stop) times that kernel without the gap that
  * events recorded around the call include (measured within a few percent
  * of a profiler's dispatch time); after a call that launches several, it
- * times the last one.  The setting is per thread; the events stay owned by
- * the caller, who must switch timing off before destroying them.  Graph-mode
- * plans capture plain launches whatever the setting; a caller capturing its
- * own stream must switch timing off first.  Returns DLRM_ERR_NULL when
- * exactly one of the two is NULL (nothing changes), else DLRM_OK.
+ * times the last one.  This is thread-local state of the library (the only
+ * mutable state it keeps): it changes how the calling thread's later
+ * launches are dispatched, never what they compute, and other threads are
+ * unaffected.  The events stay owned by the caller, who must switch timing
+ * off before destroying them.  Graph-mode plans capture plain launches
+ * whatever the setting; a caller capturing its own stream must switch
+ * timing off first.  Returns DLRM_ERR_NULL when exactly one of the two is
+ * NULL (nothing changes), else DLRM_OK.
  */
 DLRM_API int dlrm_set_kernel_timing_events(void *start, void *stop);
+
+/*
+ * dlrm_stream_read -- reads a device buffer once with a streaming-read
+ * kernel (measurement support, not a step of the method: the practical HBM
+ * read rate the gather's bytes are compared with, and a dispatch of known
+ * read bytes for calibrating memory-traffic counters).
+ *
+ *   buf    device buffer, 16-byte aligned
+ *   bytes  its size, a multiple of 16 (0: nothing to do, DLRM_OK)
+ *   sink   device float32; written only when the bytes read hash to a value
+ *          chosen not to occur (it keeps the reads from being optimised
+ *          away), so its content is unspecified afterwards
+ * One launch of 16-byte loads, 8 in flight per lane, up to 2048 workgroups
+ * of 256 lanes.  Returns DLRM_ERR_NULL for a NULL buf or sink,
+ * DLRM_ERR_SHAPE for a misaligned buffer or size.
+ */
+DLRM_API int dlrm_stream_read(const void *buf, size_t bytes, float *sink, void *stream);
 
 /*
  * emb_bag_sum_multi -- K EmbeddingBag(sum) lookups in one launch
@@ -345,6 +369,12 @@ typedef struct dlrm_layer {
 DLRM_API int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers,
                          const float *a, int64_t lda, float *c, int64_t ldc, void *stream);
 
+/* How dlrm_forward composes its launches (bits of dlrm_model.options; 0
+ * lets the library choose).  Every composition computes the same function
+ * within float rounding; these exist to compare them. */
+#define DLRM_FORWARD_LAYERED 1u  /* never the one-launch small-model kernel   */
+#define DLRM_FORWARD_UNFUSED_HEAD 2u /* the last top layer as its own launch  */
+
 /* A DLRMv1 model: bottom MLP, K embedding tables, top MLP.  All arrays of
  * this struct are [host]; the weights and tables they point to are device
  * memory owned by the caller. */
@@ -357,6 +387,8 @@ typedef struct dlrm_model {
   int32_t dim;               /* D                                          */
   const float *const *tables;/* [host] K device pointers, (rows[k], D)     */
   const int64_t *rows;       /* [host] K row counts                        */
+  uint32_t options;          /* DLRM_FORWARD_* bits, 0 = automatic; other
+                                bits are DLRM_ERR_SHAPE                    */
 } dlrm_model;
 
 /* Bytes of device workspace dlrm_forward needs for `batch` samples. */
@@ -380,8 +412,8 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  * Composition: a model whose MLPs hold at most 64 Ki weights in all (widths
  * <= 1024, <= 4 layers each) runs as ONE launch with every intermediate on
  * chip; larger models run each layer as its own tiled GEMM launch around the
- * fused gather + interaction (7 launches for 3 + 3 layers).  Setting the
- * environment variable DLRM_FORWARD_LAYERED forces the layered composition.
+ * fused gather + interaction (7 launches for 3 + 3 layers).  model->options
+ * may force the layered composition (DLRM_FORWARD_LAYERED).
  */
 DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  const int32_t *const *indices, const int32_t *const *offsets,

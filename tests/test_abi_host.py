@@ -37,10 +37,19 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.dlrm_abi_version() == 1
+    assert lib.dlrm_abi_version() == 2
     for code, name in abi.STATUS_NAMES.items():
         assert lib.dlrm_status_string(code).decode().startswith(name)
     assert lib.dlrm_status_string(99) == b"unknown dlrm_status"
+
+
+def test_stream_read_argument_errors(lib):
+    f = lib.dlrm_stream_read
+    assert f(FAKE, 0, FAKE, None) == 0                                   # nothing to read
+    assert f(None, 64, FAKE, None) == 1                                  # buf NULL
+    assert f(FAKE, 64, None, None) == 1                                  # sink NULL
+    assert f(FAKE, 63, FAKE, None) == 2                                  # size % 16
+    assert f(FAKE + 4, 64, FAKE, None) == 2                              # misaligned
 
 
 def test_kernel_timing_events_need_both_or_neither(lib):
@@ -202,7 +211,7 @@ def test_mlp_forward_argument_errors(lib):
     assert f(0, 3, good, None, 13, None, 64, None) == 0                 # m == 0: no-op
 
 
-def _model(bottom, top, K, D):
+def _model(bottom, top, K, D, options=0):
     bl = (abi.Layer * len(bottom))()
     for n, (i, o, act) in enumerate(bottom):
         bl[n].in_features, bl[n].out_features, bl[n].weight, bl[n].act = i, o, FAKE, act
@@ -210,7 +219,7 @@ def _model(bottom, top, K, D):
     for n, (i, o, act) in enumerate(top):
         tl[n].in_features, tl[n].out_features, tl[n].weight, tl[n].act = i, o, FAKE, act
     t, r, _ = _tables(K)
-    m = abi.Model(len(bottom), bl, len(top), tl, K, D, t, r)
+    m = abi.Model(len(bottom), bl, len(top), tl, K, D, t, r, options)
     m._keep = (bl, tl, t, r)
     return m
 
@@ -226,7 +235,7 @@ def test_forward_workspace_and_errors(lib):
     # buffers as wide as the widest hidden layer (B x 512)
     assert ws == B * 416 * 4 + 2 * B * 512 * 4
     odd = _model([(13, 96, 1), (96, 64, 1)], [(D + P, 96, 1), (96, 1, 2)], K, D)
-    # widths the chain kernel does not take: R + two ping-pong buffers (B x 96)
+    # other widths: R + two ping-pong buffers (B x 96)
     assert lib.dlrm_forward_workspace_bytes(ctypes.byref(odd), B) == B * 416 * 4 + 2 * B * 96 * 4
     bad_chain = _model([(13, 512, 1), (500, 64, 1)], [(D + P, 1, 2)], K, D)
     assert lib.dlrm_forward_workspace_bytes(ctypes.byref(bad_chain), B) == 0
@@ -244,6 +253,40 @@ def test_forward_workspace_and_errors(lib):
     assert f(ctypes.byref(good), B, None, idx, None, n, FAKE, FAKE, ws, None) == 1
     assert f(None, B, FAKE, idx, None, n, FAKE, FAKE, ws, None) == 1
     assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, FAKE, ws, None) == 0
+
+
+def test_forward_options_are_validated(lib):
+    """dlrm_model.options: the documented bits are accepted (they change the
+    composition, not the workspace), any other bit is DLRM_ERR_SHAPE."""
+    K, D = 26, 64
+    P = 27 * 26 // 2
+    spec = ([(13, 512, 1), (512, 256, 1), (256, 64, 1)],
+            [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)])
+    B = 256
+    base = lib.dlrm_forward_workspace_bytes(ctypes.byref(_model(*spec, K, D)), B)
+    assert base > 0
+    for bits in (abi.FORWARD_OPTIONS["layered"], abi.FORWARD_OPTIONS["unfused_head"],
+                 abi.FORWARD_OPTIONS["layered"] | abi.FORWARD_OPTIONS["unfused_head"]):
+        m = _model(*spec, K, D, options=bits)
+        assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == base
+    idx = (ctypes.c_void_p * K)(*[FAKE] * K)
+    for bits in (4, 1 << 31, 0xFFFFFFFF):
+        m = _model(*spec, K, D, options=bits)
+        assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == 0
+        assert lib.dlrm_forward(ctypes.byref(m), B, FAKE, idx, None, _n(K, B * 20), FAKE,
+                                FAKE, base, None) == 2
+    assert abi.forward_options(("layered", "unfused_head")) == 3
+    with pytest.raises(ValueError):
+        abi.forward_options(("fast",))
+
+
+def test_no_environment_switch_in_the_library():
+    """The library's behaviour is set by its arguments only: no source reads
+    the process environment."""
+    csrc = os.path.join(ROOT, "dlrm_embedding_bag_amd", "csrc")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        assert "getenv" not in text and "environ" not in text, name
 
 
 def test_plan_argument_errors(lib):

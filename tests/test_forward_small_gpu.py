@@ -2,10 +2,8 @@
 are small (at most 64 Ki weights, widths <= 1024, <= 4 layers per MLP) as a
 single kernel.  Compared with the oracle on the pages' cell shapes and on
 ragged ones (scalar path, CSR bags, batches that leave a workgroup partly
-empty), and with the layered composition (DLRM_FORWARD_LAYERED) within the
-float tolerance."""
-import os
-
+empty), and with the layered composition (the DLRM_FORWARD_LAYERED option) within
+the float tolerance."""
 import numpy as np
 import pytest
 
@@ -37,13 +35,12 @@ def _case(w, seed, bias_std=0.1, csr=False):
 
 
 def _run(model, dense, idx, offs, layered=False):
-    if layered:
-        os.environ["DLRM_FORWARD_LAYERED"] = "1"
+    model.struct.options = abi.FORWARD_OPTIONS["layered"] if layered else 0
     try:
         return host(abi.dlrm_forward(model, dev(dense), [dev(i) for i in idx],
                                      offsets=[dev(o) for o in offs] if offs else None))
     finally:
-        os.environ.pop("DLRM_FORWARD_LAYERED", None)
+        model.struct.options = 0
 
 
 SHAPES = [  # (num_tables, batch, D, bag, bottom, top)

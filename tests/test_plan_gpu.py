@@ -15,12 +15,12 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
 
 
-def _model(w, seed=0):
+def _model(w, seed=0, options=()):
     tables = [inputs.table_host(w, k, seed) for k in range(w.num_tables)]
     bottom, top = inputs.dlrm_layers(w, seed, bias_std=0.1)
     model = abi.DlrmModel([(dev(a), dev(b), act) for a, b, act in bottom],
                           [(dev(a), dev(b), act) for a, b, act in top],
-                          [dev(t) for t in tables])
+                          [dev(t) for t in tables], options=options)
     return model, tables, bottom, top
 
 
@@ -64,14 +64,12 @@ def test_plan_replays_equal_eager_forward(w, mode):
 
 @pytest.mark.parametrize("mode", ["direct", "graph"])
 @pytest.mark.parametrize("layered", [False, True])
-def test_plan_on_a_side_stream_and_update(mode, layered, monkeypatch):
+def test_plan_on_a_side_stream_and_update(mode, layered):
     """A plan replays on a caller stream; update() rebinds other buffers,
     including CSR offsets (another gather kernel: a graph is rebuilt)."""
     import torch
-    if layered:
-        monkeypatch.setenv("DLRM_FORWARD_LAYERED", "1")
     w = inputs.cell_workload(16, 300)
-    model, tables, bottom, top = _model(w, seed=3)
+    model, tables, bottom, top = _model(w, seed=3, options=("layered",) if layered else ())
     dense, idx = _batch(w, 1)
     plan = abi.DlrmPlan(model, dev(dense), [dev(i) for i in idx], mode=mode)
     side = torch.cuda.Stream()
@@ -98,8 +96,56 @@ def test_plan_on_a_side_stream_and_update(mode, layered, monkeypatch):
         assert np.array_equal(got, host(abi.dlrm_forward(model, d2, i3, offsets=o3)))
     want, _, _ = oracle.forward(dense2, bottom, top, tables, idx3, offs)
     assert_close(got, want, "plan CSR vs oracle")
+    # new indices alone keep the CSR offsets bound
+    idx4 = [rng.integers(0, w.rows, int(l.sum())).astype(np.int32) for l in lens]
+    i4 = [dev(i) for i in idx4]
+    plan.update(indices=i4)
+    got = host(plan.run())
+    assert np.array_equal(got, host(abi.dlrm_forward(model, d2, i4, offsets=o3)))
+    # offsets=None explicitly returns to uniform-stride bags
+    plan.update(indices=i2, offsets=None)
+    assert np.array_equal(host(plan.run()), host(abi.dlrm_forward(model, d2, i2)))
     plan.close()
     plan.close()                                    # closing twice is harmless
+
+
+def test_plan_update_with_mismatched_bags_keeps_the_plan():
+    """A rejected update (uniform indices whose count is no multiple of the
+    batch) leaves the plan bound to its previous buffers."""
+    w = inputs.cell_workload(4, 50)
+    model, _, _, _ = _model(w, seed=1)
+    dense, idx = _batch(w, 1)
+    d, x = dev(dense), [dev(i) for i in idx]
+    plan = abi.DlrmPlan(model, d, x)
+    want = host(plan.run())
+    with pytest.raises(abi.DlrmError) as e:
+        plan.update(indices=[i[:-1] for i in x])
+    assert e.value.name == "DLRM_ERR_SHAPE"
+    assert np.array_equal(host(plan.run()), want)
+    plan.close()
+
+
+def test_forward_on_a_side_stream_allocates_there():
+    """dlrm_forward with a caller stream and no workspace: its temporaries
+    belong to that stream, and the result equals the current-stream call."""
+    import torch
+    w = inputs.Workload("side", batch=700, num_tables=8, rows=3000, dim=64, bag=6,
+                        dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1))
+    model, _, _, _ = _model(w, seed=2)
+    dense, idx = _batch(w, 2)
+    d, x = dev(dense), [dev(i) for i in idx]
+    want = host(abi.dlrm_forward(model, d, x))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        outs.append(abi.dlrm_forward(model, d, x, stream=side))
+        # other work on the current stream in between, allocating and freeing
+        junk = torch.ones(1 << 22, device="cuda") * 3.0
+        del junk
+    side.synchronize()
+    for o in outs:
+        assert np.array_equal(host(o), want)
 
 
 def test_plan_rejects_bad_arguments():

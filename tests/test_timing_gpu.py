@@ -93,3 +93,23 @@ def test_direct_plan_replay_records_the_last_kernel():
     finally:
         timer.close()
         plan.close()
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 1 << 20, (256 << 20) + 48])
+def test_stream_read_runs_and_leaves_the_sink(nbytes):
+    """The streaming-read probe reads a buffer (sizes below one workgroup's
+    sweep, ragged tails, larger than the L2) and writes nothing: a zero
+    buffer never hashes to the key, so the sink keeps its value."""
+    import torch
+    buf = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.full((1,), 7.0, device="cuda")
+    timer = _timer(1)
+    try:
+        timer.arm(0)
+        abi.dlrm_stream_read(buf, sink)
+        timer.disarm()
+        torch.cuda.synchronize()
+        assert timer.elapsed_ms(0) > 0.0
+    finally:
+        timer.close()
+    assert host(sink)[0] == 7.0
