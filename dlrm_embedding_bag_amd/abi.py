@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "DLRM_OK", 1: "DLRM_ERR_NULL", 2: "DLRM_ERR_SHAPE",
                 3: "DLRM_ERR_UNSUPPORTED", 4: "DLRM_ERR_WORKSPACE", 5: "DLRM_ERR_HIP"}
 ACTS = {"none": 0, "relu": 1, "sigmoid": 2}
 MAX_TABLES = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MAX_DIM = 1024
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 POOLS = {"sum": 0, "mean": 1}
@@ -31,7 +32,8 @@ EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "dlrm_set_kernel_timing_eve
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
            "dlrm_emb_interact_pool", "dlrm_emb_interact_dots", "linear_bias_act",
            "linear_bias_act_split", "mlp_forward",
-           "dlrm_forward_workspace_bytes", "dlrm_forward", "dlrm_plan_create",
+           "dlrm_forward_workspace_bytes", "dlrm_forward", "dlrm_forward_noalloc",
+           "dlrm_plan_create",
            "dlrm_plan_update", "dlrm_plan_run", "dlrm_plan_destroy")
 
 _vp = ctypes.c_void_p
@@ -116,6 +118,9 @@ def load(path: str = LIB_PATH):
     lib.dlrm_forward.restype = ctypes.c_int
     lib.dlrm_forward.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
                                  ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t, _vp]
+    lib.dlrm_forward_noalloc.restype = ctypes.c_int
+    lib.dlrm_forward_noalloc.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
+                                         ctypes.POINTER(_i64), _vp, _vp]
     lib.dlrm_plan_create.restype = ctypes.c_int
     lib.dlrm_plan_create.argtypes = [ctypes.POINTER(Model), _i32, _vp, ptrs, ptrs,
                                      ctypes.POINTER(_i64), _vp, _vp, ctypes.c_size_t, _i32,
@@ -595,6 +600,27 @@ def dlrm_forward(model: DlrmModel, dense_in, indices, offsets=None, out=None, wo
                             _i64_array([i.numel() for i in indices]), out.data_ptr(), ws,
                             workspace.numel() * workspace.element_size(), s.cuda_stream),
            "dlrm_forward")
+    return out
+
+
+def dlrm_forward_noalloc(model: DlrmModel, dense_in, indices, out, offsets=None, stream=None):
+    """DLRMv1 forward into the caller's `out` (B, top[last].out_features)
+    with the library's fixed scratch array as workspace: the C call
+    allocates nothing (see include/dlrm_embedding_bag.h for its limit)."""
+    torch = _torch()
+    lib = load()
+    _dev(dense_in, torch.float32, "dense_in")
+    _dev(out, torch.float32, "out")
+    B = dense_in.shape[0]
+    indices = [_dev(i, torch.int32, f"indices[{k}]") for k, i in enumerate(indices)]
+    if offsets is not None:
+        offsets = [_dev(o, torch.int32, f"offsets[{k}]") for k, o in enumerate(offsets)]
+    _check(lib.dlrm_forward_noalloc(ctypes.byref(model.struct), B, dense_in.data_ptr(),
+                                    _ptr_array(indices),
+                                    _ptr_array(offsets) if offsets is not None else None,
+                                    _i64_array([i.numel() for i in indices]), out.data_ptr(),
+                                    _stream(stream)),
+           "dlrm_forward_noalloc")
     return out
 
 

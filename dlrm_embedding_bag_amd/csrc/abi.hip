@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <functional>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -186,11 +187,12 @@ SmallLayer small_layer_of(const dlrm_layer &L) {
   return SmallLayer{L.weight, L.bias, L.in_features, L.out_features, L.act};
 }
 
-// Checks every argument of a forward (nothing is enqueued).
+// Checks every argument of a forward (nothing is enqueued); the workspace
+// only when check_ws.
 int validate_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                      const int32_t *const *indices, const int32_t *const *offsets,
                      const int64_t *n_idx, const float *out, const void *workspace,
-                     size_t workspace_bytes) {
+                     size_t workspace_bytes, bool check_ws = true) {
   ForwardLayout lay;
   int rc = plan_forward(model, batch, lay);
   if (rc) return rc;
@@ -201,7 +203,9 @@ int validate_forward(const dlrm_model *model, int32_t batch, const float *dense_
   rc = pack_bags(g, ts, gc);
   if (rc) return rc;
   if (batch == 0) return DLRM_OK;
-  if (!dense_in || !out || !workspace) return DLRM_ERR_NULL;
+  if (!dense_in || !out) return DLRM_ERR_NULL;
+  if (!check_ws) return DLRM_OK;
+  if (!workspace) return DLRM_ERR_NULL;
   if (workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return DLRM_ERR_WORKSPACE;
   return DLRM_OK;
@@ -375,6 +379,44 @@ int capture_forward(const dlrm_model &model, int32_t batch, const float *dense_i
   }
   *graph = g;
   return DLRM_OK;
+}
+
+// The workspace of dlrm_forward_noalloc: a fixed device array of the library
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never passes `scratch` itself to a kernel (on the host it is a
+// stand-in, not a device address): it takes the array's device address from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[DLRM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void *ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's scratch address, or nullptr (status in *rc).
+void *scratch_address(int *rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *rc = DLRM_ERR_HIP;
+    return nullptr;
+  }
+  if (dev >= kMaxDevices) {
+    *rc = DLRM_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  ScratchSlot &slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot]() {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr) {
+    *rc = DLRM_ERR_HIP;
+    return nullptr;
+  }
+  *rc = DLRM_OK;
+  return slot.ptr;
 }
 
 }  // namespace
@@ -578,6 +620,24 @@ int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  void *stream) {
   return enqueue_forward(model, batch, dense_in, indices, offsets, n_idx, out, workspace,
                          workspace_bytes, Emitter{(hipStream_t)stream, nullptr});
+}
+
+int dlrm_forward_noalloc(const dlrm_model *model, int32_t batch, const float *dense_in,
+                         const int32_t *const *indices, const int32_t *const *offsets,
+                         const int64_t *n_idx, float *out, void *stream) {
+  // every argument is checked before the scratch array is looked up
+  int rc = validate_forward(model, batch, dense_in, indices, offsets, n_idx, out, nullptr, 0,
+                            /*check_ws=*/false);
+  if (rc) return rc;
+  if (batch == 0) return DLRM_OK;  // nothing to read or write
+  ForwardLayout lay;
+  rc = plan_forward(model, batch, lay);
+  if (rc) return rc;
+  if (lay.total > (size_t)DLRM_NOALLOC_SCRATCH_BYTES) return DLRM_ERR_WORKSPACE;
+  void *ws = scratch_address(&rc);
+  if (!ws) return rc;
+  return enqueue_forward(model, batch, dense_in, indices, offsets, n_idx, out, ws,
+                         (size_t)DLRM_NOALLOC_SCRATCH_BYTES, Emitter{(hipStream_t)stream, nullptr});
 }
 
 // ---------------------------------------------------------------------------

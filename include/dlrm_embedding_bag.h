@@ -13,11 +13,12 @@
  *  - The caller owns every buffer.  The compute calls allocate no device
  *    memory and keep no pointer after they return ([FASTPATHS] runtime.rs:
  *    non-owning views over caller memory); dlrm_plan_create allocates host
- *    memory for the plan it returns.  The library holds one piece of mutable
- *    state: the calling thread's kernel-timing events
+ *    memory for the plan it returns.  The library holds two pieces of
+ *    mutable state: the calling thread's kernel-timing events
  *    (dlrm_set_kernel_timing_events, measurement support, off unless a
- *    thread sets it).  Apart from it, calls on different streams or threads
- *    are independent and re-entrant.
+ *    thread sets it) and the per-GPU scratch array of dlrm_forward_noalloc
+ *    (shared by that call only).  Apart from them, calls on different
+ *    streams or threads are independent and re-entrant.
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *    Every call only enqueues work on `stream` and never synchronizes
  *    ([FASTPATHS] runtime.rs: execute() stays capturable, no trailing sync).
@@ -419,6 +420,30 @@ DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *d
                  const int32_t *const *indices, const int32_t *const *offsets,
                  const int64_t *n_idx, float *out, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/*
+ * dlrm_forward_noalloc -- dlrm_forward without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * validation and results as dlrm_forward, with the workspace taken from a
+ * fixed device array of the library of DLRM_NOALLOC_SCRATCH_BYTES bytes
+ * (every GPU the library runs on holds its own copy until the process ends).
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  Its first call on a device looks up that device's array address
+ * once (hipGetSymbolAddress, with the device current).
+ *   Limit: a forward whose dlrm_forward_workspace_bytes exceeds
+ *          DLRM_NOALLOC_SCRATCH_BYTES returns DLRM_ERR_WORKSPACE before any
+ *          work is enqueued (the full-size model 13-512-256-64 / 26 tables /
+ *          415-512-256-1 fits up to about 11,000 samples).
+ *   Sharing: all calls on one GPU share its array, which keeps the last
+ *          call's contents; calls that overlap on one GPU (other streams or
+ *          threads without ordering between them) race and give undefined
+ *          results.  Calls ordered on one stream are safe.
+ */
+#define DLRM_NOALLOC_SCRATCH_BYTES (64u << 20)
+DLRM_API int dlrm_forward_noalloc(const dlrm_model *model, int32_t batch, const float *dense_in,
+                                  const int32_t *const *indices, const int32_t *const *offsets,
+                                  const int64_t *n_idx, float *out, void *stream);
 
 /*
  * Plans -- the forward recorded once into a HIP graph and replayed

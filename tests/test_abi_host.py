@@ -289,6 +289,26 @@ def test_no_environment_switch_in_the_library():
         assert "getenv" not in text and "environ" not in text, name
 
 
+def test_noalloc_forward_argument_errors(lib):
+    """dlrm_forward_noalloc validates like dlrm_forward and refuses, before
+    any HIP call, a forward whose workspace exceeds its fixed array."""
+    K, D = 26, 64
+    P = 27 * 26 // 2
+    good = _model([(13, 512, 1), (512, 256, 1), (256, 64, 1)],
+                  [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D)
+    f = lib.dlrm_forward_noalloc
+    idx = (ctypes.c_void_p * K)(*[FAKE] * K)
+    big = 16384
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(good), big) > abi.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(good), big, FAKE, idx, None, _n(K, big * 20), FAKE, None) == 4
+    assert f(None, 64, FAKE, idx, None, _n(K, 64 * 20), FAKE, None) == 1
+    bad_dim = _model([(13, 32, 1)], [(D + P, 1, 2)], K, D)
+    assert f(ctypes.byref(bad_dim), 64, FAKE, idx, None, _n(K, 64 * 20), FAKE, None) == 2
+    assert f(ctypes.byref(good), 64, FAKE, idx, None, _n(K, 64 * 20 + 1), FAKE, None) == 2
+    assert f(ctypes.byref(good), 0, FAKE, idx, None, _n(K, 0), FAKE, None) == 0
+    assert abi.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_plan_argument_errors(lib):
     """dlrm_plan_create validates like dlrm_forward before touching HIP."""
     K, D = 26, 64
