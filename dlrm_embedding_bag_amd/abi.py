@@ -26,12 +26,12 @@ MAX_DIM = 1024
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 POOLS = {"sum": 0, "mean": 1}
 PLAN_MODES = {"direct": 0, "graph": 1}
-FORWARD_OPTIONS = {"layered": 1, "unfused_head": 2}
+FORWARD_OPTIONS = {"layered": 1, "unfused_head": 2, "unfused_bottom": 4}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "dlrm_set_kernel_timing_events",
            "dlrm_stream_read", "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",
            "dlrm_emb_interact_pool", "dlrm_emb_interact_dots", "linear_bias_act",
-           "linear_bias_act_split", "mlp_forward",
+           "linear_bias_act_split", "linear_bias_act_head", "mlp_forward",
            "dlrm_forward_workspace_bytes", "dlrm_forward", "dlrm_forward_noalloc",
            "dlrm_plan_create",
            "dlrm_plan_update", "dlrm_plan_run", "dlrm_plan_destroy")
@@ -111,6 +111,9 @@ def load(path: str = LIB_PATH):
     lib.linear_bias_act.restype = ctypes.c_int
     lib.linear_bias_act.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _i64,
                                     _vp]
+    lib.linear_bias_act_head.restype = ctypes.c_int
+    lib.linear_bias_act_head.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _i32, _vp, _vp,
+                                         _i32, _vp, _i64, _vp]
     lib.mlp_forward.restype = ctypes.c_int
     lib.mlp_forward.argtypes = [_i32, _i32, ctypes.POINTER(Layer), _vp, _i64, _vp, _i64, _vp]
     lib.dlrm_forward_workspace_bytes.restype = ctypes.c_size_t
@@ -490,6 +493,47 @@ def linear_bias_act(a, w, bias=None, act="none", out=None, stream=None):
     return out
 
 
+def linear_bias_act_head(a, w, bias, act, head_w, head_bias=None, head_act="sigmoid", out=None,
+                         stream=None):
+    """head_act(act(a @ w.T + bias) @ head_w + head_bias) as (M, 1) float32:
+    a layer and a one-output head in one launch (n <= 256)."""
+    torch = _torch()
+    lib = load()
+    _matrix(a, "a")
+    _dev(w, torch.float32, "w")
+    M, Kd = a.shape
+    N = w.shape[0]
+    if w.shape[1] != Kd:
+        raise ValueError("w must be (N, K)")
+    bp = None
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+        if bias.numel() != N:
+            raise ValueError("bias must have N elements")
+        bp = bias.data_ptr()
+    _dev(head_w, torch.float32, "head_w")
+    if head_w.numel() != N:
+        raise ValueError("head_w must have N elements")
+    hb = None
+    if head_bias is not None:
+        _dev(head_bias, torch.float32, "head_bias")
+        if head_bias.numel() != 1:
+            raise ValueError("head_bias must have one element")
+        hb = head_bias.data_ptr()
+    if out is None:
+        out = _empty((M, 1), a.device, stream)
+    if (not isinstance(out, torch.Tensor) or out.device.type != "cuda"
+            or out.dtype != torch.float32 or out.dim() != 2 or out.shape != (M, 1)):
+        raise ValueError("out must be an (M, 1) float32 GPU tensor")
+    _check(lib.linear_bias_act_head(M, N, Kd, a.data_ptr(), a.stride(0), w.data_ptr(), bp,
+                                    ACTS[act] if isinstance(act, str) else int(act),
+                                    head_w.data_ptr(), hb,
+                                    ACTS[head_act] if isinstance(head_act, str) else int(head_act),
+                                    out.data_ptr(), max(out.stride(0), 1), _stream(stream)),
+           "linear_bias_act_head")
+    return out
+
+
 def _layer_array(spec, what, keep):
     torch = _torch()
     arr = (Layer * len(spec))()
@@ -547,7 +591,8 @@ class DlrmModel:
     GPU float32 tensors; tables: list of (rows_k, D) GPU float32 tensors;
     options: names from FORWARD_OPTIONS ("layered": never the one-launch
     small-model kernel; "unfused_head": the last top layer as its own
-    launch), or the raw bits.
+    launch; "unfused_bottom": each bottom layer as its own launch), or the
+    raw bits.
     """
 
     def __init__(self, bottom, top, tables, options=()):

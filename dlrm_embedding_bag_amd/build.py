@@ -13,8 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdlrm_mi355x.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["abi.hip", "emb_interact.hip", "forward_small.hip", "linear.hip", "mlp_chain.hip",
-           "probe.hip"]
+SOURCES = ["abi.hip", "bottom_mlp.hip", "emb_interact.hip", "forward_small.hip", "linear.hip",
+           "mlp_chain.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -124,7 +124,34 @@ struct ForwardLayout {
   size_t off_R = 0, off_buf0 = 0, off_buf1 = 0, total = 0;
 };
 
-constexpr uint32_t kForwardOptions = DLRM_FORWARD_LAYERED | DLRM_FORWARD_UNFUSED_HEAD;
+constexpr uint32_t kForwardOptions =
+    DLRM_FORWARD_LAYERED | DLRM_FORWARD_UNFUSED_HEAD | DLRM_FORWARD_UNFUSED_BOTTOM;
+
+// The bottom-MLP kernel's parameters for a three-layer stack, or false.
+bool pack_bottom(int32_t m, const dlrm_layer *L, const float *x, int64_t ldx, float *y,
+                 int64_t ldy, BottomParams &bp) {
+  bp = BottomParams{};
+  bp.M = m;
+  bp.K0 = L[0].in_features;
+  bp.N0 = L[0].out_features;
+  bp.N1 = L[1].out_features;
+  bp.N2 = L[2].out_features;
+  if (L[1].in_features != bp.N0 || L[2].in_features != bp.N1) return false;
+  bp.x = x;
+  bp.ldx = ldx;
+  bp.W0 = L[0].weight;
+  bp.b0 = L[0].bias;
+  bp.W1 = L[1].weight;
+  bp.b1 = L[1].bias;
+  bp.W2 = L[2].weight;
+  bp.b2 = L[2].bias;
+  bp.act0 = L[0].act;
+  bp.act1 = L[1].act;
+  bp.act2 = L[2].act;
+  bp.y = y;
+  bp.ldy = ldy;
+  return bottom_mlp_supported(bp);
+}
 
 // Checks the model's shapes and computes the workspace layout for batch B.
 int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
@@ -257,9 +284,19 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
                    reinterpret_cast<float *>(ws + lay.off_buf1)};
 
   // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
+  // A three-layer stack the fused kernel takes runs as one launch when the
+  // batch fills the chip with 32-row bands.
   const float *x = dense_in;
   int64_t ldx = model->bottom[0].in_features;
-  for (int l = 0; l < model->num_bottom; ++l) {
+  BottomParams bp;
+  const bool fuse_bottom = !(model->options & DLRM_FORWARD_UNFUSED_BOTTOM) &&
+                           model->num_bottom == 3 && bottom_mlp_preferred(B) &&
+                           pack_bottom(B, model->bottom, dense_in, ldx, R, lay.ldR, bp);
+  if (fuse_bottom) {
+    rc = emit(em, [=](hipStream_t s) { return launch_bottom_mlp(bp, s); });
+    if (rc) return rc;
+  }
+  for (int l = 0; l < model->num_bottom && !fuse_bottom; ++l) {
     const dlrm_layer &L = model->bottom[l];
     const bool last = l + 1 == model->num_bottom;
     float *y = last ? R : buf[l & 1];
@@ -290,11 +327,27 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   rc = emit(em, [=](hipStream_t s) { return launch_interact(&ts, gc, ip, threads, s); });
   if (rc) return rc;
 
-  // Top MLP on cat(dense, dots) = R.
+  // Top MLP on cat(dense, dots) = R.  A one-output last layer (the sigmoid
+  // head) is folded into the epilogue of the layer before it when that layer
+  // is at most 256 wide and the batch fills the chip with 32-row bands: its
+  // activations are then never stored.
   x = R;
   ldx = lay.ldR;
-  for (int l = 0; l < model->num_top; ++l) {
+  const int nt = model->num_top;
+  const bool fuse_head = !(model->options & DLRM_FORWARD_UNFUSED_HEAD) && nt >= 2 &&
+                         model->top[nt - 1].out_features == 1 &&
+                         linear_head_supported(model->top[nt - 2].out_features,
+                                               model->top[nt - 2].in_features) &&
+                         linear_head_preferred(B);
+  for (int l = 0; l < nt; ++l) {
     const dlrm_layer &L = model->top[l];
+    if (fuse_head && l == nt - 2) {
+      const dlrm_layer &H = model->top[nt - 1];
+      return emit(em, [=](hipStream_t s) {
+        return launch_linear_head(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
+                                  L.act, H.weight, H.bias, H.act, out, 1, s);
+      });
+    }
     const bool last = l + 1 == model->num_top;
     float *y = last ? out : buf[l & 1];
     const int64_t ldy = last ? L.out_features : lay.ld_buf;
@@ -589,6 +642,19 @@ int linear_bias_act_split(int32_t m, int32_t n, int32_t k_lo, const float *a_lo,
                                         act, c, ldc, (hipStream_t)stream));
 }
 
+int linear_bias_act_head(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda,
+                         const float *w, const float *bias, int32_t act, const float *head_w,
+                         const float *head_bias, int32_t head_act, float *out, int64_t ldo,
+                         void *stream) {
+  if (m < 0 || n < 1 || k < 1 || lda < k || ldo < 1 || !valid_act(act) || !valid_act(head_act))
+    return DLRM_ERR_SHAPE;
+  if (!linear_head_supported(n, k)) return DLRM_ERR_UNSUPPORTED;
+  if (m == 0) return DLRM_OK;  // nothing to read or write
+  if (!a || !w || !head_w || !out) return DLRM_ERR_NULL;
+  return hip_status(launch_linear_head(m, n, k, a, lda, w, bias, act, head_w, head_bias,
+                                       head_act, out, ldo, (hipStream_t)stream));
+}
+
 int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers, const float *a,
                 int64_t lda, float *c, int64_t ldc, void *stream) {
   if (m < 0 || num_layers < 1) return DLRM_ERR_SHAPE;
@@ -603,6 +669,11 @@ int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers, const f
     return DLRM_ERR_SHAPE;
   if (m == 0) return DLRM_OK;  // nothing to read or write
   if (!a || !c) return DLRM_ERR_NULL;
+  // A three-layer stack of the bottom-MLP shape over enough rows takes the
+  // fused bottom kernel; anything else the MLP chain kernel.
+  BottomParams bp;
+  if (num_layers == 3 && bottom_mlp_preferred(m) && pack_bottom(m, layers, a, lda, c, ldc, bp))
+    return hip_status(launch_bottom_mlp(bp, (hipStream_t)stream));
   ChainParams cp;
   if (!pack_chain(m, num_layers, layers, a, lda, c, ldc, cp)) return DLRM_ERR_UNSUPPORTED;
   return hip_status(launch_mlp_chain(cp, (hipStream_t)stream));

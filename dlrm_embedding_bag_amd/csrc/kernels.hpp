@@ -119,4 +119,34 @@ hipError_t launch_linear_split(int M, int N, int K_lo, const float *A_lo, int64_
                                const float *bias, int act, float *C, int64_t ldc,
                                hipStream_t stream);
 
+// The three-layer bottom MLP in one launch (bottom_mlp.hip):
+// y = act2(act1(act0(x W0^T + b0) W1^T + b1) W2^T + b2), hidden layers on chip.
+struct BottomParams {
+  int M, K0, N0, N1, N2;
+  const float *x;  // (M, K0), row stride ldx
+  int64_t ldx;
+  const float *W0, *b0, *W1, *b1, *W2, *b2;  // (N_l, K_l) dense; biases (N_l,) or nullptr
+  int act0, act1, act2;
+  float *y;        // (M, N2), row stride ldy
+  int64_t ldy;
+};
+// True when the kernel takes these shapes: 4 <= K0 <= 15, N0 a multiple of 64
+// (>= 128), N1 <= 256 and N2 <= 64 multiples of 16, W1 and W2 16-byte
+// aligned.
+bool bottom_mlp_supported(const BottomParams &p);
+// Whether it beats three layer launches at M rows (its grid is M / 32).
+bool bottom_mlp_preferred(int M);
+hipError_t launch_bottom_mlp(const BottomParams &p, hipStream_t stream);
+
+// Two layers in one launch: h = act(A W^T + bias) (N <= 256 columns, never
+// stored) followed by a one-output head, out[m] = head_act(head_bias +
+// sum_n h[m][n] head_w[n]), out row stride ldo.
+bool linear_head_supported(int N, int K);
+// Whether the fused launch beats the two layer launches at M rows.
+bool linear_head_preferred(int M);
+hipError_t launch_linear_head(int M, int N, int K, const float *A, int64_t lda, const float *W,
+                              const float *bias, int act, const float *head_w,
+                              const float *head_bias, int head_act, float *out, int64_t ldo,
+                              hipStream_t stream);
+
 }  // namespace dlrm

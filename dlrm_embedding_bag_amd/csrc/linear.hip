@@ -70,12 +70,18 @@ struct ASrc {
   int k_lo;
 };
 
+// Four floats at a 4-byte-aligned address: global memory takes a 16-byte
+// load at dword alignment, so rows of a K that is not a multiple of 4 (the
+// 415-wide top layer) still load as one global_load_dwordx4 per lane.
+typedef float float4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 template <bool VEC>
 __device__ __forceinline__ float4 load_full(const float *__restrict__ base, int64_t ld, int row,
                                             int k) {
   const float *p = base + (int64_t)row * ld + k;
   if (VEC) return *reinterpret_cast<const float4 *>(p);
-  return make_float4(p[0], p[1], p[2], p[3]);
+  const float4_a4 v = *reinterpret_cast<const float4_a4 *>(p);
+  return make_float4(v.x, v.y, v.z, v.w);
 }
 
 // Same for the last, partial slab: columns at or past K read as zero.  The
@@ -132,14 +138,27 @@ __device__ __forceinline__ float4 load_a_tail(const ASrc &a, int row, int k, int
   }
 }
 
-template <int BM, int BN, int GM, int GN, int KS, bool VA, bool VW, bool VC, bool SPLIT>
+// A one-output layer applied to this layer's activations in the epilogue
+// (the sigmoid head of the top MLP): out[m] = act(bias + sum_n h[m][n] w[n])
+// with h = this layer's act(A W^T + bias) row, which is never stored.
+struct HeadArgs {
+  const float *w;     // (N,) weights of the head
+  const float *bias;  // (1,) or nullptr
+  int act;
+  float *out;         // out[m * ldo]
+  int64_t ldo;
+};
+
+template <int BM, int BN, int GM, int GN, int KS, bool VA, bool VW, bool VC, bool SPLIT,
+          bool HEAD = false>
 __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, int K,
                                                                  const ASrc A,
                                                                  const float *__restrict__ W,
                                                                  const float *__restrict__ bias,
                                                                  int act, float *__restrict__ C,
                                                                  int64_t ldc, int tiles_n,
-                                                                 int xcd_chunk) {
+                                                                 int xcd_chunk,
+                                                                 const HeadArgs head) {
   // KS wave groups split k: a staged slab holds KS x kBK columns and group g
   // multiplies columns [g kBK, (g + 1) kBK) of it; the groups' partial tiles
   // are added in group order through LDS at the end.
@@ -295,7 +314,24 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
   stash(0, ra0, rw0);
   if (nslab > 1) fetch(1, ra1, rw1);
   __syncthreads();
-  for (int sl = 0; sl < nslab; sl += 2) {
+  int sl = 0;
+  // Steady state: both slabs fetched in an iteration are full, so every
+  // fetch is issued unconditionally.  (With a conditional fetch the
+  // compiler's wait-count pass merges the paths with and without the new
+  // loads and makes each stash wait for the loads just issued, which turns
+  // the two-slab prefetch into one.)
+  for (; sl + 3 < nfull; sl += 2) {
+    fetch(sl + 2, ra0, rw0);
+    compute(0);
+    stash(1, ra1, rw1);
+    __syncthreads();
+    fetch(sl + 3, ra1, rw1);
+    compute(1);
+    stash(0, ra0, rw0);
+    __syncthreads();
+  }
+  // The last slabs (fewer than two full ones ahead, or a partial one).
+  for (; sl < nslab; sl += 2) {
     // even slab: buffer 0; register set 0 is free
     if (sl + 2 < nslab) fetch(sl + 2, ra0, rw0);
     compute(0);
@@ -324,17 +360,71 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
           for (int v = 0; v < 4; ++v) red[((a * TN + b) * 4 + v) * 64] = acc[a][b][v];
     }
     __syncthreads();
-    if (kg > 0) return;
+    if (kg > 0 && !HEAD) return;  // (with a head every wave meets its barrier)
+    if (kg == 0) {
 #pragma unroll
-    for (int g = 1; g < KS; ++g) {
-      const float *red = lds + ((size_t)((g - 1) * GM * GN + wg) * PER) * 64 + lane;
+      for (int g = 1; g < KS; ++g) {
+        const float *red = lds + ((size_t)((g - 1) * GM * GN + wg) * PER) * 64 + lane;
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b)
+          for (int b = 0; b < TN; ++b)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[a][b][v] += red[((a * TN + b) * 4 + v) * 64];
+            for (int v = 0; v < 4; ++v) acc[a][b][v] += red[((a * TN + b) * 4 + v) * 64];
+      }
     }
+  }
+
+  if constexpr (HEAD) {
+    // The tile owns whole rows (BN >= N): each wave of group 0 folds its
+    // columns into one partial dot per row, act(acc + bias[n]) * w[n] summed
+    // over its columns in (b, v) order; the 4 lanes of a row (lq) are then
+    // added by two butterfly steps, and the waves' partials in wave order
+    // through LDS.  The order is fixed, so the result is deterministic.
+    __shared__ float head_part[GM * GN * BM];
+    if (kg == 0) {
+      float part[TM];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) part[a] = 0.0f;
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int n = n0 + wn * WN + b * 16 + 4 * lq;
+        float bv[4], hw[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool in = n + v < N;
+          bv[v] = (bias && in) ? bias[n + v] : 0.0f;
+          hw[v] = in ? head.w[n + v] : 0.0f;
+        }
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (n + v < N) part[a] = __builtin_fmaf(apply_act(acc[a][b][v] + bv[v], act), hw[v],
+                                                    part[a]);
+      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        part[a] += __shfl_xor(part[a], 16);
+        part[a] += __shfl_xor(part[a], 32);
+      }
+      if (lq == 0) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a) head_part[wn * GM * BM + wm * WM + a * 16 + l16] = part[a];
+      }
+    }
+    __syncthreads();
+    if (tid < BM) {
+      const int m = m0 + tid;
+      if (m < M) {
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < GN; ++w) t += head_part[w * GM * BM + tid];
+        if (head.bias) t += head.bias[0];
+        head.out[(int64_t)m * head.ldo] = apply_act(t, head.act);
+      }
+    }
+    return;
   }
 
   // Epilogue: lane holds C[m][n .. n+3] for m = .. + l16, n = .. + 4*lq.
@@ -491,7 +581,7 @@ hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, const float *W, c
   dim3 grid((unsigned)tiles), block(64 * GM * GN * KS);
 #define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                          \
   launch_kernel((gemm_kernel<BM, BN, GM, GN, KS, A_, W_, C_, SPLIT>), grid, block, 0, stream, \
-                M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk)
+                M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk, HeadArgs{})
   if (va && vw && vc)
     DLRM_GEMM_LAUNCH(true, true, true);
   else if (va && !vw && vc)
@@ -616,6 +706,45 @@ hipError_t launch_linear_split(int M, int N, int K_lo, const float *A_lo, int64_
   const bool va = aligned16(A_lo) && lda_lo % 4 == 0 && aligned16(A_hi) && lda_hi % 4 == 0 &&
                   K_lo % 4 == 0;
   return launch_linear_src<true>(M, N, K_lo + K_hi, src, va, W, bias, act, C, ldc, stream);
+}
+
+// The head tile: 32 whole rows (up to 256 columns) per workgroup on 4 waves
+// of 32 x 64, split over KS wave groups along k.
+constexpr int kHeadBM = 32, kHeadBN = 256, kHeadKS = 2;
+
+bool linear_head_supported(int N, int K) { return N >= 1 && N <= kHeadBN && K >= 1; }
+
+// One workgroup per 32 rows: the fused launch pays off once its grid covers
+// most of the chip (measured at 512 -> 256 -> 1: M = 8192 24.0 us against
+// 27.3 us for the two launches; M = 2048 23.2 us against 12.8 us).
+bool linear_head_preferred(int M) { return (int64_t)(M + kHeadBM - 1) / kHeadBM >= 224; }
+
+hipError_t launch_linear_head(int M, int N, int K, const float *A, int64_t lda, const float *W,
+                              const float *bias, int act, const float *head_w,
+                              const float *head_bias, int head_act, float *out, int64_t ldo,
+                              hipStream_t stream) {
+  if (!linear_head_supported(N, K)) return hipErrorInvalidValue;
+  const ASrc src{A, lda, nullptr, 0, K};
+  const bool va = aligned16(A) && lda % 4 == 0;
+  const bool vw = aligned16(W) && K % 4 == 0;
+  const HeadArgs head{head_w, head_bias, head_act, out, ldo};
+  const int tiles = (M + kHeadBM - 1) / kHeadBM;
+  const int xcd_chunk = (tiles % 8 == 0) ? tiles / 8 : 0;
+  dim3 grid((unsigned)tiles), block(64 * 4 * kHeadKS);
+#define DLRM_HEAD_LAUNCH(A_, W_)                                                              \
+  launch_kernel((gemm_kernel<kHeadBM, kHeadBN, 1, 4, kHeadKS, A_, W_, false, false, true>), grid, \
+                block, 0, stream, M, N, K, src, W, bias, act, nullptr, (int64_t)0, 1, xcd_chunk,  \
+                head)
+  if (va && vw)
+    DLRM_HEAD_LAUNCH(true, true);
+  else if (va)
+    DLRM_HEAD_LAUNCH(true, false);
+  else if (vw)
+    DLRM_HEAD_LAUNCH(false, true);
+  else
+    DLRM_HEAD_LAUNCH(false, false);
+#undef DLRM_HEAD_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace dlrm

@@ -340,6 +340,30 @@ DLRM_API int linear_bias_act_split(int32_t m, int32_t n, int32_t k_lo, const flo
                                    int64_t lda_hi, const float *w, const float *bias, int32_t act,
                                    float *c, int64_t ldc, void *stream);
 
+/*
+ * linear_bias_act_head -- a linear layer followed by a one-output head in one
+ * launch, the end of the DLRMv1 top MLP ([FASTPATHS] matmul2d.rs, Activation
+ * epilogue and linear_bias_sigmoid; commit message: the top MLP ends in a
+ * sigmoid):
+ *
+ *   h[m, n] = act(bias[n] + sum_k a[m, k] * w[n, k])          (never stored)
+ *   out[m]  = head_act(head_bias + sum_n h[m, n] * head_w[n])
+ *
+ *   m >= 0 (0: nothing to do), 1 <= n <= 256, k >= 1
+ *   a          (m, k) float32 with row stride lda >= k
+ *   w          (n, k) float32, dense;  bias (n,) or NULL;  act a dlrm_act
+ *   head_w     (n,) float32 (the (1, n) weight of the head);  head_bias (1,)
+ *              or NULL;  head_act a dlrm_act
+ *   out        (m,) float32 with stride ldo >= 1 (out[m * ldo])
+ * n > 256 is DLRM_ERR_UNSUPPORTED.  A workgroup owns 32 whole rows, so the
+ * head's sum over n runs in a fixed order (deterministic); it differs from
+ * the order of linear_bias_act on the stored h within float rounding.
+ */
+DLRM_API int linear_bias_act_head(int32_t m, int32_t n, int32_t k, const float *a, int64_t lda,
+                                  const float *w, const float *bias, int32_t act,
+                                  const float *head_w, const float *head_bias, int32_t head_act,
+                                  float *out, int64_t ldo, void *stream);
+
 /* One MLP layer (of a dlrm_model or an mlp_forward stack). */
 typedef struct dlrm_layer {
   int32_t in_features;
@@ -375,6 +399,7 @@ DLRM_API int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers
  * within float rounding; these exist to compare them. */
 #define DLRM_FORWARD_LAYERED 1u  /* never the one-launch small-model kernel   */
 #define DLRM_FORWARD_UNFUSED_HEAD 2u /* the last top layer as its own launch  */
+#define DLRM_FORWARD_UNFUSED_BOTTOM 4u /* each bottom layer as its own launch */
 
 /* A DLRMv1 model: bottom MLP, K embedding tables, top MLP.  All arrays of
  * this struct are [host]; the weights and tables they point to are device
@@ -413,8 +438,12 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  * Composition: a model whose MLPs hold at most 64 Ki weights in all (widths
  * <= 1024, <= 4 layers each) runs as ONE launch with every intermediate on
  * chip; larger models run each layer as its own tiled GEMM launch around the
- * fused gather + interaction (7 launches for 3 + 3 layers).  model->options
- * may force the layered composition (DLRM_FORWARD_LAYERED).
+ * fused gather + interaction, except that a one-output last top layer after
+ * a layer at most 256 wide runs in that layer's launch (linear_bias_act_head;
+ * 6 launches for 3 + 3 layers) when the batch is at least 7,137 samples.
+ * model->options may force the layered
+ * composition (DLRM_FORWARD_LAYERED) or the head as its own launch
+ * (DLRM_FORWARD_UNFUSED_HEAD).
  */
 DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  const int32_t *const *indices, const int32_t *const *offsets,

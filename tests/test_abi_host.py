@@ -265,17 +265,19 @@ def test_forward_options_are_validated(lib):
     B = 256
     base = lib.dlrm_forward_workspace_bytes(ctypes.byref(_model(*spec, K, D)), B)
     assert base > 0
-    for bits in (abi.FORWARD_OPTIONS["layered"], abi.FORWARD_OPTIONS["unfused_head"],
-                 abi.FORWARD_OPTIONS["layered"] | abi.FORWARD_OPTIONS["unfused_head"]):
+    every = 0
+    for v in abi.FORWARD_OPTIONS.values():
+        every |= v
+    for bits in list(abi.FORWARD_OPTIONS.values()) + [every]:
         m = _model(*spec, K, D, options=bits)
         assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == base
     idx = (ctypes.c_void_p * K)(*[FAKE] * K)
-    for bits in (4, 1 << 31, 0xFFFFFFFF):
+    for bits in (every + 1, 1 << 31, 0xFFFFFFFF):
         m = _model(*spec, K, D, options=bits)
         assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == 0
         assert lib.dlrm_forward(ctypes.byref(m), B, FAKE, idx, None, _n(K, B * 20), FAKE,
                                 FAKE, base, None) == 2
-    assert abi.forward_options(("layered", "unfused_head")) == 3
+    assert abi.forward_options(("layered", "unfused_head", "unfused_bottom")) == 7
     with pytest.raises(ValueError):
         abi.forward_options(("fast",))
 
@@ -287,6 +289,18 @@ def test_no_environment_switch_in_the_library():
     for name in os.listdir(csrc):
         text = open(os.path.join(csrc, name)).read()
         assert "getenv" not in text and "environ" not in text, name
+
+
+def test_linear_head_argument_errors(lib):
+    f = lib.linear_bias_act_head
+    assert f(8, 257, 512, FAKE, 512, FAKE, None, 1, FAKE, None, 2, FAKE, 1, None) == 3  # n > 256
+    assert f(8, 0, 512, FAKE, 512, FAKE, None, 1, FAKE, None, 2, FAKE, 1, None) == 2    # n < 1
+    assert f(8, 64, 512, FAKE, 500, FAKE, None, 1, FAKE, None, 2, FAKE, 1, None) == 2   # lda < k
+    assert f(8, 64, 512, FAKE, 512, FAKE, None, 1, FAKE, None, 3, FAKE, 1, None) == 2   # head act
+    assert f(8, 64, 512, FAKE, 512, FAKE, None, 1, FAKE, None, 2, FAKE, 0, None) == 2   # ldo < 1
+    assert f(8, 64, 512, FAKE, 512, FAKE, None, 1, None, None, 2, FAKE, 1, None) == 1   # head_w
+    assert f(8, 64, 512, None, 512, FAKE, None, 1, FAKE, None, 2, FAKE, 1, None) == 1   # a NULL
+    assert f(0, 64, 512, None, 512, None, None, 1, None, None, 2, None, 1, None) == 0   # m == 0
 
 
 def test_noalloc_forward_argument_errors(lib):
