@@ -285,7 +285,7 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
 
   // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
   // A three-layer stack the fused kernel takes runs as one launch when the
-  // batch fills the chip with 32-row bands.
+  // batch is about one 32-row band per CU.
   const float *x = dense_in;
   int64_t ldx = model->bottom[0].in_features;
   BottomParams bp;
@@ -329,7 +329,7 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
 
   // Top MLP on cat(dense, dots) = R.  A one-output last layer (the sigmoid
   // head) is folded into the epilogue of the layer before it when that layer
-  // is at most 256 wide and the batch fills the chip with 32-row bands: its
+  // is at most 256 wide and the batch is about one 32-row band per CU: its
   // activations are then never stored.
   x = R;
   ldx = lay.ldR;
@@ -669,10 +669,11 @@ int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers, const f
     return DLRM_ERR_SHAPE;
   if (m == 0) return DLRM_OK;  // nothing to read or write
   if (!a || !c) return DLRM_ERR_NULL;
-  // A three-layer stack of the bottom-MLP shape over enough rows takes the
-  // fused bottom kernel; anything else the MLP chain kernel.
+  // A three-layer stack of the bottom-MLP shape takes the fused bottom
+  // kernel (faster than the chain kernel at every row count); anything else
+  // the MLP chain kernel.
   BottomParams bp;
-  if (num_layers == 3 && bottom_mlp_preferred(m) && pack_bottom(m, layers, a, lda, c, ldc, bp))
+  if (num_layers == 3 && pack_bottom(m, layers, a, lda, c, ldc, bp))
     return hip_status(launch_bottom_mlp(bp, (hipStream_t)stream));
   ChainParams cp;
   if (!pack_chain(m, num_layers, layers, a, lda, c, ldc, cp)) return DLRM_ERR_UNSUPPORTED;

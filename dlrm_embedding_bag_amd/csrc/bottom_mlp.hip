@@ -361,8 +361,15 @@ bool bottom_mlp_supported(const BottomParams &p) {
          p.ldx >= p.K0 && p.ldy >= p.N2 && aligned16(p.W1) && aligned16(p.W2);
 }
 
-// One workgroup per 32 rows: worth it once the grid covers most of the chip.
-bool bottom_mlp_preferred(int M) { return (int64_t)(M + kBM - 1) / kBM >= 224; }
+// One workgroup per 32 rows and per CU (157 KB of LDS): inside the forward
+// the fused launch beats three layer launches when its grid is about one band
+// per CU, 224..256 bands (measured at M = 8192: 34-35 us against 39.5 us;
+// at M = 16384 the forward's fused MLP launches took 183.6 us against 178.7
+// us for the layer launches, the second wave of bands costing more).
+bool bottom_mlp_preferred(int M) {
+  const int64_t bands = (int64_t)(M + kBM - 1) / kBM;
+  return bands >= 224 && bands <= 256;
+}
 
 hipError_t launch_bottom_mlp(const BottomParams &p, hipStream_t stream) {
   if (!bottom_mlp_supported(p)) return hipErrorInvalidValue;

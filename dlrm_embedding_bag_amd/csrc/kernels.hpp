@@ -134,7 +134,8 @@ struct BottomParams {
 // (>= 128), N1 <= 256 and N2 <= 64 multiples of 16, W1 and W2 16-byte
 // aligned.
 bool bottom_mlp_supported(const BottomParams &p);
-// Whether it beats three layer launches at M rows (its grid is M / 32).
+// Whether it beats three layer launches inside the forward at M rows (its
+// grid is M / 32 bands, one per CU at a time).
 bool bottom_mlp_preferred(int M);
 hipError_t launch_bottom_mlp(const BottomParams &p, hipStream_t stream);
 

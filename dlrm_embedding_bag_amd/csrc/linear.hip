@@ -714,10 +714,15 @@ constexpr int kHeadBM = 32, kHeadBN = 256, kHeadKS = 2;
 
 bool linear_head_supported(int N, int K) { return N >= 1 && N <= kHeadBN && K >= 1; }
 
-// One workgroup per 32 rows: the fused launch pays off once its grid covers
-// most of the chip (measured at 512 -> 256 -> 1: M = 8192 24.0 us against
-// 27.3 us for the two launches; M = 2048 23.2 us against 12.8 us).
-bool linear_head_preferred(int M) { return (int64_t)(M + kHeadBM - 1) / kHeadBM >= 224; }
+// One workgroup per 32 rows, one workgroup per CU (157 KB of LDS): the fused
+// launch pays off when its grid is about one band per CU, 224..256 bands
+// (measured at 512 -> 256 -> 1: M = 8192 24.0 us against 27.3 us for the
+// two launches; M = 2048 23.2 against 12.8 us; past 256 bands a second,
+// partial wave of bands costs more than the launch it saves).
+bool linear_head_preferred(int M) {
+  const int64_t bands = (int64_t)(M + kHeadBM - 1) / kHeadBM;
+  return bands >= 224 && bands <= 256;
+}
 
 hipError_t launch_linear_head(int M, int N, int K, const float *A, int64_t lda, const float *W,
                               const float *bias, int act, const float *head_w,

@@ -386,10 +386,16 @@ typedef struct dlrm_layer {
  *               layer l's out_features
  *   a           (m, layers[0].in_features) float32, row stride lda
  *   c           (m, layers[last].out_features) float32, row stride ldc
- * Supported widths: every layer but a last one of out_features <= 8 must
- * have out_features in {64, 128, 256, 512}, and 16-byte aligned biases; at
- * least one layer must precede an out_features <= 8 layer.  Anything else
- * returns DLRM_ERR_UNSUPPORTED (linear_bias_act per layer always works).
+ * Kernels: a three-layer stack with 4 <= in_features <= 15, a first layer
+ * as wide as a multiple of 64 (>= 128), a second of at most 256 and a third
+ * of at most 64 outputs (multiples of 16), second and third weights 16-byte
+ * aligned (the DLRMv1 bottom MLP 13-512-256-64) runs in the fused bottom
+ * kernel: 32 rows per workgroup, the hidden layers in registers and LDS.
+ * Any other stack runs in the chain kernel, whose supported widths are:
+ * every layer but a last one of out_features <= 8 must have out_features in
+ * {64, 128, 256, 512}, and 16-byte aligned biases; at least one layer must
+ * precede an out_features <= 8 layer.  Anything else returns
+ * DLRM_ERR_UNSUPPORTED (linear_bias_act per layer always works).
  */
 DLRM_API int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers,
                          const float *a, int64_t lda, float *c, int64_t ldc, void *stream);
@@ -438,9 +444,11 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  * Composition: a model whose MLPs hold at most 64 Ki weights in all (widths
  * <= 1024, <= 4 layers each) runs as ONE launch with every intermediate on
  * chip; larger models run each layer as its own tiled GEMM launch around the
- * fused gather + interaction, except that a one-output last top layer after
- * a layer at most 256 wide runs in that layer's launch (linear_bias_act_head;
- * 6 launches for 3 + 3 layers) when the batch is at least 7,137 samples.
+ * fused gather + interaction, except when the batch is about one 32-row
+ * band per compute unit (7,137..8,192 samples): then a three-layer bottom
+ * MLP of the fused kernel's shapes (see mlp_forward) runs as one launch and
+ * a one-output last top layer after a layer at most 256 wide runs in that
+ * layer's launch (linear_bias_act_head): 4 launches for 3 + 3 layers.
  * model->options may force the layered
  * composition (DLRM_FORWARD_LAYERED) or the head as its own launch
  * (DLRM_FORWARD_UNFUSED_HEAD).

@@ -1,8 +1,8 @@
 """GPU parity of the fused bottom MLP (three linear + bias + activation
 layers in one launch, the hidden activations kept on chip), taken by
-mlp_forward and dlrm_forward for a three-layer stack with 4 <= K0 <= 15, N0 a
-multiple of 64, N1 <= 256 and N2 <= 64 multiples of 16, over at least 7,137
-rows.  Checked against the CPU oracle (layer by layer, fp64) on sampled rows
+mlp_forward for a three-layer stack with 4 <= K0 <= 15, N0 a multiple of 64,
+N1 <= 256 and N2 <= 64 multiples of 16 at any row count, and by dlrm_forward
+for such a stack at 7,137..8,192 rows.  Checked against the CPU oracle (layer by layer, fp64) on sampled rows
 and against the layer-by-layer launches within the float bar, over ragged
 row counts, odd K0, strided operands, missing biases and every activation."""
 import numpy as np
@@ -37,6 +37,8 @@ def _oracle_rows(a, layers, rows):
 
 STACKS = [  # (M, widths, acts)
     (8192, (13, 512, 256, 64), ("relu", "relu", "relu")),
+    (300, (13, 512, 256, 64), ("relu", "relu", "relu")),
+    (1, (13, 512, 256, 64), ("relu", "none", "relu")),
     (7137, (13, 512, 256, 64), ("relu", "relu", "relu")),
     (9001, (7, 128, 64, 16), ("relu", "none", "sigmoid")),
     (8200, (15, 192, 256, 32), ("sigmoid", "relu", "none")),
@@ -51,8 +53,8 @@ def test_fused_bottom_mlp_vs_oracle(M, widths, acts):
     layers = _layers(rng, widths, acts)
     dl = [(dev(w), dev(b), act) for w, b, act in layers]
     got = host(abi.mlp_forward(dev(a), dl))
-    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(M - 40, M),
-                                     rng.choice(M, 200, replace=False)]))
+    rows = np.unique(np.concatenate([np.arange(0, min(40, M)), np.arange(max(0, M - 40), M),
+                                     rng.choice(M, min(200, M), replace=False)]))
     assert_close(got[rows], _oracle_rows(a, layers, rows), f"fused bottom {widths}")
     x = dev(a)
     for w, b, act in dl:
@@ -81,9 +83,9 @@ def test_fused_bottom_mlp_strided_and_no_bias():
     assert host(cbuf2)[0] == -3.0 and np.all(host(cbuf2)[1:].reshape(M, 65)[:, 64] == -3.0)
 
 
-@pytest.mark.parametrize("B", [8192, 7137, 7136])
+@pytest.mark.parametrize("B", [8192, 7137, 7136, 8193])
 def test_forward_with_fused_bottom(B):
-    """dlrm_forward takes the fused bottom MLP from 7,137 samples on; the same
+    """dlrm_forward takes the fused bottom MLP at 7,137..8,192 samples; the same
     forward with each bottom layer as its own launch agrees within the float
     bar, and both match the oracle on sampled rows."""
     w = inputs.Workload("fb", batch=B, num_tables=26, rows=2000, dim=64, bag=4, dist="zipf",

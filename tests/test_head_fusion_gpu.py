@@ -34,7 +34,7 @@ def _models(tables, bl, tl):
 
 
 # (B, K, D, top widths) -- the full-size top MLP 415-512-256-1 and narrower ones;
-# the fused launch is taken from 7,137 samples on, smaller batches check that
+# the fused launch is taken at 7,137..8,192 samples, other batches check that
 # the composition falls back to two launches
 CASES = [(8192, 26, 64, (512, 256, 1)), (7201, 4, 16, (64, 7, 1)), (7137, 3, 16, (40, 24, 1)),
          (9000, 8, 64, (512, 200, 1)), (8192, 5, 12, (130, 1)), (16385, 2, 8, (256, 1)),
