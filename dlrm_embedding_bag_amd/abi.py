@@ -26,7 +26,7 @@ MAX_DIM = 1024
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 POOLS = {"sum": 0, "mean": 1}
 PLAN_MODES = {"direct": 0, "graph": 1}
-FORWARD_OPTIONS = {"layered": 1, "unfused_head": 2, "unfused_bottom": 4}
+FORWARD_OPTIONS = {"layered": 1, "unfused_head": 2, "unfused_bottom": 4, "unsplit_k": 8}
 EXPORTS = ("dlrm_status_string", "dlrm_abi_version", "dlrm_set_kernel_timing_events",
            "dlrm_stream_read", "emb_bag_sum_multi",
            "dlrm_interact_lower_tri", "dlrm_emb_interact", "emb_bag_pool",

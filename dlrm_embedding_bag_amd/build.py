@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdlrm_mi355x.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["abi.hip", "bottom_mlp.hip", "emb_interact.hip", "forward_small.hip", "linear.hip",
-           "mlp_chain.hip", "probe.hip"]
+           "mlp_chain.hip", "probe.hip", "slice_mlp.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -5,6 +5,7 @@
 #include <limits.h>
 #include <string.h>
 
+#include <algorithm>
 #include <functional>
 #include <mutex>
 #include <new>
@@ -119,13 +120,24 @@ bool pack_chain(int32_t m, int32_t n, const dlrm_layer *layers, const float *a, 
   return chain_supported(cp);
 }
 
+// How a forward's MLP layers are launched at one batch size: fused launches,
+// and how many k partials each layer stores (1 = its finished output).
+struct MlpComposition {
+  bool fuse_bottom = false;  // the three-layer bottom MLP as one launch, 32 rows per workgroup
+  int bottom_slices = 0;     // > 0: the three-layer bottom MLP as one slice launch storing
+                             // this many partials of its last layer, which the interaction adds
+  bool fuse_head = false;    // the last top layer folded into the one before
+  std::vector<int> split_bottom, split_top;  // partials each layer launched on its own stores
+};
+
 struct ForwardLayout {
   int64_t P = 0, ldR = 0, ld_buf = 0;
   size_t off_R = 0, off_buf0 = 0, off_buf1 = 0, total = 0;
+  MlpComposition mc;
 };
 
-constexpr uint32_t kForwardOptions =
-    DLRM_FORWARD_LAYERED | DLRM_FORWARD_UNFUSED_HEAD | DLRM_FORWARD_UNFUSED_BOTTOM;
+constexpr uint32_t kForwardOptions = DLRM_FORWARD_LAYERED | DLRM_FORWARD_UNFUSED_HEAD |
+                                     DLRM_FORWARD_UNFUSED_BOTTOM | DLRM_FORWARD_UNSPLIT_K;
 
 // The bottom-MLP kernel's parameters for a three-layer stack, or false.
 bool pack_bottom(int32_t m, const dlrm_layer *L, const float *x, int64_t ldx, float *y,
@@ -151,6 +163,79 @@ bool pack_bottom(int32_t m, const dlrm_layer *L, const float *x, int64_t ldx, fl
   bp.y = y;
   bp.ldy = ldy;
   return bottom_mlp_supported(bp);
+}
+
+// Partials stored by each layer of a layered MLP: a layer whose tiles leave
+// CUs idle splits its k (linear_split_count) when the next layer can read
+// that many partials; the last layer stores its output.
+std::vector<int> plan_layer_splits(int B, int n, const dlrm_layer *L, bool allow) {
+  std::vector<int> sp((size_t)n, 1);
+  for (int l = 0; allow && l + 1 < n; ++l) {
+    int s = linear_split_count(B, L[l].out_features, L[l].in_features);
+    while (s > 1 && !linear_reduce_supported(B, L[l + 1].out_features, L[l + 1].in_features,
+                                             L[l + 1].weight, s))
+      s /= 2;
+    sp[(size_t)l] = s;
+  }
+  return sp;
+}
+
+// The slice launch's parameters for a three-layer bottom MLP (shapes only;
+// the buffers are set at launch); false if it cannot run them.
+bool pack_slice(int B, const dlrm_layer *L, SliceParams &sp) {
+  sp = SliceParams{};
+  sp.M = B;
+  sp.K0 = L[0].in_features;
+  sp.N0 = L[0].out_features;
+  sp.N1 = L[1].out_features;
+  sp.N2 = L[2].out_features;
+  if (L[1].in_features != sp.N0 || L[2].in_features != sp.N1) return false;
+  sp.W0 = L[0].weight;
+  sp.b0 = L[0].bias;
+  sp.act0 = L[0].act;
+  sp.W1 = L[1].weight;
+  sp.b1 = L[1].bias;
+  sp.act1 = L[1].act;
+  sp.W2 = L[2].weight;
+  // placeholders for the shape check
+  sp.x = L[0].weight;
+  sp.ldx = sp.K0;
+  sp.P = reinterpret_cast<float *>(uintptr_t(256));
+  sp.ldp = round4(sp.N2);
+  sp.pstride = 0;
+  return slice_mlp_supported(sp);
+}
+
+// The slice launch takes the bottom MLP while its grid (one workgroup per
+// 16-row band and 64-column slice of layer 1) is at most one workgroup per
+// CU: measured in the forward (13-512-256-64) at B = 256 15.8 us against
+// 20.6 for the three layer launches, B = 1024 15.1 against 20.4, but at
+// B = 2048 (512 workgroups) 26.2 against 21.5.
+constexpr int64_t kSliceMaxWorkgroups = 256;
+
+// The launch composition of a validated model's MLPs at batch B.
+MlpComposition plan_mlps(const dlrm_model *m, int B) {
+  MlpComposition mc;
+  const uint32_t o = m->options;
+  const bool split = !(o & DLRM_FORWARD_UNSPLIT_K);
+  const int64_t bands = (B + 31) / 32;
+  const int nb = m->num_bottom, nt = m->num_top;
+  BottomParams bp;
+  mc.fuse_bottom = !(o & DLRM_FORWARD_UNFUSED_BOTTOM) && nb == 3 && bottom_mlp_preferred(B) &&
+                   pack_bottom(B, m->bottom, nullptr, m->bottom[0].in_features, nullptr,
+                               m->bottom[2].out_features, bp);
+  SliceParams sp;
+  if (!mc.fuse_bottom && split && !(o & DLRM_FORWARD_UNFUSED_BOTTOM) && nb == 3 &&
+      pack_slice(B, m->bottom, sp) && slice_mlp_workgroups(sp) <= kSliceMaxWorkgroups)
+    mc.bottom_slices = slice_mlp_count(sp);
+  mc.fuse_head = !(o & DLRM_FORWARD_UNFUSED_HEAD) && nt >= 2 &&
+                 m->top[nt - 1].out_features == 1 &&
+                 linear_head_supported(m->top[nt - 2].out_features, m->top[nt - 2].in_features) &&
+                 linear_head_preferred(B);
+  const bool layered_bottom = !mc.fuse_bottom && mc.bottom_slices == 0;
+  mc.split_bottom = plan_layer_splits(B, nb, m->bottom, split && layered_bottom);
+  mc.split_top = plan_layer_splits(B, nt, m->top, split && !mc.fuse_head);
+  return mc;
 }
 
 // Checks the model's shapes and computes the workspace layout for batch B.
@@ -181,15 +266,27 @@ int plan_forward(const dlrm_model *m, int32_t B, ForwardLayout &lay) {
     if (l + 1 < m->num_top) widest = widest > L.out_features ? widest : L.out_features;
   }
   if (m->top[0].in_features != m->dim + lay.P) return DLRM_ERR_SHAPE;
-  // The MLPs run layer by layer (measured inside the full forward on MI355X,
-  // the one-launch MLP chain of mlp_forward made the forward 8-11 us slower
-  // than three tiled GEMM launches for 13-512-256-64, and the 415-wide top
-  // MLP is faster as tiled GEMMs in any case).
   lay.ld_buf = round4(widest);
+  lay.mc = plan_mlps(m, B);
+  // What each of the two activation buffers holds, at B rows: the outputs
+  // (or k partials) of layers launched on their own, alternating buffers;
+  // the bottom slice launch's partials of the dense feature in buffer 0.
+  const MlpComposition &mc = lay.mc;
+  size_t need[2] = {0, 0};
+  auto use = [&](int b, int64_t parts, int64_t ld) {
+    need[b] = std::max(need[b], (size_t)parts * (size_t)B * (size_t)ld);
+  };
+  if (!mc.fuse_bottom && mc.bottom_slices == 0)
+    for (int l = 0; l + 1 < m->num_bottom; ++l) use(l & 1, mc.split_bottom[(size_t)l], lay.ld_buf);
+  if (mc.bottom_slices > 0) use(0, mc.bottom_slices, round4(m->dim));
+  // (with the head folded in, layers 0 .. nt - 3 write buffers; otherwise
+  // every layer but the last)
+  const int nbuf = mc.fuse_head ? m->num_top - 2 : m->num_top - 1;
+  for (int l = 0; l < nbuf; ++l) use(l & 1, mc.split_top[(size_t)l], lay.ld_buf);
   lay.off_R = 0;
   lay.off_buf0 = round256((size_t)B * (size_t)lay.ldR * sizeof(float));
-  lay.off_buf1 = lay.off_buf0 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
-  lay.total = lay.off_buf1 + round256((size_t)B * (size_t)lay.ld_buf * sizeof(float));
+  lay.off_buf1 = lay.off_buf0 + round256(need[0] * sizeof(float));
+  lay.total = lay.off_buf1 + round256(need[1] * sizeof(float));
   return DLRM_OK;
 }
 
@@ -238,6 +335,42 @@ int validate_forward(const dlrm_model *model, int32_t batch, const float *dense_
   return DLRM_OK;
 }
 
+// A layer's input: a plain matrix, or nred partial sums of the layer before
+// (stride floats apart) still to be added, biased and activated.
+struct MlpInput {
+  const float *p;
+  int64_t ld;
+  int nred = 1;
+  int64_t stride = 0;
+  const float *bias = nullptr;
+  int act = 0;
+};
+
+// Emits layers [0, n) of an MLP, each as its own launch: layer l stores
+// split[l] partials (or its output) in buf[l & 1], row stride ld_buf,
+// partials pstride floats apart; the last one writes `out` (row stride ldo).
+// `in` is the first layer's input on entry and the next layer's on return
+// (so a caller may run further layers).  With out == nullptr every layer
+// writes a buffer.
+int emit_layers(const Emitter &em, int B, int n, const dlrm_layer *layers,
+                const std::vector<int> &split, MlpInput &in, float *const buf[2],
+                int64_t ld_buf, int64_t pstride, float *out, int64_t ldo) {
+  for (int l = 0; l < n; ++l) {
+    const dlrm_layer &L = layers[l];
+    const bool last = out && l + 1 == n;
+    const int ns = last ? 1 : split[(size_t)l];
+    float *y = last ? out : buf[l & 1];
+    const int64_t ldy = last ? ldo : ld_buf;
+    const LinearCall c{B, L.out_features, L.in_features, in.p, in.ld, in.nred, in.stride,
+                       in.bias, in.act, L.weight, L.bias, L.act, y, ldy, ns,
+                       ns > 1 ? pstride : 0};
+    const int rc = emit(em, [=](hipStream_t s) { return launch_linear_call(c, s); });
+    if (rc) return rc;
+    in = ns > 1 ? MlpInput{y, ldy, ns, pstride, L.bias, L.act} : MlpInput{y, ldy};
+  }
+  return DLRM_OK;
+}
+
 int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                     const int32_t *const *indices, const int32_t *const *offsets,
                     const int64_t *n_idx, float *out, void *workspace, size_t workspace_bytes,
@@ -283,34 +416,40 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   float *buf[2] = {reinterpret_cast<float *>(ws + lay.off_buf0),
                    reinterpret_cast<float *>(ws + lay.off_buf1)};
 
-  // Bottom MLP: the last layer writes the dense feature straight into R[:, 0:D].
-  // A three-layer stack the fused kernel takes runs as one launch when the
-  // batch is about one 32-row band per CU.
-  const float *x = dense_in;
-  int64_t ldx = model->bottom[0].in_features;
-  BottomParams bp;
-  const bool fuse_bottom = !(model->options & DLRM_FORWARD_UNFUSED_BOTTOM) &&
-                           model->num_bottom == 3 && bottom_mlp_preferred(B) &&
-                           pack_bottom(B, model->bottom, dense_in, ldx, R, lay.ldR, bp);
-  if (fuse_bottom) {
+  // Bottom MLP.  A three-layer stack runs as one launch: at about one 32-row
+  // band per CU the fused kernel (the last layer writes the dense feature
+  // straight into R[:, 0:D]); at other batches the slice kernel, whose
+  // partials of the last layer the interaction adds as it loads the dense
+  // feature.  Otherwise layer by layer, a layer whose tiles would leave CUs
+  // idle storing k partials that the next layer adds.
+  const MlpComposition &mc = lay.mc;
+  const int64_t pstride = (int64_t)B * lay.ld_buf;  // floats between partials
+  MlpInput in{dense_in, model->bottom[0].in_features};
+  if (mc.fuse_bottom) {
+    BottomParams bp;
+    if (!pack_bottom(B, model->bottom, dense_in, in.ld, R, lay.ldR, bp))
+      return DLRM_ERR_UNSUPPORTED;
     rc = emit(em, [=](hipStream_t s) { return launch_bottom_mlp(bp, s); });
     if (rc) return rc;
-  }
-  for (int l = 0; l < model->num_bottom && !fuse_bottom; ++l) {
-    const dlrm_layer &L = model->bottom[l];
-    const bool last = l + 1 == model->num_bottom;
-    float *y = last ? R : buf[l & 1];
-    const int64_t ldy = last ? lay.ldR : lay.ld_buf;
-    rc = emit(em, [=](hipStream_t s) {
-      return launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias, L.act, y,
-                           ldy, s);
-    });
+  } else if (mc.bottom_slices > 0) {
+    SliceParams sp;
+    if (!pack_slice(B, model->bottom, sp)) return DLRM_ERR_UNSUPPORTED;
+    sp.x = dense_in;
+    sp.ldx = in.ld;
+    sp.P = buf[0];
+    sp.ldp = round4(D);
+    sp.pstride = (int64_t)B * sp.ldp;
+    rc = emit(em, [=](hipStream_t s) { return launch_slice_mlp(sp, s); });
     if (rc) return rc;
-    x = y;
-    ldx = ldy;
+  } else {
+    rc = emit_layers(em, B, model->num_bottom, model->bottom, mc.split_bottom, in, buf,
+                     lay.ld_buf, pstride, R, lay.ldR);
+    if (rc) return rc;
   }
 
-  // Gather + interaction: dense is read from R[:, 0:D], dots go to R[:, D:].
+  // Gather + interaction: the dense feature is read from R[:, 0:D] (or added
+  // up from the slice kernel's partials and written there), dots go to
+  // R[:, D:].
   gc.vec = gc.vec && lay.ldR % 4 == 0;
   InteractParams ip{};
   int threads = 0;
@@ -319,6 +458,16 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   ip.dot_off = D;
   ip.dense = R;
   ip.ld_dense = lay.ldR;
+  if (mc.bottom_slices > 0) {
+    const dlrm_layer &L2 = model->bottom[2];
+    ip.copy_dense = 1;
+    ip.dense = buf[0];
+    ip.ld_dense = round4(D);
+    ip.dense_nred = mc.bottom_slices;
+    ip.dense_stride = (int64_t)B * ip.ld_dense;
+    ip.dense_bias = L2.bias;
+    ip.dense_act = L2.act;
+  }
   ip.out = R;
   ip.ld_out = lay.ldR;
   ip.out_vec = 1;
@@ -331,35 +480,21 @@ int enqueue_forward(const dlrm_model *model, int32_t batch, const float *dense_i
   // head) is folded into the epilogue of the layer before it when that layer
   // is at most 256 wide and the batch is about one 32-row band per CU: its
   // activations are then never stored.
-  x = R;
-  ldx = lay.ldR;
   const int nt = model->num_top;
-  const bool fuse_head = !(model->options & DLRM_FORWARD_UNFUSED_HEAD) && nt >= 2 &&
-                         model->top[nt - 1].out_features == 1 &&
-                         linear_head_supported(model->top[nt - 2].out_features,
-                                               model->top[nt - 2].in_features) &&
-                         linear_head_preferred(B);
-  for (int l = 0; l < nt; ++l) {
-    const dlrm_layer &L = model->top[l];
-    if (fuse_head && l == nt - 2) {
-      const dlrm_layer &H = model->top[nt - 1];
-      return emit(em, [=](hipStream_t s) {
-        return launch_linear_head(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias,
-                                  L.act, H.weight, H.bias, H.act, out, 1, s);
-      });
-    }
-    const bool last = l + 1 == model->num_top;
-    float *y = last ? out : buf[l & 1];
-    const int64_t ldy = last ? L.out_features : lay.ld_buf;
-    rc = emit(em, [=](hipStream_t s) {
-      return launch_linear(B, L.out_features, L.in_features, x, ldx, L.weight, L.bias, L.act, y,
-                           ldy, s);
-    });
+  in = MlpInput{R, lay.ldR};
+  if (mc.fuse_head) {
+    rc = emit_layers(em, B, nt - 2, model->top, mc.split_top, in, buf, lay.ld_buf, pstride,
+                     nullptr, 0);
     if (rc) return rc;
-    x = y;
-    ldx = ldy;
+    const dlrm_layer &L = model->top[nt - 2], &H = model->top[nt - 1];
+    const MlpInput x = in;
+    return emit(em, [=](hipStream_t s) {
+      return launch_linear_head(B, L.out_features, L.in_features, x.p, x.ld, L.weight, L.bias,
+                                L.act, H.weight, H.bias, H.act, out, 1, s);
+    });
   }
-  return DLRM_OK;
+  return emit_layers(em, B, nt, model->top, mc.split_top, in, buf, lay.ld_buf, pstride, out,
+                     model->top[nt - 1].out_features);
 }
 
 // Long bags whose pooled tensor the caller also asks for: the gather as its
@@ -705,10 +840,19 @@ int dlrm_forward_noalloc(const dlrm_model *model, int32_t batch, const float *de
   ForwardLayout lay;
   rc = plan_forward(model, batch, lay);
   if (rc) return rc;
-  if (lay.total > (size_t)DLRM_NOALLOC_SCRATCH_BYTES) return DLRM_ERR_WORKSPACE;
+  // A composition whose k partials do not fit runs without k splits.
+  dlrm_model unsplit = *model;
+  unsplit.options |= DLRM_FORWARD_UNSPLIT_K;
+  const dlrm_model *use = model;
+  if (lay.total > (size_t)DLRM_NOALLOC_SCRATCH_BYTES) {
+    use = &unsplit;
+    rc = plan_forward(use, batch, lay);
+    if (rc) return rc;
+    if (lay.total > (size_t)DLRM_NOALLOC_SCRATCH_BYTES) return DLRM_ERR_WORKSPACE;
+  }
   void *ws = scratch_address(&rc);
   if (!ws) return rc;
-  return enqueue_forward(model, batch, dense_in, indices, offsets, n_idx, out, ws,
+  return enqueue_forward(use, batch, dense_in, indices, offsets, n_idx, out, ws,
                          (size_t)DLRM_NOALLOC_SCRATCH_BYTES, Emitter{(hipStream_t)stream, nullptr});
 }
 

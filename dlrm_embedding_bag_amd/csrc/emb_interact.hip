@@ -46,6 +46,29 @@ __global__ __launch_bounds__(256) void emb_bag_kernel(TableSet ts, int B, int K,
                                  out + ((int64_t)b * K + k) * D, nullptr);
 }
 
+// Feature 0 from the bottom MLP's partial sums: partial 0 (already loaded as
+// v) plus partials 1.. in order, then the bias and the activation.
+template <typename V, int VW>
+__device__ __forceinline__ V dense_reduce(const InteractParams &ip, V v, int b, int c) {
+  float x[VW];
+  const float *p = ip.dense + (int64_t)b * ip.ld_dense + c * VW;
+#pragma unroll
+  for (int e = 0; e < VW; ++e) x[e] = reinterpret_cast<const float *>(&v)[e];
+  for (int r = 1; r < ip.dense_nred; ++r) {
+    const V t = *reinterpret_cast<const V *>(p + (int64_t)r * ip.dense_stride);
+#pragma unroll
+    for (int e = 0; e < VW; ++e) x[e] += reinterpret_cast<const float *>(&t)[e];
+  }
+#pragma unroll
+  for (int e = 0; e < VW; ++e) {
+    float y = x[e] + (ip.dense_bias ? ip.dense_bias[c * VW + e] : 0.0f);
+    if (ip.dense_act == 1) y = y > 0.0f ? y : 0.0f;
+    else if (ip.dense_act == 2) y = 1.0f / (1.0f + expf(-y));
+    reinterpret_cast<float *>(&v)[e] = y;
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Interaction (and fused gather + interaction): one workgroup per S samples.
 // MODE_FUSED pools the bags into the LDS tile; MODE_LOAD reads a (B, K, D)
@@ -63,12 +86,15 @@ __global__ __launch_bounds__(1024) void interact_kernel(TableSet ts, InteractPar
   const int nthreads = blockDim.x;
 
   // Phase 1a: dense rows -> feature 0 of each sample (and the output copy).
+  // With partial sums of the bottom MLP's last layer, they are added in
+  // order, then that layer's bias and activation.
   for (int t = threadIdx.x; t < S * nvec; t += nthreads) {
     const int s = t / nvec;
     const int c = t - s * nvec;
     const int b = b0 + s;
     if (b >= B) continue;
-    const V v = reinterpret_cast<const V *>(ip.dense + (int64_t)b * ip.ld_dense)[c];
+    V v = reinterpret_cast<const V *>(ip.dense + (int64_t)b * ip.ld_dense)[c];
+    if (ip.dense_nred > 0) v = dense_reduce<V, VW>(ip, v, b, c);
     reinterpret_cast<V *>(X + (size_t)(s * FR) * DP)[c] = v;
     if (ip.copy_dense) {
       float *o = ip.out + (int64_t)b * ip.ld_out;

@@ -26,6 +26,14 @@ struct InteractParams {
   int64_t ld_out;
   float *emb_out;        // optional (B, K, D) copy of the pooled vectors
   const float *emb_in;   // (B, K, D) input of the interaction-only kernel
+  // dense_nred >= 1: dense holds dense_nred partial sums of the bottom MLP's
+  // last layer (its pre-activation when there is one), dense_stride floats
+  // apart, and feature 0 is dense_act(dense_bias + (P_0 + P_1 + ...))
+  // (dense_bias may be null); 0: dense is feature 0.
+  int dense_nred;
+  int64_t dense_stride;
+  const float *dense_bias;
+  int dense_act;
 };
 
 // How a gather reads its bags: table storage type, vector (16-byte chunk) or
@@ -119,6 +127,36 @@ hipError_t launch_linear_split(int M, int N, int K_lo, const float *A_lo, int64_
                                const float *bias, int act, float *C, int64_t ldc,
                                hipStream_t stream);
 
+// One layer with the k split across workgroups and the split's partial sums
+// reduced by the next layer (linear.hip).  A is either a plain (M, K) matrix
+// (a_nred <= 1) or a_nred partial sums of the layer before, a_stride floats
+// apart, read as a_act(a_bias[k] + (P_0 + P_1 + ...)[m][k]) (a_bias may be
+// null).  With nsplit >= 2 the layer stores nsplit raw partial sums (no bias,
+// no activation: its reader applies them) at C + s c_stride, else
+// C = act(A W^T + bias).
+struct LinearCall {
+  int M, N, K;
+  const float *A;
+  int64_t lda;
+  int a_nred;
+  int64_t a_stride;
+  const float *a_bias;
+  int a_act;
+  const float *W;
+  const float *bias;
+  int act;
+  float *C;
+  int64_t ldc;
+  int nsplit;
+  int64_t c_stride;
+};
+hipError_t launch_linear_call(const LinearCall &c, hipStream_t stream);
+// How many partial sums an M x N x K layer is split into so that its tiles
+// fill the chip (a power of two up to 8; 1 = not split).
+int linear_split_count(int M, int N, int K);
+// Whether an M x N x K layer with weights W can read its A as nred partials.
+bool linear_reduce_supported(int M, int N, int K, const float *W, int nred);
+
 // The three-layer bottom MLP in one launch (bottom_mlp.hip):
 // y = act2(act1(act0(x W0^T + b0) W1^T + b1) W2^T + b2), hidden layers on chip.
 struct BottomParams {
@@ -138,6 +176,28 @@ bool bottom_mlp_supported(const BottomParams &p);
 // grid is M / 32 bands, one per CU at a time).
 bool bottom_mlp_preferred(int M);
 hipError_t launch_bottom_mlp(const BottomParams &p, hipStream_t stream);
+
+// The three-layer bottom MLP in one launch cut by h1's columns into 64-wide
+// slices (slice_mlp.hip): workgroup (16-row band, slice s) stores
+// P_s = act1(act0(x W0^T + b0) W1[slice]^T + b1[slice]) W2[:, slice]^T, and
+// the N1 / 64 partials summed in slice order are y's pre-activation (b2 and
+// act2 are the reader's).
+struct SliceParams {
+  int M, K0, N0, N1, N2;
+  const float *x;  // (M, K0), row stride ldx
+  int64_t ldx;
+  const float *W0, *b0, *W1, *b1, *W2;  // (N_l, K_l) dense; biases (N_l,) or nullptr
+  int act0, act1;
+  float *P;        // partial s at P + s pstride, row stride ldp
+  int64_t ldp, pstride;
+};
+int slice_mlp_count(const SliceParams &p);         // partials written (N1 / 64)
+int64_t slice_mlp_workgroups(const SliceParams &p);
+// True for 1 <= K0 <= 15, N0 a multiple of 64 up to 512, N1 a multiple of 64,
+// N2 a multiple of 16 up to 256, P 16-byte aligned with ldp, pstride
+// multiples of 4.
+bool slice_mlp_supported(const SliceParams &p);
+hipError_t launch_slice_mlp(const SliceParams &p, hipStream_t stream);
 
 // Two layers in one launch: h = act(A W^T + bias) (N <= 256 columns, never
 // stored) followed by a one-output head, out[m] = head_act(head_bias +

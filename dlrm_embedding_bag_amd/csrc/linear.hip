@@ -68,6 +68,13 @@ struct ASrc {
   const float *hi;
   int64_t ld_hi;
   int k_lo;
+  // The reducing instantiations (NRED > 1) read A as the NRED partial sums
+  // of the layer before, red_stride floats apart from lo on: A[m][k] =
+  // red_act(red_bias[k] + ((P_0[m][k] + P_1[m][k]) + ...)), red_bias may be
+  // null.
+  int64_t red_stride = 0;
+  const float *red_bias = nullptr;
+  int red_act = 0;
 };
 
 // Four floats at a 4-byte-aligned address: global memory takes a 16-byte
@@ -121,6 +128,66 @@ __device__ __forceinline__ float4 load_a_full(const ASrc &a, int row, int k) {
   }
 }
 
+// Branch-free activation (both forms computed, one selected): inside the k
+// loop a branch would make the compiler's wait-count pass drain the
+// outstanding prefetch loads where the paths join.
+__device__ __forceinline__ float act_select(float x, int act) {
+  const float r = (act == 1 && !(x > 0.0f)) ? 0.0f : x;
+  const float sg = 1.0f / (1.0f + expf(-x));
+  return act == 2 ? sg : r;
+}
+
+// Columns k..k+3 of row `row` of a reduced source, inside its K: the NRED
+// partials' float4s (16-byte aligned) are all loaded before any is added,
+// then added in partial order; the bias (one dword-aligned 16-byte load
+// from a valid address whether or not there is a bias) and the activation
+// follow.
+template <int NRED>
+__device__ __forceinline__ float4 load_red_full(const ASrc &a, int row, int k) {
+  const float *p = a.lo + (int64_t)row * a.ld_lo + k;
+  float4 t[NRED];
+#pragma unroll
+  for (int s = 0; s < NRED; ++s)
+    t[s] = *reinterpret_cast<const float4 *>(p + (int64_t)s * a.red_stride);
+  const float4_a4 b = *reinterpret_cast<const float4_a4 *>(a.red_bias ? a.red_bias + k : p);
+  float v[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
+#pragma unroll
+  for (int s = 1; s < NRED; ++s) {
+    v[0] += t[s].x;
+    v[1] += t[s].y;
+    v[2] += t[s].z;
+    v[3] += t[s].w;
+  }
+  const bool hb = a.red_bias != nullptr;
+  return make_float4(act_select(v[0] + (hb ? b.x : 0.0f), a.red_act),
+                     act_select(v[1] + (hb ? b.y : 0.0f), a.red_act),
+                     act_select(v[2] + (hb ? b.z : 0.0f), a.red_act),
+                     act_select(v[3] + (hb ? b.w : 0.0f), a.red_act));
+}
+
+// The same for the last, partial slab: columns at or past K read as zero
+// (clamped addresses, every load inside the row).
+template <int NRED>
+__device__ __forceinline__ float4 load_red_tail(const ASrc &a, int row, int k, int K) {
+  const float *p = a.lo + (int64_t)row * a.ld_lo;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int kk = min(k + e, K - 1);
+    float t[NRED];
+#pragma unroll
+    for (int s = 0; s < NRED; ++s) t[s] = p[(int64_t)s * a.red_stride + kk];
+    const float bl = *(a.red_bias ? a.red_bias + kk : p + kk);
+    const float b = a.red_bias ? bl : 0.0f;
+    float x = t[0];
+#pragma unroll
+    for (int s = 1; s < NRED; ++s) x += t[s];
+    x = act_select(x + b, a.red_act);
+    v[e] = k + e < K ? x : 0.0f;
+  }
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 template <bool SPLIT>
 __device__ __forceinline__ float4 load_a_tail(const ASrc &a, int row, int k, int K) {
   if constexpr (!SPLIT) {
@@ -149,16 +216,27 @@ struct HeadArgs {
   int64_t ldo;
 };
 
+// k split across workgroups: workgroup (tile, s) multiplies k in
+// [s kc, s kc + kc) and stores its raw partial sums (the launcher passes no
+// bias and no activation) to C + s c_stride.  kc = 0: one workgroup per tile.
+struct KSplitArgs {
+  int kc;
+  int tiles;
+  int64_t c_stride;
+};
+
 template <int BM, int BN, int GM, int GN, int KS, bool VA, bool VW, bool VC, bool SPLIT,
-          bool HEAD = false>
-__global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, int K,
-                                                                 const ASrc A,
-                                                                 const float *__restrict__ W,
+          bool HEAD = false, int NRED = 1>
+__global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, int Kfull,
+                                                                 const ASrc Afull,
+                                                                 const float *__restrict__ Wfull,
                                                                  const float *__restrict__ bias,
-                                                                 int act, float *__restrict__ C,
+                                                                 int act, float *__restrict__ Cs,
                                                                  int64_t ldc, int tiles_n,
                                                                  int xcd_chunk,
-                                                                 const HeadArgs head) {
+                                                                 const HeadArgs head,
+                                                                 const KSplitArgs ks) {
+  static_assert(NRED == 1 || (VA && !SPLIT && !HEAD), "a reduced A is aligned and unsplit");
   // KS wave groups split k: a staged slab holds KS x kBK columns and group g
   // multiplies columns [g kBK, (g + 1) kBK) of it; the groups' partial tiles
   // are added in group order through LDS at the end.
@@ -183,6 +261,23 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
   // give XCD x the contiguous m-major tile range [x*chunk, (x+1)*chunk).
   int bid = blockIdx.x;
   if (xcd_chunk > 0) bid = (bid & 7) * xcd_chunk + (bid >> 3);
+  // With a k split, the workgroup's k range: A's columns and W's columns
+  // from k0 on, K of them (every range holds at least one column).
+  int K = Kfull;
+  ASrc A = Afull;
+  const float *W = Wfull;
+  float *C = Cs;
+  if (ks.kc > 0) {
+    const int s = bid / ks.tiles;
+    bid -= s * ks.tiles;
+    const int k0 = s * ks.kc;
+    K = min(ks.kc, Kfull - k0);
+    A.lo += k0;
+    if (A.red_bias) A.red_bias += k0;
+    W += k0;
+    C += s * ks.c_stride;
+  }
+  const int64_t ldw = Kfull;
   const int tm_blk = bid / tiles_n;
   const int tn_blk = bid - tm_blk * tiles_n;
   const int m0 = tm_blk * BM, n0 = tn_blk * BN;
@@ -223,14 +318,24 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
     const int kb = sl * SK;
     if (sl < nfull) {
 #pragma unroll
-      for (int i = 0; i < A_V4; ++i) ra[i] = load_a_full<SPLIT, VA>(A, arow[i], kb + acol[i]);
+      for (int i = 0; i < A_V4; ++i) {
+        if constexpr (NRED > 1)
+          ra[i] = load_red_full<NRED>(A, arow[i], kb + acol[i]);
+        else
+          ra[i] = load_a_full<SPLIT, VA>(A, arow[i], kb + acol[i]);
+      }
 #pragma unroll
-      for (int i = 0; i < W_V4; ++i) rw[i] = load_full<VW>(W, K, wrow[i], kb + wcol[i]);
+      for (int i = 0; i < W_V4; ++i) rw[i] = load_full<VW>(W, ldw, wrow[i], kb + wcol[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < A_V4; ++i) ra[i] = load_a_tail<SPLIT>(A, arow[i], kb + acol[i], K);
+      for (int i = 0; i < A_V4; ++i) {
+        if constexpr (NRED > 1)
+          ra[i] = load_red_tail<NRED>(A, arow[i], kb + acol[i], K);
+        else
+          ra[i] = load_a_tail<SPLIT>(A, arow[i], kb + acol[i], K);
+      }
 #pragma unroll
-      for (int i = 0; i < W_V4; ++i) rw[i] = load_tail(W, K, wrow[i], kb + wcol[i], K);
+      for (int i = 0; i < W_V4; ++i) rw[i] = load_tail(W, ldw, wrow[i], kb + wcol[i], K);
     }
   };
   auto stash = [&](int buf, const float4 (&ra)[A_V4], const float4 (&rw)[W_V4]) {
@@ -453,12 +558,15 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
   }
 }
 
-// N <= 8: each wave computes 4 rows at a time, 16 lanes per row.
-template <bool VEC, bool SPLIT>
+// N <= 8: each wave computes 4 rows at a time, 16 lanes per row.  With
+// NRED > 1, A is reduced from the partial sums of the layer before (vector
+// path only).
+template <bool VEC, bool SPLIT, int NRED = 1>
 __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K, const ASrc A,
                                                    const float *__restrict__ W,
                                                    const float *__restrict__ bias, int act,
                                                    float *__restrict__ C, int64_t ldc) {
+  static_assert(NRED == 1 || (VEC && !SPLIT), "a reduced A is aligned and unsplit");
   const int lane = threadIdx.x & 63;
   const int row_in_wave = lane >> 4;
   const int c = lane & 15;
@@ -471,7 +579,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K, const AS
   for (int n = 0; n < N; ++n) {
     const float *w = W + (int64_t)n * K;
     float acc = 0.0f;
-    if (VEC) {
+    if (NRED > 1) {
+      for (int k = 4 * c; k < K; k += 64)
+        acc = vdot_acc(load_red_full<NRED>(A, mr, k), *reinterpret_cast<const float4 *>(w + k),
+                       acc);
+    } else if (VEC) {
       for (int k = 4 * c; k < K; k += 64) {
         const float *src = (SPLIT && k >= A.k_lo) ? ah : a;
         const float4 x = *reinterpret_cast<const float4 *>(src + k);
@@ -572,30 +684,123 @@ __global__ __launch_bounds__(256) void thin_k_kernel(int M, int N, const ASrc A,
 }
 
 template <int BM, int BN, int GM, int GN, bool SPLIT, int KS = 1>
-hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, const float *W, const float *bias,
-                           int act, float *C, int64_t ldc, bool va, bool vw, bool vc,
-                           hipStream_t stream) {
+hipError_t launch_gemm_cfg(int M, int N, int K, const ASrc &A, int nred, const float *W,
+                           const float *bias, int act, float *C, int64_t ldc, bool va, bool vw,
+                           bool vc, int kc, int64_t c_stride, hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  const int xcd_chunk = (tiles % 8 == 0) ? (int)(tiles / 8) : 0;
-  dim3 grid((unsigned)tiles), block(64 * GM * GN * KS);
-#define DLRM_GEMM_LAUNCH(A_, W_, C_)                                                          \
-  launch_kernel((gemm_kernel<BM, BN, GM, GN, KS, A_, W_, C_, SPLIT>), grid, block, 0, stream, \
-                M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk, HeadArgs{})
-  if (va && vw && vc)
-    DLRM_GEMM_LAUNCH(true, true, true);
+  const int64_t splits = kc > 0 ? (K + kc - 1) / kc : 1;
+  const int64_t wgs = tiles * splits;
+  const int xcd_chunk = (wgs % 8 == 0) ? (int)(wgs / 8) : 0;
+  const KSplitArgs ks{kc, (int)tiles, c_stride};
+  dim3 grid((unsigned)wgs), block(64 * GM * GN * KS);
+#define DLRM_GEMM_LAUNCH(A_, W_, C_, R_)                                                    \
+  launch_kernel((gemm_kernel<BM, BN, GM, GN, KS, A_, W_, C_, SPLIT, false, R_>), grid, block, \
+                0, stream, M, N, K, A, W, bias, act, C, ldc, tiles_n, xcd_chunk, HeadArgs{}, ks)
+  if (nred > 1) {
+    // reduced sources exist for aligned A and W, and for the tiles a K of at
+    // least 128 selects (the launcher checked both)
+    if constexpr (!SPLIT && (KS > 1 || BM == 128)) {
+      if (vc) {
+        if (nred == 2) DLRM_GEMM_LAUNCH(true, true, true, 2);
+        else if (nred == 4) DLRM_GEMM_LAUNCH(true, true, true, 4);
+        else DLRM_GEMM_LAUNCH(true, true, true, 8);
+      } else {
+        if (nred == 2) DLRM_GEMM_LAUNCH(true, true, false, 2);
+        else if (nred == 4) DLRM_GEMM_LAUNCH(true, true, false, 4);
+        else DLRM_GEMM_LAUNCH(true, true, false, 8);
+      }
+    }
+  } else if (va && vw && vc)
+    DLRM_GEMM_LAUNCH(true, true, true, 1);
   else if (va && !vw && vc)
-    DLRM_GEMM_LAUNCH(true, false, true);
+    DLRM_GEMM_LAUNCH(true, false, true, 1);
   else if (!va && vw && vc)
-    DLRM_GEMM_LAUNCH(false, true, true);
+    DLRM_GEMM_LAUNCH(false, true, true, 1);
   else if (!va && !vw && vc)
-    DLRM_GEMM_LAUNCH(false, false, true);
+    DLRM_GEMM_LAUNCH(false, false, true, 1);
   else if (va && vw)
-    DLRM_GEMM_LAUNCH(true, true, false);
+    DLRM_GEMM_LAUNCH(true, true, false, 1);
   else
-    DLRM_GEMM_LAUNCH(false, false, false);
+    DLRM_GEMM_LAUNCH(false, false, false, 1);
 #undef DLRM_GEMM_LAUNCH
   return hipGetLastError();
+}
+
+// The tile launch_linear takes for an M x N x K layer (N > 8, K > 16): the
+// largest tile that still gives every CU a workgroup.  128 x 128 tiles on 8
+// waves (two per SIMD) when there are enough of them for every CU, else
+// 128 x 64 on 8 waves of 32 x 32, else 64 x 64, else 64 x 32 on 4 waves.
+// (At 8192 x 256 x 512, 128 x 64 on 8 waves: 24.5 us, 64 x 64 on 4 waves:
+// 26.6 us, the same sums bit for bit.)  The 64-row tiles leave one wave per
+// SIMD: with K of at least two staged slabs, kKSplit wave groups split each
+// tile's k (kKSplit times the waves, 1/kKSplit of the MFMA chain and of the
+// slab round trips).
+enum class GemmCfg { T128x128, T128x64, T64x64, T64x64KS, T64x32, T64x32KS };
+
+// Across-workgroup k splits: at most kMaxSplit partials, enough to give about
+// kSplitFill workgroups (one per CU).
+constexpr int kMaxSplit = 8;
+constexpr int kSplitFill = 256;
+
+// k columns per partial when K is cut into s partials of whole slabs of sk.
+int split_width(int K, int s, int sk) {
+  const int per = (K + s - 1) / s;
+  return (per + sk - 1) / sk * sk;
+}
+
+int64_t gemm_tiles(int M, int N, int bm, int bn) {
+  return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
+GemmCfg gemm_cfg(int M, int N, int K) {
+  if (gemm_tiles(M, N, 128, 128) >= 256) return GemmCfg::T128x128;
+  if (gemm_tiles(M, N, 128, 64) >= 256) return GemmCfg::T128x64;
+  const bool ksplit = kKSplit > 1 && K >= 2 * kBK * kKSplit;
+  if (gemm_tiles(M, N, 64, 64) >= 256) return ksplit ? GemmCfg::T64x64KS : GemmCfg::T64x64;
+  return ksplit ? GemmCfg::T64x32KS : GemmCfg::T64x32;
+}
+
+int64_t cfg_tiles(GemmCfg c, int M, int N) {
+  switch (c) {
+    case GemmCfg::T128x128: return gemm_tiles(M, N, 128, 128);
+    case GemmCfg::T128x64: return gemm_tiles(M, N, 128, 64);
+    case GemmCfg::T64x64:
+    case GemmCfg::T64x64KS: return gemm_tiles(M, N, 64, 64);
+    default: return gemm_tiles(M, N, 64, 32);
+  }
+}
+
+// k per staged slab of the tile: the unit a k split is cut in.
+int cfg_slab_k(GemmCfg c) {
+  return (c == GemmCfg::T64x64KS || c == GemmCfg::T64x32KS) ? kBK * kKSplit : kBK;
+}
+
+hipError_t launch_gemm(GemmCfg cfg, int M, int N, int K, const ASrc &A, int nred,
+                       const float *W, const float *bias, int act, float *C, int64_t ldc,
+                       bool va, bool vw, bool vc, int kc, int64_t c_stride,
+                       hipStream_t stream) {
+  constexpr int KS = kKSplit;
+  switch (cfg) {
+    case GemmCfg::T128x128:
+      return launch_gemm_cfg<128, 128, 2, 4, false>(M, N, K, A, nred, W, bias, act, C, ldc, va,
+                                                    vw, vc, kc, c_stride, stream);
+    case GemmCfg::T128x64:
+      return launch_gemm_cfg<128, 64, 4, 2, false>(M, N, K, A, nred, W, bias, act, C, ldc, va,
+                                                   vw, vc, kc, c_stride, stream);
+    case GemmCfg::T64x64KS:
+      return launch_gemm_cfg<64, 64, 2, 2, false, KS>(M, N, K, A, nred, W, bias, act, C, ldc,
+                                                      va, vw, vc, kc, c_stride, stream);
+    case GemmCfg::T64x64:
+      return launch_gemm_cfg<64, 64, 2, 2, false>(M, N, K, A, nred, W, bias, act, C, ldc, va,
+                                                  vw, vc, kc, c_stride, stream);
+    case GemmCfg::T64x32KS:
+      return launch_gemm_cfg<64, 32, 2, 2, false, KS>(M, N, K, A, nred, W, bias, act, C, ldc,
+                                                      va, vw, vc, kc, c_stride, stream);
+    default:
+      return launch_gemm_cfg<64, 32, 2, 2, false>(M, N, K, A, nred, W, bias, act, C, ldc, va,
+                                                  vw, vc, kc, c_stride, stream);
+  }
 }
 
 template <bool SPLIT>
@@ -658,35 +863,34 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
       default: break;
     }
   }
-  // Tile shape: the largest tile that still gives every CU a workgroup.
-  auto tiles = [&](int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  // 128 x 128 tiles on 8 waves (two per SIMD) when there are enough of them
-  // for every CU, else 128 x 64 on 8 waves of 32 x 32, else 64 x 64, else
-  // 64 x 32 on 4 waves.  (At 8192 x 256 x 512, 128 x 64 on 8 waves: 24.5 us,
-  // 64 x 64 on 4 waves: 26.6 us, the same sums bit for bit.)
-  if (tiles(128, 128) >= 256)
-    return launch_gemm_cfg<128, 128, 2, 4, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                  stream);
-  if (tiles(128, 64) >= 256)
-    return launch_gemm_cfg<128, 64, 4, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                 stream);
-  // The 64-row tiles leave one wave per SIMD: with K of at least two staged
-  // slabs, KS wave groups split each tile's k (KS times the waves, 1/KS of
-  // the MFMA chain and of the slab round trips).
-  constexpr int KS = kKSplit;
-  const bool ksplit = KS > 1 && K >= 2 * kBK * KS;
-  if (tiles(64, 64) >= 256) {
-    if (ksplit)
-      return launch_gemm_cfg<64, 64, 2, 2, SPLIT, KS>(M, N, K, A, W, bias, act, C, ldc, va, vw,
-                                                      vc, stream);
-    return launch_gemm_cfg<64, 64, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                stream);
+  if constexpr (SPLIT) {
+    // the two-part A source keeps the tile rules of the plain one
+    const GemmCfg cfg = gemm_cfg(M, N, K);
+    constexpr int KS = kKSplit;
+    switch (cfg) {
+      case GemmCfg::T128x128:
+        return launch_gemm_cfg<128, 128, 2, 4, true>(M, N, K, A, 1, W, bias, act, C, ldc, va,
+                                                     vw, vc, 0, 0, stream);
+      case GemmCfg::T128x64:
+        return launch_gemm_cfg<128, 64, 4, 2, true>(M, N, K, A, 1, W, bias, act, C, ldc, va, vw,
+                                                    vc, 0, 0, stream);
+      case GemmCfg::T64x64KS:
+        return launch_gemm_cfg<64, 64, 2, 2, true, KS>(M, N, K, A, 1, W, bias, act, C, ldc, va,
+                                                       vw, vc, 0, 0, stream);
+      case GemmCfg::T64x64:
+        return launch_gemm_cfg<64, 64, 2, 2, true>(M, N, K, A, 1, W, bias, act, C, ldc, va, vw,
+                                                   vc, 0, 0, stream);
+      case GemmCfg::T64x32KS:
+        return launch_gemm_cfg<64, 32, 2, 2, true, KS>(M, N, K, A, 1, W, bias, act, C, ldc, va,
+                                                       vw, vc, 0, 0, stream);
+      default:
+        return launch_gemm_cfg<64, 32, 2, 2, true>(M, N, K, A, 1, W, bias, act, C, ldc, va, vw,
+                                                   vc, 0, 0, stream);
+    }
+  } else {
+    return launch_gemm(gemm_cfg(M, N, K), M, N, K, A, 1, W, bias, act, C, ldc, va, vw, vc, 0, 0,
+                       stream);
   }
-  if (ksplit)
-    return launch_gemm_cfg<64, 32, 2, 2, SPLIT, KS>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                                    stream);
-  return launch_gemm_cfg<64, 32, 2, 2, SPLIT>(M, N, K, A, W, bias, act, C, ldc, va, vw, vc,
-                                              stream);
 }
 
 }  // namespace
@@ -696,6 +900,78 @@ hipError_t launch_linear(int M, int N, int K, const float *A, int64_t lda, const
   const ASrc src{A, lda, nullptr, 0, K};
   const bool va = aligned16(A) && lda % 4 == 0;
   return launch_linear_src<false>(M, N, K, src, va, W, bias, act, C, ldc, stream);
+}
+
+// The fewest k partials (a power of two, at most kMaxSplit) that give the
+// layer's tiles about one workgroup per CU, each partial a whole number of
+// staged slabs and none empty; 1 when the tiles already fill the chip or the
+// layer does not take a GEMM tile.
+int linear_split_count(int M, int N, int K) {
+  if (M < 1 || N <= 8 || K <= kThinMaxK) return 1;
+  const GemmCfg cfg = gemm_cfg(M, N, K);
+  const int64_t tiles = cfg_tiles(cfg, M, N);
+  const int sk = cfg_slab_k(cfg);
+  int s = 1;
+  while (s < kMaxSplit && tiles * s < kSplitFill) s *= 2;
+  while (s > 1) {
+    const int kc = split_width(K, s, sk);
+    if ((K + kc - 1) / kc == s) break;
+    s /= 2;
+  }
+  return s;
+}
+
+bool linear_reduce_supported(int M, int N, int K, const float *W, int nred) {
+  if (nred != 2 && nred != 4 && nred != 8) return false;
+  if (!aligned16(W) || K % 4 != 0) return false;
+  if (N <= 8) return true;  // the vector matrix-vector kernel
+  if (K < 2 * kBK * kKSplit) return false;  // tiles with reduced-source instantiations
+  // (64 x 64 tiles reading 8 partials would spill registers)
+  return !(nred == 8 && gemm_cfg(M, N, K) == GemmCfg::T64x64KS);
+}
+
+hipError_t launch_linear_call(const LinearCall &c, hipStream_t stream) {
+  const int M = c.M, N = c.N, K = c.K;
+  if (c.a_nred <= 1 && c.nsplit <= 1)
+    return launch_linear(M, N, K, c.A, c.lda, c.W, c.bias, c.act, c.C, c.ldc, stream);
+  ASrc src{c.A, c.lda, nullptr, 0, K};
+  const bool red = c.a_nred > 1;
+  if (red) {
+    if (!linear_reduce_supported(M, N, K, c.W, c.a_nred) || !aligned16(c.A) || c.lda % 4 != 0 ||
+        c.a_stride % 4 != 0)
+      return hipErrorInvalidValue;
+    src.red_stride = c.a_stride;
+    src.red_bias = c.a_bias;
+    src.red_act = c.a_act;
+  }
+  const bool va = aligned16(c.A) && c.lda % 4 == 0;
+  const bool vw = aligned16(c.W) && K % 4 == 0;
+  const bool vc = aligned16(c.C) && c.ldc % 4 == 0;
+  if (N <= 8) {
+    if (c.nsplit > 1) return hipErrorInvalidValue;
+    const int rows_per_block = 16;
+    dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(256);
+    if (c.a_nred == 2)
+      launch_kernel((gemv_kernel<true, false, 2>), grid, block, 0, stream, M, N, K, src, c.W,
+                    c.bias, c.act, c.C, c.ldc);
+    else if (c.a_nred == 4)
+      launch_kernel((gemv_kernel<true, false, 4>), grid, block, 0, stream, M, N, K, src, c.W,
+                    c.bias, c.act, c.C, c.ldc);
+    else
+      launch_kernel((gemv_kernel<true, false, 8>), grid, block, 0, stream, M, N, K, src, c.W,
+                    c.bias, c.act, c.C, c.ldc);
+    return hipGetLastError();
+  }
+  if (K <= kThinMaxK) return hipErrorInvalidValue;
+  const GemmCfg cfg = gemm_cfg(M, N, K);
+  int kc = 0;
+  if (c.nsplit > 1) {
+    kc = split_width(K, c.nsplit, cfg_slab_k(cfg));
+    if ((K + kc - 1) / kc != c.nsplit || !vc) return hipErrorInvalidValue;
+  }
+  return launch_gemm(cfg, M, N, K, src, red ? c.a_nred : 1, c.W, c.nsplit > 1 ? nullptr : c.bias,
+                     c.nsplit > 1 ? 0 : c.act, c.C, c.ldc, va, vw, vc, kc,
+                     c.nsplit > 1 ? c.c_stride : 0, stream);
 }
 
 hipError_t launch_linear_split(int M, int N, int K_lo, const float *A_lo, int64_t lda_lo,
@@ -739,7 +1015,7 @@ hipError_t launch_linear_head(int M, int N, int K, const float *A, int64_t lda, 
 #define DLRM_HEAD_LAUNCH(A_, W_)                                                              \
   launch_kernel((gemm_kernel<kHeadBM, kHeadBN, 1, 4, kHeadKS, A_, W_, false, false, true>), grid, \
                 block, 0, stream, M, N, K, src, W, bias, act, nullptr, (int64_t)0, 1, xcd_chunk,  \
-                head)
+                head, KSplitArgs{0, 0, 0})
   if (va && vw)
     DLRM_HEAD_LAUNCH(true, true);
   else if (va)

@@ -406,6 +406,7 @@ DLRM_API int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers
 #define DLRM_FORWARD_LAYERED 1u  /* never the one-launch small-model kernel   */
 #define DLRM_FORWARD_UNFUSED_HEAD 2u /* the last top layer as its own launch  */
 #define DLRM_FORWARD_UNFUSED_BOTTOM 4u /* each bottom layer as its own launch */
+#define DLRM_FORWARD_UNSPLIT_K 8u /* no layer's k split across workgroups     */
 
 /* A DLRMv1 model: bottom MLP, K embedding tables, top MLP.  All arrays of
  * this struct are [host]; the weights and tables they point to are device

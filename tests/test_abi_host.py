@@ -231,12 +231,22 @@ def test_forward_workspace_and_errors(lib):
                   [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D)
     B = 8192
     ws = lib.dlrm_forward_workspace_bytes(ctypes.byref(good), B)
-    # both MLPs run layer by layer: R (B x 416 floats) + two ping-pong
-    # buffers as wide as the widest hidden layer (B x 512)
-    assert ws == B * 416 * 4 + 2 * B * 512 * 4
+    # at 8192 samples the bottom MLP is one launch and the head is folded into
+    # top layer 1: R (B x 416 floats) + one buffer for top layer 0's output
+    # (B x 512)
+    assert ws == B * 416 * 4 + B * 512 * 4
+    # layer by layer (no fused or slice launches, no k partials): R + two
+    # ping-pong buffers (B x 512)
+    layered = _model([(13, 512, 1), (512, 256, 1), (256, 64, 1)],
+                     [(D + P, 512, 1), (512, 256, 1), (256, 1, 2)], K, D,
+                     options=abi.forward_options(("unfused_head", "unfused_bottom",
+                                                  "unsplit_k")))
+    assert (lib.dlrm_forward_workspace_bytes(ctypes.byref(layered), B)
+            == B * 416 * 4 + 2 * B * 512 * 4)
     odd = _model([(13, 96, 1), (96, 64, 1)], [(D + P, 96, 1), (96, 1, 2)], K, D)
-    # other widths: R + two ping-pong buffers (B x 96)
-    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(odd), B) == B * 416 * 4 + 2 * B * 96 * 4
+    # other widths: R + the bottom MLP's hidden layer (B x 96); the head is
+    # folded into top layer 0
+    assert lib.dlrm_forward_workspace_bytes(ctypes.byref(odd), B) == B * 416 * 4 + B * 96 * 4
     bad_chain = _model([(13, 512, 1), (500, 64, 1)], [(D + P, 1, 2)], K, D)
     assert lib.dlrm_forward_workspace_bytes(ctypes.byref(bad_chain), B) == 0
     bad_dim = _model([(13, 32, 1)], [(D + P, 1, 2)], K, D)       # bottom out != D
@@ -257,7 +267,9 @@ def test_forward_workspace_and_errors(lib):
 
 def test_forward_options_are_validated(lib):
     """dlrm_model.options: the documented bits are accepted (they change the
-    composition, not the workspace), any other bit is DLRM_ERR_SHAPE."""
+    composition, and with it the workspace: with DLRM_FORWARD_UNSPLIT_K it
+    holds no partial sums, so at 256 samples it is smaller), any other bit
+    is DLRM_ERR_SHAPE."""
     K, D = 26, 64
     P = 27 * 26 // 2
     spec = ([(13, 512, 1), (512, 256, 1), (256, 64, 1)],
@@ -268,9 +280,14 @@ def test_forward_options_are_validated(lib):
     every = 0
     for v in abi.FORWARD_OPTIONS.values():
         every |= v
+    unsplit = abi.FORWARD_OPTIONS["unsplit_k"]
+    plain = lib.dlrm_forward_workspace_bytes(ctypes.byref(_model(*spec, K, D, options=unsplit)),
+                                             B)
+    assert 0 < plain < base, "at 256 samples the default composition stores k partials"
     for bits in list(abi.FORWARD_OPTIONS.values()) + [every]:
         m = _model(*spec, K, D, options=bits)
-        assert lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B) == base
+        ws = lib.dlrm_forward_workspace_bytes(ctypes.byref(m), B)
+        assert ws == plain if bits & unsplit else ws > 0, bits
     idx = (ctypes.c_void_p * K)(*[FAKE] * K)
     for bits in (every + 1, 1 << 31, 0xFFFFFFFF):
         m = _model(*spec, K, D, options=bits)

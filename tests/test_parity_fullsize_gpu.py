@@ -141,11 +141,13 @@ def _mlp(x, layers, chain):
 
 
 def test_full_forward_matches_its_parts():
-    """dlrm_forward with its head as its own launch equals its parts called
-    one by one, bit for bit: both MLPs layer by layer through linear_bias_act
-    around dlrm_emb_interact.  The default forward (head folded into the
-    layer before it) and the same forward with the MLPs as mlp_forward chains
-    agree within the float tolerance."""
+    """dlrm_forward with its head as its own launch and no layer's k split
+    across workgroups equals its parts called one by one, bit for bit: both
+    MLPs layer by layer through linear_bias_act around dlrm_emb_interact.
+    The default forward (at this batch: the bottom MLP's first two layers as
+    one launch storing k partials, the top layers split over k) and the same
+    forward with the MLPs as mlp_forward chains agree within the float
+    tolerance."""
     w = inputs.Workload("fwd-parts", batch=1000, num_tables=26, rows=20000, dim=64, bag=20,
                         dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1))
     import torch
@@ -155,7 +157,7 @@ def test_full_forward_matches_its_parts():
     bottom, top = inputs.dlrm_layers(w, bias_std=0.1)
     bl = [(dev(a), dev(b), act) for a, b, act in bottom]
     tl = [(dev(a), dev(b), act) for a, b, act in top]
-    model = abi.DlrmModel(bl, tl, tables, options=("unfused_head",))
+    model = abi.DlrmModel(bl, tl, tables, options=("unfused_head", "unsplit_k"))
     got = host(abi.dlrm_forward(model, dense, idx))
     d = _mlp(dense, bl, chain=False)
     R = abi.dlrm_emb_interact(tables, idx, d)

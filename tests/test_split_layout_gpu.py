@@ -88,7 +88,8 @@ def test_pages_layout_forward_equals_dlrm_forward():
     """The forward composed in the pages' layout -- bottom MLP, the (B, P) dots,
     a split-A first top layer, the rest of the top MLP -- equals dlrm_forward
     (which writes R = [dense | dots]) bit for bit when dlrm_forward runs the
-    head as its own launch too, and within the float bar with its fused head."""
+    head as its own launch and splits no layer's k, and within the float bar
+    with its default composition."""
     w = inputs.Workload("fwd-split", batch=1000, num_tables=26, rows=20000, dim=64, bag=20,
                         dist="zipf", dense_in=13, bottom=(512, 256, 64), top=(512, 256, 1))
     tables = [dev(inputs.table_host(w, k)) for k in range(w.num_tables)]
@@ -97,7 +98,7 @@ def test_pages_layout_forward_equals_dlrm_forward():
     bottom, top = inputs.dlrm_layers(w, bias_std=0.1)
     bl = [(dev(a), dev(b), act) for a, b, act in bottom]
     tl = [(dev(a), dev(b), act) for a, b, act in top]
-    model = abi.DlrmModel(bl, tl, tables, options=("unfused_head",))
+    model = abi.DlrmModel(bl, tl, tables, options=("unfused_head", "unsplit_k"))
     want = host(abi.dlrm_forward(model, dense, idx))
     fused = host(abi.dlrm_forward(abi.DlrmModel(bl, tl, tables), dense, idx))
     x = dense
