@@ -45,12 +45,13 @@ batch) per call, eager dlrm_forward against a graph-replayed plan, and
 
 Options: --workload {nc32,nc32-uniform,mid,tiny,large,large-uniform} (or one variant,
 nc32-bf16 / nc32-fp8 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-variants,
---no-cells,
---sweep (batch x
-num_tables grid instead of the default line), --warm, --no-cpu-baseline,
---no-forward, --profile-run (timed cold steps only, for profilers),
---copy-calibration (a plain 1 GiB copy, the scale for rocprofv3 FETCH_SIZE /
-WRITE_SIZE).
+--no-cells, --sweep (batch x num_tables grid instead of the default line),
+--sweep-forward (the full forward over batch size), --warm, --no-cpu-baseline,
+--no-forward; for profiler runs: --profile-run (the timed cold steps only),
+--profile-forward B1,B2 (cold full forwards), --profile-linear N K LDA (one
+layer), --read-probe (1 GiB streaming reads, the practical peak and the
+FETCH_SIZE scale), --copy-calibration (1 GiB copies, the WRITE_SIZE scale);
+--record-counters DIR (counter runs to profiles/counters.json).
 """
 import argparse
 import ctypes
@@ -780,15 +781,21 @@ def bench_forward(args, stream, flush):
     plan_same = bool(torch.equal(plan.out, out))
     plan.close()
     log(f"forward as a graph-mode plan: {t_plan * 1000:.1f} us, same output: {plan_same}")
-    # each layer alone (warm: weights and activations are on-chip-sized)
+    # each layer alone (warm: weights and activations are on-chip-sized), on
+    # the forward's own activations: the bottom MLP on dense_in, the top MLP
+    # on R = [d | dots] of this batch (a layer's time depends on its data: the
+    # 415 -> 512 layer on N(0, 1) inputs and N(0, 0.05^2) weights takes ~10%
+    # longer than on these)
     layers = []
-    acts = {}
     x = dense_in
     specs = [("bottom", i, l) for i, l in enumerate(bl)] + [("top", i, l) for i, l in enumerate(tl)]
-    R = torch.empty((B, w.out_width), device="cuda")
+    R = None
+    acts = {}
     for part, i, (wt, b, act) in specs:
         if part == "top" and i == 0:
+            R = abi.dlrm_emb_interact(tables, idx, x, stream=stream)
             x = R
+        acts[(part, i)] = x
         n, k = wt.shape
         y = torch.empty((B, n), device="cuda")
         largs = (B, n, k, x.data_ptr(), x.stride(0), wt.data_ptr(), b.data_ptr(),
@@ -813,10 +820,9 @@ def bench_forward(args, stream, flush):
     # sigmoid head folded into the 512 -> 256 layer's epilogue
     (w1, b1, a1), (wh, bh, ah) = tl[-2], tl[-1]
     n1, k1 = w1.shape
-    xin = torch.empty((B, k1), device="cuda")
-    xin.copy_(torch.rand((B, k1), device="cuda"))
+    xin = acts[("top", len(tl) - 2)]
     yh = torch.empty((B, 1), device="cuda")
-    hargs = (B, n1, k1, xin.data_ptr(), k1, w1.data_ptr(), b1.data_ptr(), abi.ACTS[a1],
+    hargs = (B, n1, k1, xin.data_ptr(), xin.stride(0), w1.data_ptr(), b1.data_ptr(), abi.ACTS[a1],
              wh.data_ptr(), bh.data_ptr(), abi.ACTS[ah], yh.data_ptr(), 1, stream.cuda_stream)
     t_head = _back_to_back_time(lambda: lib.linear_bias_act_head(*hargs), stream)
     f_head = 2.0 * B * n1 * k1 + 2.0 * B * n1
@@ -1109,15 +1115,20 @@ def bench_sweep_forward(args, stream, flush):
         emb_bytes = B * emb_interact_bytes_per_sample(K, D, L)
         emb_comp = (sum(int(x.unique().numel()) for x in xs) * D * 4 + emb_bytes
                     - B * K * L * D * 4)
-        # the six layers alone, and the MLP launches dlrm_forward issues at
-        # this batch (from 7,137 samples on: the bottom MLP as one launch and
-        # the sigmoid head folded into the layer before it)
-        mlp_t, mlp_f, t_by = 0.0, 0.0, {}
+        # the six layers alone; at 7,137..8,192 samples also the MLP launches
+        # dlrm_forward issues there (the bottom MLP as one launch and the
+        # sigmoid head folded into the layer before it).  At other batches
+        # the forward's MLP launches are the layers' own tiles, split over k
+        # where the tiles leave CUs idle, and up to 1,024 samples a one-launch
+        # bottom MLP whose output the interaction finishes: none of these is
+        # callable alone, so only forward_us - emb_interact_us bounds them.
+        mlp_t, mlp_f, t_by, acts = 0.0, 0.0, {}, {}
         x = dense_in[:B]
         for part, layers in (("bottom", bl), ("top", tl)):
-            if part == "top":
-                x = torch.zeros((B, D + P), device="cuda")
+            if part == "top":  # R = [d | dots] of this batch
+                x = abi.dlrm_emb_interact(tables, xs, x, stream=stream)
             for i, (wt, b, act) in enumerate(layers):
+                acts[(part, i)] = x
                 n, k = wt.shape
                 y = torch.empty((B, n), device="cuda")
                 la = (B, n, k, x.data_ptr(), x.stride(0), wt.data_ptr(), b.data_ptr(),
@@ -1127,36 +1138,45 @@ def bench_sweep_forward(args, stream, flush):
                 mlp_t += t_by[(part, i)]
                 mlp_f += 2.0 * B * n * k
                 x = y
-        mlp_fwd = mlp_t
-        if B >= 7137:
+        mlp_fwd = None
+        if 7137 <= B <= 8192:
             arr = abi._layer_array(bl, "bottom", [])
             yb = torch.empty((B, D), device="cuda")
             ca = (B, len(bl), arr, dense_in.data_ptr(), dense_in.stride(0), yb.data_ptr(), D,
                   stream.cuda_stream)
             t_bottom = _back_to_back_time(lambda: lib.mlp_forward(*ca), stream, 20, 3)
             (w1, b1, a1), (wh, bh, ah) = tl[-2], tl[-1]
-            xh = torch.zeros((B, w1.shape[1]), device="cuda")
+            xh = acts[("top", len(tl) - 2)]
             yh = torch.empty((B, 1), device="cuda")
-            ha = (B, w1.shape[0], w1.shape[1], xh.data_ptr(), w1.shape[1], w1.data_ptr(),
+            ha = (B, w1.shape[0], w1.shape[1], xh.data_ptr(), xh.stride(0), w1.data_ptr(),
                   b1.data_ptr(), abi.ACTS[a1], wh.data_ptr(), bh.data_ptr(), abi.ACTS[ah],
                   yh.data_ptr(), 1, stream.cuda_stream)
             t_head = _back_to_back_time(lambda: lib.linear_bias_act_head(*ha), stream, 20, 3)
             mlp_fwd = (t_bottom + sum(t_by[("top", i)] for i in range(len(tl) - 2)) + t_head)
         tf = mlp_f / (mlp_t * 1e-3) / 1e12
-        tf_fwd = mlp_f / (mlp_fwd * 1e-3) / 1e12
         gbs = emb_bytes / (t_emb * 1e-3) / 1e9
         cgbs = emb_comp / (t_emb * 1e-3) / 1e9
-        cells.append({"batch": B, "forward_us": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
-                      "emb_interact_us": t_emb * 1e3, "emb_interact_logical_gbps": gbs,
-                      "emb_interact_compulsory_gbps": cgbs,
-                      "emb_interact_compulsory_frac": cgbs / HBM_PEAK_GBPS,
-                      "mlp_layers_us": mlp_t * 1e3, "mlp_layers_tflops": tf,
-                      "mlp_us": mlp_fwd * 1e3, "mlp_tflops": tf_fwd,
-                      "mlp_frac_f32_mfma": tf_fwd / F32_MFMA_PEAK_TFLOPS})
-        log(f"sweep-forward B={B:5d}: forward {t_fwd * 1e3:7.1f} us "
-            f"({B / (t_fwd * 1e-3) / 1e6:5.1f} M/s), emb+interact {t_emb * 1e3:6.1f} us "
-            f"({gbs:6.0f} GB/s logical, {cgbs:6.0f} compulsory), MLP as the forward runs it "
-            f"{mlp_fwd * 1e3:6.1f} us ({tf_fwd:5.1f} TFLOP/s; layers alone {mlp_t * 1e3:6.1f} us)")
+        rest = t_fwd - t_emb
+        cell = {"batch": B, "forward_us": t_fwd * 1e3, "samples_per_s": B / (t_fwd * 1e-3),
+                "emb_interact_us": t_emb * 1e3, "emb_interact_logical_gbps": gbs,
+                "emb_interact_compulsory_gbps": cgbs,
+                "emb_interact_compulsory_frac": cgbs / HBM_PEAK_GBPS,
+                "forward_minus_emb_interact_us": rest * 1e3,
+                "forward_minus_emb_interact_tflops": mlp_f / (rest * 1e-3) / 1e12,
+                "mlp_layers_us": mlp_t * 1e3, "mlp_layers_tflops": tf,
+                "mlp_layers_frac_f32_mfma": tf / F32_MFMA_PEAK_TFLOPS}
+        msg = (f"sweep-forward B={B:5d}: forward {t_fwd * 1e3:7.1f} us "
+               f"({B / (t_fwd * 1e-3) / 1e6:5.1f} M/s), emb+interact {t_emb * 1e3:6.1f} us "
+               f"({gbs:6.0f} GB/s logical, {cgbs:6.0f} compulsory), forward - emb+interact "
+               f"{rest * 1e3:6.1f} us, the six layers alone {mlp_t * 1e3:6.1f} us "
+               f"({tf:5.1f} TFLOP/s)")
+        if mlp_fwd is not None:
+            tf_fwd = mlp_f / (mlp_fwd * 1e-3) / 1e12
+            cell.update({"mlp_us": mlp_fwd * 1e3, "mlp_tflops": tf_fwd,
+                         "mlp_frac_f32_mfma": tf_fwd / F32_MFMA_PEAK_TFLOPS})
+            msg += f", the forward's MLP launches alone {mlp_fwd * 1e3:6.1f} us ({tf_fwd:5.1f})"
+        cells.append(cell)
+        log(msg)
         del ws, out, d64, r
     return {"workload": f"dlrm: {w.description}", "cache": "cold forward and gather, warm "
             "MLP layers (back to back)", "cells": cells}
@@ -1257,6 +1277,49 @@ def profile_linear(shape, stream):
             raise RuntimeError(f"linear_bias_act: {rc}")
     torch.cuda.synchronize()
     log(f"profile-linear {M}x{N}x{K} (lda {lda}): 10 launches done")
+
+
+def profile_forward(batches, args, stream):
+    """Twelve cold forwards (1 GiB read before each) of the full DLRMv1 model
+    at each batch, for kernel-trace and counter runs; prints the median
+    event-timed forward of the last eleven."""
+    import dataclasses
+    import torch
+    from dlrm_embedding_bag_amd import abi, inputs
+    w = dataclasses.replace(inputs.WORKLOADS["dlrm"], batch=max(batches))
+    tables = [inputs.table_device(w, k, args.seed) for k in range(w.num_tables)]
+    idx = [torch.from_numpy(inputs.indices(w, k, args.seed)).cuda() for k in range(w.num_tables)]
+    dense_in = torch.from_numpy(inputs.dense(w, args.seed)).cuda()
+    bottom, top = inputs.dlrm_layers(w, args.seed)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    model = abi.DlrmModel([(dev(a), dev(b), act) for a, b, act in bottom],
+                          [(dev(a), dev(b), act) for a, b, act in top], tables)
+    lib = abi.load()
+    flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+    for B in batches:
+        xs = [i[: B * w.bag] for i in idx]
+        ws = torch.empty(model.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, 1), device="cuda")
+        fa = (ctypes.byref(model.struct), B, dense_in.data_ptr(), abi._ptr_array(xs), None,
+              abi._i64_array([x.numel() for x in xs]), out.data_ptr(), ws.data_ptr(), ws.numel(),
+              stream.cuda_stream)
+        torch.cuda.synchronize()
+        evs = []
+        with torch.cuda.stream(stream):
+            for _ in range(12):
+                if not args.warm:
+                    flush.max()
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record(stream)
+                rc = lib.dlrm_forward(*fa)
+                if rc:
+                    raise RuntimeError(f"dlrm_forward: {rc}")
+                e[1].record(stream)
+                evs.append(e)
+        torch.cuda.synchronize()
+        t = statistics.median(a.elapsed_time(b) for a, b in evs[1:])
+        log(f"profile-forward B={B}: {t * 1e3:.1f} us per forward "
+            f"({'warm' if args.warm else 'cold'}, median of 11)")
 
 
 def copy_calibration(stream):
@@ -1394,6 +1457,9 @@ def main():
                     help="only 10 launches of one 8192-row linear layer (for counter runs)")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the cold timed steps (for profiler runs)")
+    ap.add_argument("--profile-forward", default="", metavar="B1,B2,...",
+                    help="only twelve cold forwards of the full DLRMv1 model at each batch "
+                         "(for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -1419,6 +1485,9 @@ def main():
         return
     if args.profile_linear:
         profile_linear(args.profile_linear, stream)
+        return
+    if args.profile_forward:
+        profile_forward([int(b) for b in args.profile_forward.split(",")], args, stream)
         return
     if args.sweep_forward:
         import torch

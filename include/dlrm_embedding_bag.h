@@ -406,7 +406,7 @@ DLRM_API int mlp_forward(int32_t m, int32_t num_layers, const dlrm_layer *layers
 #define DLRM_FORWARD_LAYERED 1u  /* never the one-launch small-model kernel   */
 #define DLRM_FORWARD_UNFUSED_HEAD 2u /* the last top layer as its own launch  */
 #define DLRM_FORWARD_UNFUSED_BOTTOM 4u /* each bottom layer as its own launch */
-#define DLRM_FORWARD_UNSPLIT_K 8u /* no layer's k split across workgroups     */
+#define DLRM_FORWARD_UNSPLIT_K 8u /* no partial sums across workgroups      */
 
 /* A DLRMv1 model: bottom MLP, K embedding tables, top MLP.  All arrays of
  * this struct are [host]; the weights and tables they point to are device
@@ -445,14 +445,28 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  * Composition: a model whose MLPs hold at most 64 Ki weights in all (widths
  * <= 1024, <= 4 layers each) runs as ONE launch with every intermediate on
  * chip; larger models run each layer as its own tiled GEMM launch around the
- * fused gather + interaction, except when the batch is about one 32-row
- * band per compute unit (7,137..8,192 samples): then a three-layer bottom
- * MLP of the fused kernel's shapes (see mlp_forward) runs as one launch and
- * a one-output last top layer after a layer at most 256 wide runs in that
- * layer's launch (linear_bias_act_head): 4 launches for 3 + 3 layers.
- * model->options may force the layered
- * composition (DLRM_FORWARD_LAYERED) or the head as its own launch
- * (DLRM_FORWARD_UNFUSED_HEAD).
+ * fused gather + interaction, except:
+ *   - when the batch is about one 32-row band per compute unit
+ *     (7,137..8,192 samples), a three-layer bottom MLP of the fused kernel's
+ *     shapes (see mlp_forward) runs as one launch and a one-output last top
+ *     layer after a layer at most 256 wide runs in that layer's launch
+ *     (linear_bias_act_head): 4 launches for 3 + 3 layers;
+ *   - at small batches (the full-size model: up to 1,024 samples), a
+ *     three-layer bottom MLP (first layer <= 15 inputs, hidden widths
+ *     multiples of 64, N0 <= 512, output <= 256 a multiple of 16) runs as
+ *     one launch cut by its hidden layer's columns, whose partial sums of
+ *     the output the interaction adds as it loads the dense feature;
+ *   - a layer whose tiles would leave compute units idle splits its k over
+ *     up to 8 workgroups storing partial sums, which the next layer adds in
+ *     a fixed order as it loads them (when it can: K a multiple of 4 and at
+ *     least 128, or a matrix-vector last layer).
+ * Every composition gives the same function within float rounding, and the
+ * same bits on every call.  model->options may force the layered
+ * composition (DLRM_FORWARD_LAYERED), the head or the bottom MLP as their
+ * own launches (DLRM_FORWARD_UNFUSED_HEAD, DLRM_FORWARD_UNFUSED_BOTTOM) or
+ * no partial sums across workgroups (DLRM_FORWARD_UNSPLIT_K: each layer a
+ * launch of its own that finishes its outputs; with
+ * DLRM_FORWARD_UNFUSED_HEAD its bits equal linear_bias_act layer by layer).
  */
 DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *dense_in,
                  const int32_t *const *indices, const int32_t *const *offsets,
@@ -469,10 +483,13 @@ DLRM_API int dlrm_forward(const dlrm_model *model, int32_t batch, const float *d
  * The call allocates nothing: no hipMalloc, hipFree or allocating library
  * routine.  Its first call on a device looks up that device's array address
  * once (hipGetSymbolAddress, with the device current).
- *   Limit: a forward whose dlrm_forward_workspace_bytes exceeds
- *          DLRM_NOALLOC_SCRATCH_BYTES returns DLRM_ERR_WORKSPACE before any
- *          work is enqueued (the full-size model 13-512-256-64 / 26 tables /
- *          415-512-256-1 fits up to about 11,000 samples).
+ *   Limit: when the forward's workspace (dlrm_forward_workspace_bytes)
+ *          exceeds DLRM_NOALLOC_SCRATCH_BYTES, the call runs the composition
+ *          without partial sums across workgroups (DLRM_FORWARD_UNSPLIT_K
+ *          added to model->options; same function within float rounding);
+ *          when that too exceeds it, DLRM_ERR_WORKSPACE before any work is
+ *          enqueued (the full-size model 13-512-256-64 / 26 tables /
+ *          415-512-256-1 fits up to 11,650 samples).
  *   Sharing: all calls on one GPU share its array, which keeps the last
  *          call's contents; calls that overlap on one GPU (other streams or
  *          threads without ordering between them) race and give undefined
