@@ -180,6 +180,19 @@ std::vector<int> plan_layer_splits(int B, int n, const dlrm_layer *L, bool allow
   return sp;
 }
 
+// The slice launch takes the bottom MLP while its grid (one workgroup per
+// 16-row band and slice of layer 1) is small.  With 64-column slices, up to
+// one workgroup per CU: measured in the forward (13-512-256-64) at B = 256
+// 15.8 us against 20.6 for the three layer launches, B = 1024 15.1 against
+// 20.4, but at B = 2048 (512 workgroups) 26.2 against 21.5.  16-column
+// slices move a quarter of the W1 bytes per workgroup (each workgroup's
+// weight loads take memory round trips, which set these launches' time):
+// measured (trace) at B = 256 7.8 us against 14.7 for 64-column ones; the
+// forward at B = 512 50.4 us with them (512 workgroups) against 52.9 with
+// 64-column slices, at B = 1024 66.9 against 60.6.
+constexpr int64_t kSliceMaxWorkgroups = 256;
+constexpr int64_t kNarrowMaxWorkgroups = 512;
+
 // The slice launch's parameters for a three-layer bottom MLP (shapes only;
 // the buffers are set at launch); false if it cannot run them.
 bool pack_slice(int B, const dlrm_layer *L, SliceParams &sp) {
@@ -203,15 +216,14 @@ bool pack_slice(int B, const dlrm_layer *L, SliceParams &sp) {
   sp.P = reinterpret_cast<float *>(uintptr_t(256));
   sp.ldp = round4(sp.N2);
   sp.pstride = 0;
+  // 16-column slices while their grid is at most two workgroups per CU,
+  // else 64
+  sp.sw = 16;
+  if (slice_mlp_supported(sp) && slice_mlp_workgroups(sp) <= kNarrowMaxWorkgroups) return true;
+  sp.sw = 64;
   return slice_mlp_supported(sp);
 }
 
-// The slice launch takes the bottom MLP while its grid (one workgroup per
-// 16-row band and 64-column slice of layer 1) is at most one workgroup per
-// CU: measured in the forward (13-512-256-64) at B = 256 15.8 us against
-// 20.6 for the three layer launches, B = 1024 15.1 against 20.4, but at
-// B = 2048 (512 workgroups) 26.2 against 21.5.
-constexpr int64_t kSliceMaxWorkgroups = 256;
 
 // The launch composition of a validated model's MLPs at batch B.
 MlpComposition plan_mlps(const dlrm_model *m, int B) {
@@ -226,7 +238,8 @@ MlpComposition plan_mlps(const dlrm_model *m, int B) {
                                m->bottom[2].out_features, bp);
   SliceParams sp;
   if (!mc.fuse_bottom && split && !(o & DLRM_FORWARD_UNFUSED_BOTTOM) && nb == 3 &&
-      pack_slice(B, m->bottom, sp) && slice_mlp_workgroups(sp) <= kSliceMaxWorkgroups)
+      pack_slice(B, m->bottom, sp) &&
+      slice_mlp_workgroups(sp) <= (sp.sw == 16 ? kNarrowMaxWorkgroups : kSliceMaxWorkgroups))
     mc.bottom_slices = slice_mlp_count(sp);
   mc.fuse_head = !(o & DLRM_FORWARD_UNFUSED_HEAD) && nt >= 2 &&
                  m->top[nt - 1].out_features == 1 &&

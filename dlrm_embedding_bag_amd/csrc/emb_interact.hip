@@ -46,6 +46,24 @@ __global__ __launch_bounds__(256) void emb_bag_kernel(TableSet ts, int B, int K,
                                  out + ((int64_t)b * K + k) * D, nullptr);
 }
 
+// Partials 1 .. nred - 1 (nred <= NR) added to x in order.  All NR - 1 loads
+// are issued before the first add (indices past nred - 1 repeat the last
+// partial and are not added), so the partials arrive in one memory round
+// trip rather than one each.
+template <typename V, int VW, int NR>
+__device__ __forceinline__ void add_partials(const float *p, int64_t stride, int nred, float *x) {
+  V t[NR - 1];
+#pragma unroll
+  for (int r = 1; r < NR; ++r)
+    t[r - 1] = *reinterpret_cast<const V *>(p + (int64_t)min(r, nred - 1) * stride);
+#pragma unroll
+  for (int r = 1; r < NR; ++r)
+    if (r < nred) {
+#pragma unroll
+      for (int e = 0; e < VW; ++e) x[e] += reinterpret_cast<const float *>(&t[r - 1])[e];
+    }
+}
+
 // Feature 0 from the bottom MLP's partial sums: partial 0 (already loaded as
 // v) plus partials 1.. in order, then the bias and the activation.
 template <typename V, int VW>
@@ -54,10 +72,12 @@ __device__ __forceinline__ V dense_reduce(const InteractParams &ip, V v, int b, 
   const float *p = ip.dense + (int64_t)b * ip.ld_dense + c * VW;
 #pragma unroll
   for (int e = 0; e < VW; ++e) x[e] = reinterpret_cast<const float *>(&v)[e];
-  for (int r = 1; r < ip.dense_nred; ++r) {
-    const V t = *reinterpret_cast<const V *>(p + (int64_t)r * ip.dense_stride);
-#pragma unroll
-    for (int e = 0; e < VW; ++e) x[e] += reinterpret_cast<const float *>(&t)[e];
+  if (ip.dense_nred <= 4) {
+    add_partials<V, VW, 4>(p, ip.dense_stride, ip.dense_nred, x);
+  } else {
+    for (int r0 = 0; r0 < ip.dense_nred - 1; r0 += 15)
+      add_partials<V, VW, 16>(p + (int64_t)r0 * ip.dense_stride, ip.dense_stride,
+                              min(16, ip.dense_nred - r0), x);
   }
 #pragma unroll
   for (int e = 0; e < VW; ++e) {

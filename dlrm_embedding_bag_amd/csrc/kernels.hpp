@@ -177,13 +177,14 @@ bool bottom_mlp_supported(const BottomParams &p);
 bool bottom_mlp_preferred(int M);
 hipError_t launch_bottom_mlp(const BottomParams &p, hipStream_t stream);
 
-// The three-layer bottom MLP in one launch cut by h1's columns into 64-wide
-// slices (slice_mlp.hip): workgroup (16-row band, slice s) stores
-// P_s = act1(act0(x W0^T + b0) W1[slice]^T + b1[slice]) W2[:, slice]^T, and
-// the N1 / 64 partials summed in slice order are y's pre-activation (b2 and
-// act2 are the reader's).
+// The three-layer bottom MLP in one launch cut by h1's columns into slices
+// of sw = 64 or 16 columns (slice_mlp.hip): workgroup (16-row band, slice s)
+// stores P_s = act1(act0(x W0^T + b0) W1[slice]^T + b1[slice]) W2[:, slice]^T,
+// and the N1 / sw partials summed in slice order are y's pre-activation (b2
+// and act2 are the reader's).
 struct SliceParams {
   int M, K0, N0, N1, N2;
+  int sw;          // slice width: 64, or 16 for the smallest batches
   const float *x;  // (M, K0), row stride ldx
   int64_t ldx;
   const float *W0, *b0, *W1, *b1, *W2;  // (N_l, K_l) dense; biases (N_l,) or nullptr
@@ -191,11 +192,11 @@ struct SliceParams {
   float *P;        // partial s at P + s pstride, row stride ldp
   int64_t ldp, pstride;
 };
-int slice_mlp_count(const SliceParams &p);         // partials written (N1 / 64)
+int slice_mlp_count(const SliceParams &p);         // partials written (N1 / sw)
 int64_t slice_mlp_workgroups(const SliceParams &p);
-// True for 1 <= K0 <= 15, N0 a multiple of 64 up to 512, N1 a multiple of 64,
-// N2 a multiple of 16 up to 256, P 16-byte aligned with ldp, pstride
-// multiples of 4.
+// True for sw 64 or 16, 1 <= K0 <= 15, N0 a multiple of 64 up to 512, N1 a
+// multiple of sw, N2 a multiple of 16 up to 256, P 16-byte aligned with ldp,
+// pstride multiples of 4.
 bool slice_mlp_supported(const SliceParams &p);
 hipError_t launch_slice_mlp(const SliceParams &p, hipStream_t stream);
 

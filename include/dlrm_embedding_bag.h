@@ -454,8 +454,9 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  *   - at small batches (the full-size model: up to 1,024 samples), a
  *     three-layer bottom MLP (first layer <= 15 inputs, hidden widths
  *     multiples of 64, N0 <= 512, output <= 256 a multiple of 16) runs as
- *     one launch cut by its hidden layer's columns, whose partial sums of
- *     the output the interaction adds as it loads the dense feature;
+ *     one launch cut by its hidden layer's columns (16-column slices up to
+ *     512 samples, 64-column ones above), whose partial sums of the output
+ *     the interaction adds as it loads the dense feature;
  *   - a layer whose tiles would leave compute units idle splits its k over
  *     up to 8 workgroups storing partial sums, which the next layer adds in
  *     a fixed order as it loads them (when it can: K a multiple of 4 and at

@@ -3,8 +3,8 @@ whose GEMM tiles would leave compute units idle, dlrm_forward cuts a layer's
 k over several workgroups that store partial sums, and the next layer reads
 their sum (in partial order), adds the bias and applies the activation as
 it loads its A operand; a three-layer bottom MLP runs as one launch cut by
-its hidden layer's columns, storing partials of its output that the
-interaction adds as it loads the dense feature.  Checked against the CPU
+its hidden layer's columns (16- or 64-column slices), storing partials of
+its output that the interaction adds as it loads the dense feature.  Checked against the CPU
 oracle on sampled rows and against the composition without partials
 (DLRM_FORWARD_UNSPLIT_K) within the float bar, over batches from 1 to past
 the range where partials are taken, hidden activations other than ReLU,
@@ -87,7 +87,9 @@ SHAPES = [
     (1500, 16, (128, 64, 16), (256, 128, 3), {("b", 0): "none"}, (("b", 0),)),
     (64, 64, (512, 256, 128, 64), (512, 256, 128, 1), {}, ()),
     (500, 48, (640, 48), (320, 160, 2), {("b", 0): "sigmoid"}, ()),
-    (200, 32, (128, 64, 32), (96, 48, 1), {("b", 2): "sigmoid"}, ()),  # one bottom slice
+    (200, 32, (128, 64, 32), (96, 48, 1), {("b", 2): "sigmoid"}, ()),
+    (3000, 32, (128, 64, 32), (512, 48, 1), {("b", 2): "sigmoid"}, ()),  # one 64-wide slice
+    (250, 32, (128, 512, 32), (512, 48, 1), {}, (("b", 2),)),  # 32 narrow slices
 ]
 
 
@@ -106,6 +108,26 @@ def test_split_forward_shapes(B, D, bottom, top, acts, no_bias):
     samples = np.unique(np.linspace(0, B - 1, min(B, 64)).astype(int))
     assert_close(got[samples], _oracle_rows(w, dense, bl, tl, tables, idx, samples),
                  "split forward vs oracle")
+
+
+# Bottom MLPs (N0, 256, 32) for every hidden width N0 the slice kernels take
+# (64 .. 512): at 250 samples the launch uses 16-column slices (16 bands x 16
+# slices), at 1000 samples 64-column ones (63 bands x 4 slices).  The wide top
+# MLP keeps the model above the one-launch forward's weight limit.
+@pytest.mark.parametrize("B", [250, 1000])
+@pytest.mark.parametrize("N0", [64, 128, 192, 256, 320, 448, 512])
+def test_slice_kernels_every_width(B, N0):
+    """Each slice-count instantiation of both slice kernels against the
+    composition without partials and against the oracle."""
+    K, D = 8, 32
+    w, tables, idx, dense, bl, tl = _case(B, K, D, (N0, 256, D), (512, 256, 1), seed=N0 + B)
+    d, x = dev(dense), [dev(i) for i in idx]
+    got = host(abi.dlrm_forward(_model(tables, bl, tl), d, x))
+    ref = host(abi.dlrm_forward(_model(tables, bl, tl, options=("unsplit_k",)), d, x))
+    assert_close(got, ref, "slices vs unsplit")
+    samples = np.unique(np.linspace(0, B - 1, 48).astype(int))
+    assert_close(got[samples], _oracle_rows(w, dense, bl, tl, tables, idx, samples),
+                 "slices vs oracle")
 
 
 def test_split_forward_plans_noalloc_and_guards():
