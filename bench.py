@@ -1424,6 +1424,70 @@ def record_counters(run_root, workload, kernel_part="interact_kernel"):
     return entry
 
 
+def forward_penalty(args, stream):
+    """Where the B=8192 forward's MLP launches lose time against their
+    standalone runs: the cold forward with and without every MLP weight
+    read back into the caches after the flush, and the top launches back
+    to back alone, in pairs, and after the gather."""
+    import torch
+    from dlrm_embedding_bag_amd import abi, inputs
+    w = inputs.WORKLOADS["dlrm"]
+    B = w.batch
+    tables = [inputs.table_device(w, k, args.seed) for k in range(w.num_tables)]
+    idx = [torch.from_numpy(inputs.indices(w, k, args.seed)).cuda() for k in range(w.num_tables)]
+    dense_in = torch.from_numpy(inputs.dense(w, args.seed)).cuda()
+    bottom, top = inputs.dlrm_layers(w, args.seed)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    bl = [(dev(a), dev(b), act) for a, b, act in bottom]
+    tl = [(dev(a), dev(b), act) for a, b, act in top]
+    model = abi.DlrmModel(bl, tl, tables)
+    flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+    out = abi.dlrm_forward(model, dense_in, idx, stream=stream)
+    sink = torch.zeros(1, device="cuda")
+    weights = [x[0] for x in bl + tl]
+    for warm in (False, True):
+        ts = []
+        for it in range(25):
+            with torch.cuda.stream(stream):
+                flush.max()
+                if warm:
+                    for t in weights:
+                        sink += t.sum()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                abi.dlrm_forward(model, dense_in, idx, out=out, stream=stream)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            if it >= 5:
+                ts.append(e0.elapsed_time(e1) * 1000)
+        log(f"forward-penalty: forward {'with the MLP weights read after the flush' if warm else 'cold'}"
+            f": {statistics.median(ts):.1f} us")
+    lib = abi.load()
+    d = abi.mlp_forward(dense_in, bl, stream=stream)
+    R = abi.dlrm_emb_interact(tables, idx, d, stream=stream)
+    H = torch.empty(B, tl[0][0].shape[0], device="cuda")
+    o = torch.empty(B, 1, device="cuda")
+    (w0, b0, a0), (w1, b1, a1), (w2, b2, a2) = tl
+    t0 = (B, w0.shape[0], w0.shape[1], R.data_ptr(), R.stride(0), w0.data_ptr(), b0.data_ptr(),
+          abi.ACTS[a0], H.data_ptr(), H.stride(0), stream.cuda_stream)
+    t1 = (B, w1.shape[0], w1.shape[1], H.data_ptr(), H.stride(0), w1.data_ptr(), b1.data_ptr(),
+          abi.ACTS[a1], w2.data_ptr(), b2.data_ptr(), abi.ACTS[a2], o.data_ptr(), 1,
+          stream.cuda_stream)
+    top0 = lambda: lib.linear_bias_act(*t0)
+    top1 = lambda: lib.linear_bias_act_head(*t1)
+    gather = lambda: abi.dlrm_emb_interact(tables, idx, d, out=R, stream=stream)
+    torch.cuda.synchronize()
+    a = _back_to_back_time(top0, stream)
+    b = _back_to_back_time(top1, stream)
+    p = _back_to_back_time(lambda: (top0(), top1()), stream)
+    g = _back_to_back_time(gather, stream, launches=10)
+    q = _back_to_back_time(lambda: (gather(), top0(), top1()), stream, launches=10)
+    log(f"forward-penalty: back to back, per launch or sequence: top 0 {a * 1e3:.1f} us, "
+        f"top 1 + head {b * 1e3:.1f}, the two alternating {p * 1e3:.1f}, gather + interaction "
+        f"{g * 1e3:.1f}, gather then both {q * 1e3:.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1457,6 +1521,8 @@ def main():
                     help="only 10 launches of one 8192-row linear layer (for counter runs)")
     ap.add_argument("--profile-run", action="store_true",
                     help="only the cold timed steps (for profiler runs)")
+    ap.add_argument("--forward-penalty", action="store_true",
+                    help="the B=8192 forward's MLP launches in and out of the forward")
     ap.add_argument("--profile-forward", default="", metavar="B1,B2,...",
                     help="only twelve cold forwards of the full DLRMv1 model at each batch "
                          "(for profiler runs)")
@@ -1488,6 +1554,9 @@ def main():
         return
     if args.profile_forward:
         profile_forward([int(b) for b in args.profile_forward.split(",")], args, stream)
+        return
+    if args.forward_penalty:
+        forward_penalty(args, stream)
         return
     if args.sweep_forward:
         import torch
