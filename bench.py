@@ -49,7 +49,8 @@ nc32-bf16 / nc32-fp8 / nc32-mean / nc32-weighted / nc32-csr, timed alone), --no-
 --sweep-forward (the full forward over batch size), --warm, --no-cpu-baseline,
 --no-forward; for profiler runs: --profile-run (the timed cold steps only),
 --profile-forward B1,B2 (cold full forwards), --profile-linear N K LDA (one
-layer), --read-probe (1 GiB streaming reads, the practical peak and the
+layer), --forward-penalty (the B=8192 forward's MLP launches in and out of
+the forward), --read-probe (1 GiB streaming reads, the practical peak and the
 FETCH_SIZE scale), --copy-calibration (1 GiB copies, the WRITE_SIZE scale);
 --record-counters DIR (counter runs to profiles/counters.json).
 """
