@@ -230,7 +230,6 @@ MlpComposition plan_mlps(const dlrm_model *m, int B) {
   MlpComposition mc;
   const uint32_t o = m->options;
   const bool split = !(o & DLRM_FORWARD_UNSPLIT_K);
-  const int64_t bands = (B + 31) / 32;
   const int nb = m->num_bottom, nt = m->num_top;
   BottomParams bp;
   mc.fuse_bottom = !(o & DLRM_FORWARD_UNFUSED_BOTTOM) && nb == 3 && bottom_mlp_preferred(B) &&

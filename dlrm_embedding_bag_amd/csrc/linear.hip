@@ -27,7 +27,8 @@
 // LDS in group order (measured at M = 256: 512 -> 256 10.5 -> 9.2 us).
 //
 // Layers with N <= 8 (the final 256 -> 1 head) are a matrix-vector product
-// bound by reading A; they take a wave-per-4-rows kernel with DPP row sums.
+// bound by reading A; they take a wave-per-4-rows kernel with DPP row sums
+// (for N = 1 with aligned rows, with each row's loads issued together).
 // Layers with K <= 16 (the 13 -> 512 first layer) are bound by writing C;
 // they take a VALU kernel with the weights in registers (thin_k_kernel).
 //
@@ -142,14 +143,22 @@ __device__ __forceinline__ float act_select(float x, int act) {
 // then added in partial order; the bias (one dword-aligned 16-byte load
 // from a valid address whether or not there is a bias) and the activation
 // follow.
+// Split in two for callers that issue several of them before any add:
+// red_raw loads, red_combine adds and activates.
 template <int NRED>
-__device__ __forceinline__ float4 load_red_full(const ASrc &a, int row, int k) {
+__device__ __forceinline__ void red_raw(const ASrc &a, int row, int k, float4 (&t)[NRED],
+                                        float4 &b) {
   const float *p = a.lo + (int64_t)row * a.ld_lo + k;
-  float4 t[NRED];
 #pragma unroll
   for (int s = 0; s < NRED; ++s)
     t[s] = *reinterpret_cast<const float4 *>(p + (int64_t)s * a.red_stride);
-  const float4_a4 b = *reinterpret_cast<const float4_a4 *>(a.red_bias ? a.red_bias + k : p);
+  const float4_a4 bb = *reinterpret_cast<const float4_a4 *>(a.red_bias ? a.red_bias + k : p);
+  b = make_float4(bb.x, bb.y, bb.z, bb.w);
+}
+
+template <int NRED>
+__device__ __forceinline__ float4 red_combine(const ASrc &a, const float4 (&t)[NRED],
+                                              const float4 &b) {
   float v[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
 #pragma unroll
   for (int s = 1; s < NRED; ++s) {
@@ -163,6 +172,13 @@ __device__ __forceinline__ float4 load_red_full(const ASrc &a, int row, int k) {
                      act_select(v[1] + (hb ? b.y : 0.0f), a.red_act),
                      act_select(v[2] + (hb ? b.z : 0.0f), a.red_act),
                      act_select(v[3] + (hb ? b.w : 0.0f), a.red_act));
+}
+
+template <int NRED>
+__device__ __forceinline__ float4 load_red_full(const ASrc &a, int row, int k) {
+  float4 t[NRED], b;
+  red_raw<NRED>(a, row, k, t, b);
+  return red_combine<NRED>(a, t, b);
 }
 
 // The same for the last, partial slab: columns at or past K read as zero
@@ -415,7 +431,26 @@ __global__ __launch_bounds__(64 * GM * GN * KS) void gemm_kernel(int M, int N, i
   // stored to LDS buffer s & 1 one slab ahead: each global load has two slabs
   // of MFMA work to arrive.
   float4 ra0[A_V4], rw0[W_V4], ra1[A_V4], rw1[W_V4];
-  fetch(0, ra0, rw0);
+  if constexpr (NRED > 1) {
+    // The first slab of a reduced A: every partial and W load issued before
+    // the first add (a scheduling barrier keeps the adds from being moved
+    // between them), so the slab arrives in one memory round trip; nothing
+    // else is in flight yet to hide more.
+    if (nfull > 0) {
+      float4 t[A_V4][NRED], b[A_V4];
+#pragma unroll
+      for (int i = 0; i < A_V4; ++i) red_raw<NRED>(A, arow[i], acol[i], t[i], b[i]);
+#pragma unroll
+      for (int i = 0; i < W_V4; ++i) rw0[i] = load_full<VW>(W, ldw, wrow[i], wcol[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < A_V4; ++i) ra0[i] = red_combine<NRED>(A, t[i], b[i]);
+    } else {
+      fetch(0, ra0, rw0);
+    }
+  } else {
+    fetch(0, ra0, rw0);
+  }
   stash(0, ra0, rw0);
   if (nslab > 1) fetch(1, ra1, rw1);
   __syncthreads();
@@ -600,6 +635,116 @@ __global__ __launch_bounds__(256) void gemv_kernel(int M, int N, int K, const AS
       C[(int64_t)m * ldc + n] = apply_act(acc + bv, act);
     }
   }
+}
+
+// N == 1 (the sigmoid head) with 16-byte aligned A and W and K % 4 == 0:
+// RW rows per wave, 64 / RW lanes per row, lane c taking columns
+// 4c + 256 j / RW (chunks j < NCH) in j order, then a DPP sum over the row's
+// lanes (a reduced A adds its partials in order, then the bias and the
+// activation, as gemv_kernel).  Every load of the lane (all partials of all
+// its chunks, the bias and W) is issued before any arithmetic, which a
+// scheduling barrier keeps from being interleaved with it: one memory round
+// trip per row rather than one per chunk.  Chunks past K load a clamped
+// column and add nothing.
+template <int NRED, int NCH, int RW>
+__global__ __launch_bounds__(256) void head_row_kernel(int M, int K, const ASrc A,
+                                                       const float *__restrict__ W,
+                                                       const float *__restrict__ bias, int act,
+                                                       float *__restrict__ C, int64_t ldc) {
+  static_assert(RW == 1 || RW == 4, "one or four rows per wave");
+  constexpr int LPR = 64 / RW;  // lanes per row
+  constexpr int CW = 4 * LPR;   // columns per chunk
+  const int lane = threadIdx.x & 63;
+  const int c = lane % LPR;
+  const int m = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * RW + lane / LPR;
+  // All lanes of a row stay active through the DPP sums, so rows past M
+  // compute on row M-1 and skip the store.
+  const int mr = m < M ? m : M - 1;
+  const float *row = A.lo + (int64_t)mr * A.ld_lo;
+  float4 t[NCH][NRED], rb[NCH], w[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int k = min(4 * c + CW * j, K - 4);
+#pragma unroll
+    for (int s = 0; s < NRED; ++s)
+      t[j][s] = *reinterpret_cast<const float4 *>(row + (int64_t)s * A.red_stride + k);
+    if constexpr (NRED > 1) {
+      // (a dword-aligned load from a valid address whether or not there is
+      // a bias)
+      const float4_a4 b = *reinterpret_cast<const float4_a4 *>(A.red_bias ? A.red_bias + k
+                                                                           : row + k);
+      rb[j] = make_float4(b.x, b.y, b.z, b.w);
+    }
+    w[j] = *reinterpret_cast<const float4 *>(W + k);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    float4 x = t[j][0];
+    if constexpr (NRED > 1) {
+#pragma unroll
+      for (int s = 1; s < NRED; ++s) {
+        x.x += t[j][s].x;
+        x.y += t[j][s].y;
+        x.z += t[j][s].z;
+        x.w += t[j][s].w;
+      }
+      const bool hb = A.red_bias != nullptr;
+      x = make_float4(act_select(x.x + (hb ? rb[j].x : 0.0f), A.red_act),
+                      act_select(x.y + (hb ? rb[j].y : 0.0f), A.red_act),
+                      act_select(x.z + (hb ? rb[j].z : 0.0f), A.red_act),
+                      act_select(x.w + (hb ? rb[j].w : 0.0f), A.red_act));
+    }
+    const float d = vdot_acc(x, w[j], acc);
+    acc = 4 * c + CW * j < K ? d : acc;
+  }
+  acc = row16_sum(acc);
+  if constexpr (LPR == 64) {
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+  }
+  if (c == 0 && m < M) C[(int64_t)m * ldc] = apply_act(acc + (bias ? bias[0] : 0.0f), act);
+}
+
+// Up to kHeadWaveRowMaxM rows, a wave per row (more workgroups, each with
+// fewer bytes to fetch); above, four rows per wave.
+constexpr int kHeadWaveRowMaxM = 4096;
+
+// Launches head_row_kernel for K <= 1024 while a lane's loads fit in
+// registers (NRED x chunks <= 32); false otherwise.
+template <int NRED>
+bool launch_head_row(int M, int K, const ASrc &A, const float *W, const float *bias, int act,
+                     float *C, int64_t ldc, hipStream_t stream) {
+#define DLRM_HEAD_ROW(NCH_, RW_)                                                             \
+  launch_kernel((head_row_kernel<NRED, NCH_, RW_>), dim3((unsigned)((M + 4 * RW_ - 1) /       \
+                                                                    (4 * RW_))),             \
+                dim3(256), 0, stream, M, K, A, W, bias, act, C, ldc)
+  if (M <= kHeadWaveRowMaxM) {
+    if (K <= 256) {
+      DLRM_HEAD_ROW(1, 1);
+    } else if (K <= 512) {
+      DLRM_HEAD_ROW(2, 1);
+    } else {
+      if constexpr (NRED > 4) return false;
+      if (K > 1024) return false;
+      DLRM_HEAD_ROW(4, 1);
+    }
+  } else {
+    if (K <= 64) {
+      DLRM_HEAD_ROW(1, 4);
+    } else if (K <= 128) {
+      DLRM_HEAD_ROW(2, 4);
+    } else if (K <= 256) {
+      DLRM_HEAD_ROW(4, 4);
+    } else {
+      if constexpr (NRED > 4) return false;
+      if (K > 512) return false;
+      DLRM_HEAD_ROW(8, 4);
+    }
+  }
+#undef DLRM_HEAD_ROW
+  return true;
 }
 
 // K <= 16 (the 13 -> 512 first bottom layer): the layer is bound by writing
@@ -809,6 +954,9 @@ hipError_t launch_linear_src(int M, int N, int K, const ASrc &A, bool va, const 
                              hipStream_t stream) {
   const bool vw = aligned16(W) && K % 4 == 0;
   const bool vc = aligned16(C) && ldc % 4 == 0;
+  if (!SPLIT && N == 1 && va && vw && K >= 4 &&
+      launch_head_row<1>(M, K, A, W, bias, act, C, ldc, stream))
+    return hipGetLastError();
   if (N <= 8) {
     const int rows_per_block = 16;
     dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(256);
@@ -949,6 +1097,15 @@ hipError_t launch_linear_call(const LinearCall &c, hipStream_t stream) {
   const bool vc = aligned16(c.C) && c.ldc % 4 == 0;
   if (N <= 8) {
     if (c.nsplit > 1) return hipErrorInvalidValue;
+    if (N == 1 && K >= 4) {
+      bool ok = false;
+      if (c.a_nred == 2) ok = launch_head_row<2>(M, K, src, c.W, c.bias, c.act, c.C, c.ldc, stream);
+      else if (c.a_nred == 4)
+        ok = launch_head_row<4>(M, K, src, c.W, c.bias, c.act, c.C, c.ldc, stream);
+      else
+        ok = launch_head_row<8>(M, K, src, c.W, c.bias, c.act, c.C, c.ldc, stream);
+      if (ok) return hipGetLastError();
+    }
     const int rows_per_block = 16;
     dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block)), block(256);
     if (c.a_nred == 2)

@@ -125,8 +125,7 @@ __global__ __launch_bounds__(kThreads) void slice_mlp_kernel(SliceParams p, int 
   const int wn = wave & 3;   // 16-column block of the slice
   const int l16 = lane & 15, lq = lane >> 4;
 
-  constexpr int nslab = NS;       // N0 / kSK
-  static_assert(NS >= 1 && NS <= kMaxSlabs, "slab count");
+  static_assert(NS >= 1 && NS <= kMaxSlabs, "slab count (N0 / kSK)");
   const int SW1 = N0 + 4;         // LDS row stride of the W1 slice
   float *W1s = lds;               // 64 x SW1
   float *Abuf = lds + kSW * SW1;  // two h0 slabs of 16 x kSTR (then the h1_s tile)

@@ -1,10 +1,13 @@
 """GPU parity of the fused sigmoid head: dlrm_forward folds a one-output last
 top layer into the epilogue of the layer before it (that layer's
-activations are never stored).  Checked against the CPU oracle and against
-the unfused composition (DLRM_FORWARD_UNFUSED_HEAD) within the float bar,
-over batches that leave the last 32-row tile partly empty, penultimate
-widths below the 256-column tile, K not a multiple of 4, and every head
-activation."""
+activations are never stored) when tiles that own whole rows give about
+one 32-row band per CU; at other batches the head is a launch of its own,
+reading the layer before's k partials.  Checked against the CPU oracle and
+against the unfused composition (DLRM_FORWARD_UNFUSED_HEAD) within the
+float bar, over batches that leave the last tile partly empty, penultimate
+widths below or between tile widths, K not a multiple of 4, every head
+activation, and repeated calls on one workspace, in plans and without
+allocation."""
 import numpy as np
 import pytest
 
@@ -27,18 +30,31 @@ def _case(B, K, D, top, seed, bottom=(64,), head_act="sigmoid"):
 
 
 def _models(tables, bl, tl):
+    """The model with the head folded and with it unfused, both layered (the
+    smaller models here would otherwise run as one launch)."""
     dv = [dev(t) for t in tables]
     b = [(dev(a), dev(x), act) for a, x, act in bl]
     t = [(dev(a), dev(x), act) for a, x, act in tl]
-    return (abi.DlrmModel(b, t, dv), abi.DlrmModel(b, t, dv, options=("unfused_head",)))
+    return (abi.DlrmModel(b, t, dv, options=("layered",)),
+            abi.DlrmModel(b, t, dv, options=("layered", "unfused_head")))
 
 
 # (B, K, D, top widths) -- the full-size top MLP 415-512-256-1 and narrower ones;
-# the fused launch is taken at 7,137..8,192 samples, other batches check that
-# the composition falls back to two launches
+# the whole-row launch is taken at 7,137..8,192 samples, other batches check
+# that the composition falls back to two launches
 CASES = [(8192, 26, 64, (512, 256, 1)), (7201, 4, 16, (64, 7, 1)), (7137, 3, 16, (40, 24, 1)),
          (9000, 8, 64, (512, 200, 1)), (8192, 5, 12, (130, 1)), (16385, 2, 8, (256, 1)),
          (1, 26, 64, (512, 256, 1)), (1000, 26, 64, (512, 256, 1)), (7136, 3, 16, (40, 24, 1))]
+# the head launched on its own after a penultimate layer whose k is split
+# in 8 (256 samples), 4 (333) and 2 (1000 above) or not (2049, 4096,
+# 16384), on 64 x 32, 64 x 64 and 128-row tiles; a penultimate width that
+# leaves the last column tile partly empty (202), one column tile (32), and
+# the top MLP's first layer as the penultimate one (reading R at K = 92 and
+# K = 74)
+SMALL_CASES = [(256, 26, 64, (512, 256, 1)), (333, 26, 64, (512, 256, 1)),
+               (2049, 26, 64, (512, 256, 1)), (4096, 26, 64, (512, 256, 1)),
+               (16384, 26, 64, (512, 256, 1)), (300, 8, 64, (512, 202, 1)),
+               (700, 8, 32, (96, 32, 1)), (2000, 7, 64, (512, 1)), (129, 4, 64, (256, 1))]
 
 
 @pytest.mark.parametrize("B,K,D,top", CASES)
@@ -55,6 +71,47 @@ def test_fused_head_vs_oracle_and_unfused(B, K, D, top):
                                 [np.concatenate([i[s * w.bag:(s + 1) * w.bag] for s in samples])
                                  for i in idx])
     assert_close(got[samples], want, "fused head vs oracle")
+
+
+@pytest.mark.parametrize("B,K,D,top", SMALL_CASES)
+def test_head_after_split_layers_vs_oracle(B, K, D, top):
+    w, tables, idx, dense, bl, tl = _case(B, K, D, top, seed=B + 3 * len(top))
+    fused, unfused = _models(tables, bl, tl)
+    d, x = dev(dense), [dev(i) for i in idx]
+    got = host(abi.dlrm_forward(fused, d, x))
+    ref = host(abi.dlrm_forward(unfused, d, x))
+    assert got.shape == (B, 1)
+    assert_close(got, ref, "default vs unfused head")
+    samples = np.unique(np.linspace(0, B - 1, min(B, 200)).astype(int))
+    want, _, _ = oracle.forward(dense[samples], bl, tl, tables,
+                                [np.concatenate([i[s * w.bag:(s + 1) * w.bag] for s in samples])
+                                 for i in idx])
+    assert_close(got[samples], want, "head after split layers vs oracle")
+
+
+@pytest.mark.parametrize("B", [256, 1000, 2048])
+def test_small_batch_forward_repeats_in_plans_and_noalloc(B):
+    """The small-batch compositions (slice launch, k partials, the head on its
+    own): eager calls on one workspace, both plan modes replayed several
+    times and the no-alloc forward all give the first call's output bit for
+    bit."""
+    import torch
+    w, tables, idx, dense, bl, tl = _case(B, 26, 64, (512, 256, 1), seed=B)
+    fused, _ = _models(tables, bl, tl)
+    d, x = dev(dense), [dev(i) for i in idx]
+    out = torch.empty((B, 1), device="cuda")
+    ws = torch.empty(fused.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+    first = host(abi.dlrm_forward(fused, d, x, out=out, workspace=ws))
+    for _ in range(3):
+        out.fill_(float("nan"))
+        assert np.array_equal(host(abi.dlrm_forward(fused, d, x, out=out, workspace=ws)), first)
+    for mode in ("direct", "graph"):
+        plan = abi.DlrmPlan(fused, d, x, mode=mode)
+        for _ in range(3):
+            assert np.array_equal(host(plan.run()), first), mode
+        plan.close()
+    out2 = torch.empty((B, 1), device="cuda")
+    assert np.array_equal(host(abi.dlrm_forward_noalloc(fused, d, x, out2)), first)
 
 
 @pytest.mark.parametrize("head_act", ["none", "relu", "sigmoid"])
