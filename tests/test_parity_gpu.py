@@ -224,6 +224,42 @@ def test_linear_parity(M, N, K, act):
     assert_close(got, want, f"linear {M}x{N}x{K} {act}")
 
 
+# N = 1 (the sigmoid head's kernel): one wave per row up to 4,096 rows with
+# 256-column chunks, four rows per wave above with 64-column chunks; K that
+# fills 1, 2, 4 or 8 chunks exactly or leaves the last one ragged, K = 4 (one
+# float4), K > 1024 (the wave-per-4-rows fallback), an unaligned row stride
+# (the fallback too), ragged row counts on both sides of the switch.
+HEAD_ROW_SHAPES = [  # (M, K, lda)
+    (1, 4, 4), (17, 60, 60), (300, 256, 256), (301, 260, 260), (4096, 512, 512),
+    (63, 516, 516), (5, 1024, 1024), (4097, 64, 64), (4100, 100, 100), (8195, 256, 256),
+    (4101, 300, 300), (6000, 512, 512), (9000, 516, 516), (33, 1028, 1028),
+    (4200, 1100, 1100), (50, 255, 255), (70, 256, 257),
+]
+
+
+@pytest.mark.parametrize("M,K,lda", HEAD_ROW_SHAPES)
+def test_linear_one_output_column(M, K, lda):
+    import torch
+    rng = np.random.default_rng(M + 3 * K + lda)
+    abuf = rng.standard_normal((M, lda)).astype(np.float32)
+    a = abuf[:, :K]
+    w = rng.uniform(-0.2, 0.2, (1, K)).astype(np.float32)
+    b = np.array([0.1], np.float32)
+    want = oracle.linear(np.ascontiguousarray(a), w, b, "sigmoid")
+    out = torch.full((M + 2,), float("nan"), device="cuda")
+    got = abi.linear_bias_act(dev(abuf)[:, :K], dev(w), dev(b), "sigmoid",
+                              out=out[1:M + 1].view(M, 1))
+    assert_close(host(got), want, f"one output column {M}x{K}")
+    o = host(out)
+    assert np.isnan(o[0]) and np.isnan(o[-1])
+    # dyadic inputs: every order of the sum is exact, so the kernel's output
+    # equals the oracle's bit for bit
+    ad = inputs.dyadic(rng, (M, K), max_int=64)
+    wd = inputs.dyadic(rng, (1, K), max_int=64)
+    got = host(abi.linear_bias_act(dev(ad), dev(wd), None, "none"))
+    assert np.array_equal(got, oracle.linear(ad, wd, None, "none"))
+
+
 def test_linear_dyadic_bit_exact_and_no_bias():
     rng = np.random.default_rng(2)
     for M, N, K in ((300, 512, 13), (129, 130, 131), (300, 1, 256)):
