@@ -711,8 +711,9 @@ __global__ __launch_bounds__(256) void head_row_kernel(int M, int K, const ASrc 
 // fewer bytes to fetch); above, four rows per wave.
 constexpr int kHeadWaveRowMaxM = 4096;
 
-// Launches head_row_kernel for K <= 1024 while a lane's loads fit in
-// registers (NRED x chunks <= 32); false otherwise.
+// Launches head_row_kernel for K up to 1,024 (a wave per row) or 512 (four
+// rows per wave) while a lane's loads fit in registers (NRED x chunks at
+// most 32); false otherwise (the caller then takes gemv_kernel).
 template <int NRED>
 bool launch_head_row(int M, int K, const ASrc &A, const float *W, const float *bias, int act,
                      float *C, int64_t ldc, hipStream_t stream) {
@@ -1099,7 +1100,8 @@ hipError_t launch_linear_call(const LinearCall &c, hipStream_t stream) {
     if (c.nsplit > 1) return hipErrorInvalidValue;
     if (N == 1 && K >= 4) {
       bool ok = false;
-      if (c.a_nred == 2) ok = launch_head_row<2>(M, K, src, c.W, c.bias, c.act, c.C, c.ldc, stream);
+      if (c.a_nred == 2)
+        ok = launch_head_row<2>(M, K, src, c.W, c.bias, c.act, c.C, c.ldc, stream);
       else if (c.a_nred == 4)
         ok = launch_head_row<4>(M, K, src, c.W, c.bias, c.act, c.C, c.ldc, stream);
       else
