@@ -1428,8 +1428,9 @@ def record_counters(run_root, workload, kernel_part="interact_kernel"):
 def forward_penalty(args, stream):
     """Where the B=8192 forward's MLP launches lose time against their
     standalone runs: the cold forward with and without every MLP weight
-    read back into the caches after the flush, and the top launches back
-    to back alone, in pairs, and after the gather."""
+    read back into the caches after the flush, the top launches back to
+    back alone, in pairs, and after the gather, and top layer 0 alone on a
+    warm and a cold A."""
     import torch
     from dlrm_embedding_bag_amd import abi, inputs
     w = inputs.WORKLOADS["dlrm"]
@@ -1487,6 +1488,29 @@ def forward_penalty(args, stream):
     log(f"forward-penalty: back to back, per launch or sequence: top 0 {a * 1e3:.1f} us, "
         f"top 1 + head {b * 1e3:.1f}, the two alternating {p * 1e3:.1f}, gather + interaction "
         f"{g * 1e3:.1f}, gather then both {q * 1e3:.1f}")
+    # Top 0 alone on a warm and on a cold A (the cache flush before each
+    # launch), with R's rows 415 floats apart (dword-aligned loads) and
+    # padded to 416 as inside the forward (16-byte loads).
+    Rp = torch.zeros((B, R.shape[1] + 1), device="cuda")
+    Rp[:, :R.shape[1]] = R
+    for name, A, lda in (("stride 416", Rp, Rp.stride(0)), ("stride 415", R, R.stride(0))):
+        ta = (B, w0.shape[0], w0.shape[1], A.data_ptr(), lda, w0.data_ptr(), b0.data_ptr(),
+              abi.ACTS[a0], H.data_ptr(), H.stride(0), stream.cuda_stream)
+        warm = _back_to_back_time(lambda: lib.linear_bias_act(*ta), stream, launches=20)
+        ts = []
+        for it in range(25):
+            with torch.cuda.stream(stream):
+                flush.max()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                lib.linear_bias_act(*ta)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            if it >= 5:
+                ts.append(e0.elapsed_time(e1) * 1000)
+        log(f"forward-penalty: top 0 alone, A {name}: warm {warm * 1e3:.1f} us, cold "
+            f"{statistics.median(ts):.1f} us")
 
 
 def main():
