@@ -182,15 +182,17 @@ std::vector<int> plan_layer_splits(int B, int n, const dlrm_layer *L, bool allow
 
 // The slice launch takes the bottom MLP while its grid (one workgroup per
 // 16-row band and slice of layer 1) is small.  With 64-column slices, up to
-// one workgroup per CU: measured in the forward (13-512-256-64) at B = 256
+// 1.5 workgroups per CU: measured in the forward (13-512-256-64) at B = 256
 // 15.8 us against 20.6 for the three layer launches, B = 1024 15.1 against
-// 20.4, but at B = 2048 (512 workgroups) 26.2 against 21.5.  16-column
+// 20.4; the whole cold forward at B = 1536 (384 workgroups) 78.3-78.6 us
+// against 81.7, at B = 2048 (512) 85.8-86.1 against 85.2-85.5, at B = 3072
+// 126.1 against 121.0.  16-column
 // slices move a quarter of the W1 bytes per workgroup (each workgroup's
 // weight loads take memory round trips, which set these launches' time):
 // measured (trace) at B = 256 7.8 us against 14.7 for 64-column ones; the
 // forward at B = 512 50.4 us with them (512 workgroups) against 52.9 with
 // 64-column slices, at B = 1024 66.9 against 60.6.
-constexpr int64_t kSliceMaxWorkgroups = 256;
+constexpr int64_t kSliceMaxWorkgroups = 384;
 constexpr int64_t kNarrowMaxWorkgroups = 512;
 
 // The slice launch's parameters for a three-layer bottom MLP (shapes only;

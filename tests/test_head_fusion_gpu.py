@@ -46,12 +46,13 @@ CASES = [(8192, 26, 64, (512, 256, 1)), (7201, 4, 16, (64, 7, 1)), (7137, 3, 16,
          (9000, 8, 64, (512, 200, 1)), (8192, 5, 12, (130, 1)), (16385, 2, 8, (256, 1)),
          (1, 26, 64, (512, 256, 1)), (1000, 26, 64, (512, 256, 1)), (7136, 3, 16, (40, 24, 1))]
 # the head launched on its own after a penultimate layer whose k is split
-# in 8 (256 samples), 4 (333) and 2 (1000 above) or not (2049, 4096,
-# 16384), on 64 x 32, 64 x 64 and 128-row tiles; a penultimate width that
-# leaves the last column tile partly empty (202), one column tile (32), and
-# the top MLP's first layer as the penultimate one (reading R at K = 92 and
-# K = 74)
+# in 8 (256 samples), 4 (333) and 2 (1000 above, 1536) or not (2049, 4096,
+# 16384), on 64 x 32, 64 x 64 and 128-row tiles (at 1536 the bottom MLP is
+# one launch of 384 slice workgroups); a penultimate width that leaves the
+# last column tile partly empty (202), one column tile (32), and the top
+# MLP's first layer as the penultimate one (reading R at K = 92 and K = 74)
 SMALL_CASES = [(256, 26, 64, (512, 256, 1)), (333, 26, 64, (512, 256, 1)),
+               (1536, 26, 64, (512, 256, 1)),
                (2049, 26, 64, (512, 256, 1)), (4096, 26, 64, (512, 256, 1)),
                (16384, 26, 64, (512, 256, 1)), (300, 8, 64, (512, 202, 1)),
                (700, 8, 32, (96, 32, 1)), (2000, 7, 64, (512, 1)), (129, 4, 64, (256, 1))]
