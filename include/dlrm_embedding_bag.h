@@ -451,7 +451,7 @@ DLRM_API size_t dlrm_forward_workspace_bytes(const dlrm_model *model, int32_t ba
  *     shapes (see mlp_forward) runs as one launch and a one-output last top
  *     layer after a layer at most 256 wide runs in that layer's launch
  *     (linear_bias_act_head): 4 launches for 3 + 3 layers;
- *   - at small batches (the full-size model: up to 1,024 samples), a
+ *   - at small batches (the full-size model: up to 1,536 samples), a
  *     three-layer bottom MLP (first layer <= 15 inputs, hidden widths
  *     multiples of 64, N0 <= 512, output <= 256 a multiple of 16) runs as
  *     one launch cut by its hidden layer's columns (16-column slices up to
